@@ -1,0 +1,181 @@
+"""Vision-tower forward throughput on one MI355X.
+
+Workload: the 8-image mixed-resolution batch (seeded sides 28 * U{8..48} px,
+17,624 patches), Qwen2-VL-shaped 32-layer tower (hidden 1280, 16 heads of 80,
+LayerNorm, GELU MLP 5120, 2D RoPE, per-image block-diagonal attention, 2x2
+patch merger to 3584), bf16 MFMA with fp32 accumulation, random N(0, 0.02)
+weights, uint8 pixels already in HBM.  One step = one whole forward (uint8
+pixels -> normalise/patchify -> 32 blocks -> merger), replayed as one HIP
+graph; K steps are timed between device synchronisations.
+
+Also reported: a per-kernel breakdown from hipEvents around every launch
+(one profiled eager forward per timed step), the dominant kernel's roofline
+fraction, aggregate MFMA utilisation, and the CPU oracle's throughput on a
+bounded sample of the same batch (the three smallest images, full depth).
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "vision patches/sec (bf16 32-layer ViT, mixed-res batch) + MFMA util % of peak"
+WORKLOAD = 3
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, n_items=3):
+    import numpy as np
+    from oracle import vit_oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    sizes = [it.n_patches for it in wl.items]
+    pick = sorted(range(len(sizes)), key=lambda i: sizes[i])[:n_items]
+    n = sum(sizes[i] for i in pick)
+    t0 = time.perf_counter()
+    vit_oracle.forward_workload(wl, items=pick, dtype=np.float64)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "patches/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(pick)} smallest images of the batch ({n} patches), all 32 layers + merger, "
+                      f"float64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--workload", type=int, default=WORKLOAD)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the vision tower is not sharded "
+              "across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from multimodal_vlm_vision_amd import VisionTower
+    from workloads import make_workload, pack_pixels
+
+    t0 = time.perf_counter()
+    wl = make_workload(args.workload)
+    cfg = wl.cfg
+    log(f"workload {cfg.name}: {len(wl.items)} items, N={wl.n_patches} patches, "
+        f"grids={[it.grid_thw for it in wl.items]} ({time.perf_counter() - t0:.1f} s to draw)")
+    dev = torch.device("cuda:0")
+    tower = VisionTower(cfg)
+    tower.load_weights(wl.weights)
+    tower.finalize()
+    plan = tower.plan(wl.grid_thw, wl.n_frames)
+    pixels = torch.from_numpy(pack_pixels(wl.items)).to(dev)
+    ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(plan.out_rows, plan.out_cols, dtype=torch.float32, device=dev)
+    log(f"weights uploaded, workspace {plan.ws_bytes / 2**20:.0f} MiB ({time.perf_counter() - t0:.1f} s)")
+
+    # ---- graph: the whole forward, normalisation included, replayed
+    gws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device=dev)
+    graph = tower.capture(plan, gws)
+    off = graph.pixels_ptr - gws.data_ptr()
+    gws[off:off + pixels.numel()].copy_(pixels)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        graph.launch(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.launch(stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t1
+    ms_step = dt / args.steps * 1e3
+    value = wl.n_patches / (dt / args.steps)
+    log(f"graph: {ms_step:.3f} ms/step, {value:,.0f} patches/s")
+
+    # ---- eager (no events) for reference
+    for _ in range(2):
+        tower.encode(plan, pixels, ws, out, stream)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        tower.encode(plan, pixels, ws, out, stream)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t2) / args.steps * 1e3
+
+    # ---- per-kernel breakdown: hipEvents around every launch, same stream
+    agg = {}
+    for _ in range(args.steps):
+        for k in tower.encode_profiled(plan, pixels, ws, out, stream):
+            a = agg.setdefault(k["name"], {"launches": 0, "total_ms": 0.0, "flops": 0.0, "bytes": 0.0,
+                                           "mfma_bound": k["mfma_bound"]})
+            for f in ("launches", "total_ms", "flops", "bytes"):
+                a[f] += k[f]
+    kern = {}
+    tot_ms = sum(a["total_ms"] for a in agg.values())
+    for name, a in sorted(agg.items(), key=lambda kv: -kv[1]["total_ms"]):
+        avg_ms = a["total_ms"] / a["launches"]
+        e = {"launches_per_step": a["launches"] // args.steps, "avg_us": avg_ms * 1e3,
+             "share_pct": 100.0 * a["total_ms"] / tot_ms}
+        if a["mfma_bound"]:
+            e["tflops"] = a["flops"] / (a["total_ms"] * 1e-3) / 1e12
+            e["mfma_pct"] = 100.0 * e["tflops"] / PEAK_BF16_TFLOPS
+        else:
+            e["gbs"] = a["bytes"] / (a["total_ms"] * 1e-3) / 1e9
+            e["hbm_pct"] = 100.0 * e["gbs"] / PEAK_HBM_GBS
+        kern[name] = e
+        log(f"  {name:24s} {e['share_pct']:5.1f}%  avg {e['avg_us']:9.1f} us  " +
+            (f"{e['tflops']:7.1f} TFLOP/s ({e['mfma_pct']:.1f}% MFMA)" if a["mfma_bound"]
+             else f"{e['gbs']:7.1f} GB/s ({e['hbm_pct']:.1f}% HBM)"))
+    dom = max(agg, key=lambda n: agg[n]["total_ms"])
+    da = agg[dom]
+    per_launch_ms = da["total_ms"] / da["launches"]
+    if da["mfma_bound"]:
+        achieved = da["flops"] / da["launches"] / (per_launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "kernel": dom,
+                "avg_launch_us": per_launch_ms * 1e3}
+    else:
+        achieved = da["bytes"] / da["launches"] / (per_launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom,
+                "avg_launch_us": per_launch_ms * 1e3}
+    flops_step = sum(a["flops"] for a in agg.values()) / args.steps
+    mfma_util = 100.0 * flops_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "patches/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "items": len(wl.items), "patches": wl.n_patches,
+                   "layers": cfg.layers, "hidden": cfg.hidden, "heads": cfg.heads, "mlp": cfg.mlp_dim,
+                   "out_dim": cfg.out_dim, "mode": "hipgraph", "parallelism": "single-gpu"},
+        "mfma_util_pct": mfma_util,
+        "algorithmic_tflop_per_step": flops_step / 1e12,
+        "eager_ms_per_step": eager_ms,
+        "roofline": roof,
+        "kernels": kern,
+    }
+    graph.close()
+    if not args.no_cpu:
+        log("CPU oracle baseline ...")
+        line["cpu_baseline"] = cpu_baseline(wl)
+        log(f"CPU oracle: {line['cpu_baseline']['value']:.1f} patches/s on {line['cpu_baseline']['cores']} threads")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * vit.h -- C ABI of the MI355X (gfx950) vision-tower library.
+ *
+ * The library runs the Qwen2-VL / Qwen2.5-VL-style vision tower forward over
+ * packed variable-resolution images and videos on one GPU:
+ *
+ *   uint8 pixels -> rescale/normalise + patchify -> patch-embed GEMM
+ *   -> L x [norm -> QKV GEMM + 2D RoPE -> block-diagonal attention
+ *           -> out-proj + residual -> norm -> MLP + residual]
+ *   -> 2x2 patch merger MLP -> embeddings.
+ *
+ * Sources for what each step computes (pages, not code):
+ *  - vLLM PR #55370 report ("Make mm_device_do_normalize encoder-cudagraph
+ *    safe"), implementation breakdown and review highlights: the tower owns
+ *    the rescale + normalise of integer pixels as its first step, so eager and
+ *    graph-replayed forwards both normalise exactly once; uint8 values are
+ *    exact in bfloat16.
+ *  - "vLLM multimodal inference | ViT performance optimisation" (blog):
+ *    section 2.2 (patchify in merge-unit order, flatten_patches, patch
+ *    embedding, 2D RoPE, encoder, patch merger), 3.2 (patch embedding is a
+ *    stride = kernel 3D conv done as one GEMM), 3.3 (cos/sin cache, 2D
+ *    positions, first half of the angles from the row position, second half
+ *    from the column position, window-attention order), 3.4 (cu_seqlens
+ *    computed once per forward, uploaded asynchronously, shared by every
+ *    layer; attention never crosses an item boundary), 3.5 (fused norm/RoPE/
+ *    activation kernels to cut launches).
+ *  - "GPUModelRunner.execute_model" notes, limits section: an empty batch
+ *    runs no forward; graphs are captured against a fixed workspace.
+ *
+ * Conventions
+ *  - Every call returns vit_status (VIT_OK == 0) unless noted.  On failure
+ *    nothing has been enqueued and vit_last_error() describes the problem.
+ *  - All validation happens before the first enqueue.
+ *  - The caller owns every device buffer (pixels, workspace, output).  The
+ *    library owns its weight arena (inside vit_ctx) and the plan's host data.
+ *    Only vit_finalize_weights and vit_graph_capture allocate device memory.
+ *  - Device pointers are plain HIP device addresses; streams are hipStream_t
+ *    passed as void* (NULL = the default stream).
+ *  - Pixels are uint8 only: there is no float input and no "already
+ *    normalised" mode, so un-normalised and doubly-normalised inputs cannot
+ *    be expressed.
+ *  - A finalized vit_ctx is read-only: concurrent vit_encode calls on
+ *    distinct workspaces are allowed.  Two calls sharing a workspace race.
+ */
+#ifndef VIT_H_
+#define VIT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vit_status;
+#define VIT_OK           0
+#define VIT_E_ARG        1  /* bad argument (null pointer, bad enum, bad config value) */
+#define VIT_E_SHAPE      2  /* bad grid_thw / n_frames / tensor shape */
+#define VIT_E_WEIGHTS    3  /* unknown, duplicate, missing or mis-shaped weight */
+#define VIT_E_WORKSPACE  4  /* workspace or destination buffer too small */
+#define VIT_E_STATE      5  /* call out of order (e.g. encode before finalize) */
+#define VIT_E_HIP        6  /* HIP runtime error (asynchronous faults surface here) */
+
+#define VIT_MLP_GELU     0  /* fc1 -> exact-erf GELU -> fc2 */
+#define VIT_MLP_SWIGLU   1  /* SiLU(gate) * up -> down */
+#define VIT_NORM_LAYER   0  /* LayerNorm with gain and shift, biased variance */
+#define VIT_NORM_RMS     1  /* RMSNorm with gain */
+#define VIT_F32          0
+#define VIT_BF16         1
+
+#define VIT_MAX_FULL_LAYERS 64
+
+/* Tower hyper-parameters.  Fixed by this build: patch 14, temporal_patch 2,
+ * merge 2 (checked).  hidden % 64 == 0, head_dim = hidden / heads must be 32,
+ * 64 or 80 (80 is the Qwen2-VL head size), layers >= 0. */
+typedef struct vit_config {
+  int32_t hidden;
+  int32_t heads;
+  int32_t layers;
+  int32_t mlp_dim;          /* fc1 width (GELU) or gate/up width (SwiGLU) */
+  int32_t mlp_kind;         /* VIT_MLP_* */
+  int32_t norm_kind;        /* VIT_NORM_* (blocks and merger) */
+  float   norm_eps;         /* 1e-6 */
+  int32_t patch;            /* 14 */
+  int32_t temporal_patch;   /* 2 */
+  int32_t merge;            /* 2 */
+  int32_t out_dim;          /* merger output width */
+  float   rope_theta;       /* 10000 */
+  float   mean[3];          /* per-channel mean of x/255, RGB */
+  float   std[3];           /* per-channel std, > 0 */
+  int32_t window_px;        /* 0: no window attention; else window side in pixels (multiple of 28) */
+  int32_t n_full_attn_layers;
+  int32_t full_attn_layers[VIT_MAX_FULL_LAYERS]; /* 0-based layers that attend over whole items */
+} vit_config;
+
+typedef struct vit_ctx vit_ctx;
+typedef struct vit_plan vit_plan;
+typedef struct vit_graph vit_graph;
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* vit_last_error(void);
+
+/* Validates cfg and builds the exact normalise table on the host.  No GPU call. */
+vit_status vit_create(const vit_config* cfg, vit_ctx** out);
+
+/* Copies one host tensor into the context (host buffer may be freed after
+ * the call).  Canonical names and shapes ([out, in] for linears):
+ *   pe.w [hidden][3][2][14][14] (or [hidden][1176])
+ *   blk{l}.n1.g, blk{l}.n1.b (LayerNorm only), blk{l}.n2.g, blk{l}.n2.b  [hidden]
+ *   blk{l}.qkv.w [3*hidden][hidden], blk{l}.qkv.b [3*hidden]
+ *     (or split blk{l}.q.w/.b, blk{l}.k.w/.b, blk{l}.v.w/.b, stacked q;k;v)
+ *   blk{l}.proj.w [hidden][hidden], blk{l}.proj.b [hidden]
+ *   GELU:   blk{l}.fc1.w [mlp][hidden], .b; blk{l}.fc2.w [hidden][mlp], .b
+ *   SwiGLU: blk{l}.gate.w, blk{l}.up.w [mlp][hidden], .b; blk{l}.down.w [hidden][mlp], .b
+ *   mrg.nq.g, mrg.nq.b (LayerNorm only) [hidden]
+ *   mrg.fc1.w [4h][4h], mrg.fc1.b [4h]; mrg.fc2.w [out][4h], mrg.fc2.b [out]
+ * dtype VIT_F32 values are rounded to bfloat16 (nearest, ties to even) for
+ * matrices; norm parameters and biases are kept in float32. */
+vit_status vit_load_weight(vit_ctx* ctx, const char* name, int32_t dtype, const int64_t* shape,
+                           int32_t ndim, const void* host_ptr);
+
+/* Checks completeness, packs (q/k/v stacking, RoPE pair order, K padding,
+ * gate/up interleave) and uploads the weights into a device arena owned by
+ * ctx.  Synchronises `stream` before returning.  ctx is read-only afterwards. */
+vit_status vit_finalize_weights(vit_ctx* ctx, void* stream);
+
+/* Pure host: validates the batch and builds every piece of per-forward
+ * metadata (cu_seqlens, merge-ordered positions, window order, attention
+ * work lists, RoPE cos/sin cache, workspace layout).
+ *   grid_thw [n_items][3] = (t, h, w) in patches; h, w even, t >= 1.
+ *   n_frames [n_items]: 1 for an image (t must be 1; the frame is used for
+ *     both temporal slots), or 2*t for a video.
+ * n_items == 0 is allowed: encode is then a no-op. */
+vit_status vit_plan_create(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t* n_frames,
+                           int32_t n_items, vit_plan** out);
+void vit_plan_destroy(vit_plan* plan);
+
+/* pixel_bytes = sum over items of n_frames*H*W*3 (H = 14h, W = 14w);
+ * ws_bytes = workspace the plan needs; out_rows = N/4 merged tokens;
+ * out_cols = out_dim.  Any output pointer may be NULL. */
+vit_status vit_plan_sizes(const vit_plan* plan, size_t* pixel_bytes, size_t* ws_bytes,
+                          int64_t* out_rows, int64_t* out_cols);
+
+/* Number of patches N and the library's internal row order: dst[i] = the
+ * merge-order row index of internal row i (identity unless window attention
+ * reorders rows).  dst may be NULL; otherwise it holds N int32 (host). */
+vit_status vit_plan_rows(const vit_plan* plan, int64_t* n_patches, int32_t* dst);
+
+/* Enqueues the whole forward on `stream` and returns without synchronising.
+ *   pixels_u8: device, pixel_bytes; items in order, each n_frames frames of
+ *              H x W x 3 uint8, HWC, RGB, row-major.
+ *   ws:        device, >= ws_bytes, 256-byte aligned; contents are scratch.
+ *   out:       device float32 [N/4][out_dim], merged tokens in item order. */
+vit_status vit_encode(const vit_ctx* ctx, const vit_plan* plan, const uint8_t* pixels_u8, void* ws,
+                      size_t ws_bytes, float* out, void* stream);
+
+/* Same forward from uint8 flatten_patches instead of frames:
+ *   patches_u8: device [N][1176] uint8 rows in merge order, features
+ *   (channel, temporal slot, row, column). */
+vit_status vit_encode_patches_u8(const vit_ctx* ctx, const vit_plan* plan,
+                                 const uint8_t* patches_u8, void* ws, size_t ws_bytes, float* out,
+                                 void* stream);
+
+/* Captures the whole forward (normalisation included) into a HIP graph that
+ * reads pixels from, and writes the output into, regions inside `ws`
+ * (see vit_graph_io).  The plan's metadata is uploaded into ws before the
+ * capture begins; the graph is bound to (ctx, plan, ws). */
+vit_status vit_graph_capture(const vit_ctx* ctx, const vit_plan* plan, void* ws, size_t ws_bytes,
+                             void* stream, vit_graph** out);
+/* Device addresses of the graph's uint8 pixel input (pixel_bytes) and
+ * float32 output ([N/4][out_dim]) regions. */
+vit_status vit_graph_io(const vit_graph* g, uint8_t** pixels_in, float** out);
+vit_status vit_graph_launch(vit_graph* g, void* stream);
+void vit_graph_destroy(vit_graph* g);
+
+void vit_destroy(vit_ctx* ctx);
+
+/* Per-kernel timing of one forward.  One record per kernel class (e.g.
+ * "gemm_qkv_rope", "attention"); `flops` counts algorithmic MFMA work
+ * (2 per multiply-add, unpadded shapes; attention 4*hidden*sum(len^2)) and
+ * `bytes` algorithmic HBM traffic of memory-bound kernels, both summed over
+ * the class's launches. */
+typedef struct vit_kernel_stat {
+  char    name[32];
+  int32_t launches;
+  int32_t mfma_bound;   /* 1: judged against MFMA peak, 0: against HBM bandwidth */
+  double  total_ms;     /* sum of hipEvent-measured launch durations */
+  double  flops;
+  double  bytes;
+} vit_kernel_stat;
+
+/* vit_encode with hipEvents recorded around every kernel launch on `stream`.
+ * Synchronises `stream` before returning and writes up to max_stats records
+ * into stats (host array); *n_stats receives the number of classes. */
+vit_status vit_encode_profiled(const vit_ctx* ctx, const vit_plan* plan, const uint8_t* pixels_u8,
+                               void* ws, size_t ws_bytes, float* out, void* stream,
+                               vit_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
+
+/* Test hook: runs the forward up to one intermediate and copies it to `dst`
+ * (device), in internal row order.
+ *   layer = -1: step 0 normalised patches bf16 [N][1176];
+ *               step 1 patch embedding f32 [N][hidden]
+ *   0 <= layer < layers:
+ *               1 norm1 bf16 [N][hidden]; 2 q bf16 [heads][N][head_dim];
+ *               3 k bf16 [heads][N][head_dim]; 4 v bf16 [heads][head_dim][N];
+ *               5 attention bf16 [N][hidden]; 6 residual after out-proj f32 [N][hidden];
+ *               7 norm2 bf16 [N][hidden]; 8 MLP activation bf16 [N][mlp_dim];
+ *               9 block output f32 [N][hidden]
+ *   layer = layers: 1 merger norm bf16 [N][hidden]; 2 merger hidden bf16 [N/4][4*hidden];
+ *               3 output f32 [N/4][out_dim] (item order)
+ * dst_bytes must cover the tensor; VIT_E_WORKSPACE otherwise. */
+vit_status vit_debug_stage(const vit_ctx* ctx, const vit_plan* plan, const uint8_t* pixels_u8,
+                           void* ws, size_t ws_bytes, int32_t layer, int32_t step, void* dst,
+                           size_t dst_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIT_H_ */

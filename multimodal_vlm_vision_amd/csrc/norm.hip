@@ -1,0 +1,120 @@
+// Row normalisation of the float32 residual stream into bfloat16 GEMM inputs.
+//
+// LayerNorm (Qwen2-VL tower) or RMSNorm (Qwen2.5-VL tower) over the hidden
+// width with eps 1e-6 (vLLM PR #55370 report, key code: the towers take a
+// norm epsilon defaulting to 1e-6; "vLLM multimodal inference | ViT
+// performance optimisation", section 3.5 names RMSNorm among the fused ops).
+// One wave per row; the row stays in registers, so the statistics are exact
+// two-pass sums in float32; output is rounded to nearest-even bfloat16.
+#include <hip/hip_runtime.h>
+
+#include "vit_internal.h"
+
+namespace vitmi {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// VPL = float4 chunks per lane (d = 256 * VPL)
+template <int KIND, int VPL>
+__global__ void __launch_bounds__(kThreads)
+rownorm_kernel(const float* __restrict__ r, int64_t rows, int d, const float* __restrict__ g,
+               const float* __restrict__ b, float eps, uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float4* src = reinterpret_cast<const float4*>(r + row * d);
+  const int n4 = d >> 2;
+  float4 v[VPL];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = c < n4 ? src[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (KIND == VIT_NORM_LAYER) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  }
+  float mean = 0.f;
+  if (KIND == VIT_NORM_LAYER) mean = wave_sum(s) / (float)d;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < n4) {
+      const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+      q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
+  uint2* dst = reinterpret_cast<uint2*>(out + row * d);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < n4) {
+      const float4 gg = g4[c];
+      float4 y;
+      y.x = (v[i].x - mean) * rstd * gg.x;
+      y.y = (v[i].y - mean) * rstd * gg.y;
+      y.z = (v[i].z - mean) * rstd * gg.z;
+      y.w = (v[i].w - mean) * rstd * gg.w;
+      if (KIND == VIT_NORM_LAYER) {
+        const float4 bb = b4[c];
+        y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
+      }
+      dst[c] = make_uint2(pack_bf16(y.x, y.y), pack_bf16(y.z, y.w));
+    }
+  }
+}
+
+template <int KIND>
+vit_status launch_kind(const float* r, int64_t rows, int d, const float* g, const float* b,
+                       float eps, uint16_t* out, hipStream_t st) {
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const int vpl = (d / 4 + 63) / 64;
+  if (vpl <= 1)
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 1>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+  else if (vpl <= 2)
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 2>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+  else if (vpl <= 5)
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 5>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+  else if (vpl <= 8)
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 8>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+  else {
+    set_error("rownorm: hidden %d too wide (max 2048)", d);
+    return VIT_E_ARG;
+  }
+  return VIT_OK;
+}
+
+}  // namespace
+
+vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
+                          const float* b, float eps, uint16_t* out, void* stream) {
+  if (rows <= 0) return VIT_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  vit_status s = kind == VIT_NORM_LAYER ? launch_kind<VIT_NORM_LAYER>(r, rows, d, g, b, eps, out, st)
+                                        : launch_kind<VIT_NORM_RMS>(r, rows, d, g, b, eps, out, st);
+  if (s != VIT_OK) return s;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("rownorm launch: %s", hipGetErrorString(e));
+    return VIT_E_HIP;
+  }
+  return VIT_OK;
+}
+
+}  // namespace vitmi

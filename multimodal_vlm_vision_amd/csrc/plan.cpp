@@ -1,0 +1,212 @@
+// Host planner: validates a batch and builds every piece of per-forward
+// metadata once (no GPU call).  What it encodes:
+//  - merge-unit order of patch rows, with each 2x2 unit's four rows adjacent
+//    and the T temporal patches of an item concatenated ("vLLM multimodal
+//    inference | ViT performance optimisation", sections 2.2 and 3.3);
+//  - per-row (hpos, wpos) for the 2D rotary embedding and the cos/sin cache
+//    of max(h, w) positions (same blog, section 3.3);
+//  - window-attention order for towers with windows (section 3.3 names the
+//    reorder; the window geometry is a reading: square windows of
+//    window_px / 14 patches per frame, tiled from the top-left, truncated at
+//    the edges, units row-major inside a window);
+//  - segment bounds for block-diagonal attention, computed once per forward
+//    and shared by every layer (section 3.4), as attention work lists.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "vit_internal.h"
+
+namespace vitmi {
+
+namespace {
+
+template <class T>
+int64_t put(std::vector<uint8_t>& blob, const std::vector<T>& v) {
+  int64_t off = round_up((int64_t)blob.size(), 256);
+  blob.resize(off + v.size() * sizeof(T));
+  if (!v.empty()) std::memcpy(blob.data() + off, v.data(), v.size() * sizeof(T));
+  return off;
+}
+
+struct Seg {
+  int32_t start, len;
+};
+
+// Long segments go to 4-wave workgroups of 256 queries, short ones to 1-wave
+// workgroups of 64 queries; long units are ordered largest segment first.
+void build_lists(const std::vector<Seg>& segs, std::vector<uint8_t>& blob, AttnLists& out,
+                 int32_t& max_len) {
+  std::vector<AttnWork> lw, sw;
+  out.sq_long = out.sq_short = 0.0;
+  std::vector<Seg> order(segs);
+  std::stable_sort(order.begin(), order.end(),
+                   [](const Seg& a, const Seg& b) { return a.len > b.len; });
+  max_len = 0;
+  for (const Seg& s : order) {
+    max_len = std::max(max_len, s.len);
+    if (s.len > 128) {
+      for (int32_t q0 = 0; q0 < s.len; q0 += 256) lw.push_back({s.start, s.len, q0, 0});
+      out.sq_long += (double)s.len * s.len;
+    } else {
+      for (int32_t q0 = 0; q0 < s.len; q0 += 64) sw.push_back({s.start, s.len, q0, 0});
+      out.sq_short += (double)s.len * s.len;
+    }
+  }
+  out.n_long = (int32_t)lw.size();
+  out.n_short = (int32_t)sw.size();
+  out.off_long = put(blob, lw);
+  out.off_short = put(blob, sw);
+}
+
+}  // namespace
+
+vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t* n_frames,
+                      int32_t n_items, vit_plan* p) {
+  const vit_config& c = ctx->cfg;
+  p->cfg = c;
+  p->head_dim = ctx->head_dim;
+  p->mlp_pad = ctx->mlp_pad;
+  if (n_items < 0) {
+    set_error("n_items must be >= 0 (got %d)", n_items);
+    return VIT_E_ARG;
+  }
+  if (n_items > 0 && (!grid_thw || !n_frames)) {
+    set_error("grid_thw and n_frames must not be NULL");
+    return VIT_E_ARG;
+  }
+  p->n_items = n_items;
+  p->grid.assign(grid_thw, grid_thw + 3 * (size_t)n_items);
+  p->nframes.assign(n_frames, n_frames + (size_t)n_items);
+
+  int64_t n_rows = 0;
+  size_t px = 0;
+  int32_t max_pos = 1;
+  for (int i = 0; i < n_items; ++i) {
+    const int32_t t = grid_thw[3 * i], h = grid_thw[3 * i + 1], w = grid_thw[3 * i + 2];
+    const int32_t nf = n_frames[i];
+    if (t < 1 || h < 2 || w < 2 || (h % kMerge) || (w % kMerge)) {
+      set_error("item %d: grid_thw (%d,%d,%d) needs t >= 1 and even h, w >= 2", i, t, h, w);
+      return VIT_E_SHAPE;
+    }
+    if (h > 16384 || w > 16384) {
+      set_error("item %d: h, w must be <= 16384 patches", i);
+      return VIT_E_SHAPE;
+    }
+    if (!((nf == 1 && t == 1) || (nf == kTemporal * t))) {
+      set_error("item %d: n_frames %d does not match t=%d (1 for an image, 2t for a video)", i, nf,
+                t);
+      return VIT_E_SHAPE;
+    }
+    n_rows += (int64_t)t * h * w;
+    px += (size_t)nf * (size_t)(kPatch * h) * (size_t)(kPatch * w) * 3;
+    max_pos = std::max(max_pos, std::max(h, w));
+  }
+  if (n_rows > (int64_t)1 << 28) {
+    set_error("batch has %lld patches; at most 2^28 are supported", (long long)n_rows);
+    return VIT_E_SHAPE;
+  }
+  p->n_rows = n_rows;
+  p->n_units = n_rows / 4;
+  p->pixel_bytes = px;
+  p->pixel_read_bytes = px;
+  p->max_pos = max_pos;
+  p->nfreq = ctx->head_dim / 4;
+
+  // ---- rows in internal order
+  const int wu = c.window_px > 0 ? c.window_px / kUnitPx : 0;   // window side in merge units
+  std::vector<UnitDesc> units;
+  std::vector<int32_t> rowpos, unitdst;
+  units.reserve(p->n_units);
+  rowpos.reserve(n_rows);
+  unitdst.reserve(p->n_units);
+  p->row_order.clear();
+  p->row_order.reserve(n_rows);
+  std::vector<Seg> item_segs, win_segs;
+  int64_t px_base = 0, unit_base = 0;
+  for (int i = 0; i < n_items; ++i) {
+    const int32_t t = grid_thw[3 * i], h = grid_thw[3 * i + 1], w = grid_thw[3 * i + 2];
+    const int32_t nf = n_frames[i];
+    const int64_t W = (int64_t)kPatch * w, H = (int64_t)kPatch * h;
+    const int64_t frame_bytes = H * W * 3;
+    const int32_t uh = h / kMerge, uw = w / kMerge;
+    item_segs.push_back({(int32_t)(unit_base * 4), t * h * w});
+    for (int32_t ti = 0; ti < t; ++ti) {
+      const int64_t slot0 = (nf == 1) ? 0 : (int64_t)kTemporal * ti;
+      auto emit = [&](int32_t bh, int32_t bw) {
+        UnitDesc u;
+        u.px_off = px_base + slot0 * frame_bytes + (int64_t)kUnitPx * bh * W * 3 +
+                   (int64_t)kUnitPx * bw * 3;
+        u.pitch = (int32_t)(W * 3);
+        u.fstride = (nf == 1) ? 0 : (int32_t)frame_bytes;
+        units.push_back(u);
+        const int64_t orig = unit_base + (int64_t)ti * uh * uw + (int64_t)bh * uw + bw;
+        unitdst.push_back((int32_t)orig);
+        for (int dh = 0; dh < kMerge; ++dh)
+          for (int dw = 0; dw < kMerge; ++dw) {
+            rowpos.push_back(((kMerge * bh + dh) << 16) | (kMerge * bw + dw));
+            p->row_order.push_back((int32_t)(4 * orig + kMerge * dh + dw));
+          }
+      };
+      if (wu > 0) {
+        for (int32_t wy = 0; wy < uh; wy += wu)
+          for (int32_t wx = 0; wx < uw; wx += wu) {
+            const int32_t start = (int32_t)(units.size() * 4);
+            for (int32_t bh = wy; bh < std::min(uh, wy + wu); ++bh)
+              for (int32_t bw = wx; bw < std::min(uw, wx + wu); ++bw) emit(bh, bw);
+            win_segs.push_back({start, (int32_t)(units.size() * 4) - start});
+          }
+      } else {
+        for (int32_t bh = 0; bh < uh; ++bh)
+          for (int32_t bw = 0; bw < uw; ++bw) emit(bh, bw);
+      }
+    }
+    unit_base += (int64_t)t * uh * uw;
+    px_base += (int64_t)nf * frame_bytes;
+  }
+
+  // ---- 2D RoPE cos/sin cache: [max_pos][nfreq], angle = pos * theta^(-2j / (head_dim/2))
+  const int nfreq = p->nfreq;
+  const double rd = ctx->head_dim / 2;
+  std::vector<float> cs((size_t)max_pos * nfreq), sn((size_t)max_pos * nfreq);
+  for (int32_t pos = 0; pos < max_pos; ++pos)
+    for (int j = 0; j < nfreq; ++j) {
+      const double a = (double)pos * std::pow((double)c.rope_theta, -2.0 * j / rd);
+      cs[(size_t)pos * nfreq + j] = (float)std::cos(a);
+      sn[(size_t)pos * nfreq + j] = (float)std::sin(a);
+    }
+
+  std::vector<uint8_t>& blob = p->meta;
+  blob.clear();
+  p->off_units = put(blob, units);
+  p->off_rowpos = put(blob, rowpos);
+  p->off_unitdst = put(blob, unitdst);
+  p->off_cos = put(blob, cs);
+  p->off_sin = put(blob, sn);
+  build_lists(item_segs, blob, p->full, p->max_seg_full);
+  if (wu > 0) build_lists(win_segs, blob, p->win, p->max_seg_win);
+  blob.resize(round_up((int64_t)blob.size(), 256));
+
+  // ---- workspace layout
+  const int64_t N = n_rows, d = c.hidden;
+  size_t off = blob.size();
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = round_up((int64_t)(off + bytes), 256);
+    return o;
+  };
+  p->off_x = take((size_t)N * kFeatPad * 2);
+  p->off_r = take((size_t)N * d * 4);
+  p->off_h = take((size_t)N * d * 2);
+  p->off_q = take((size_t)N * d * 2);
+  p->off_k = take((size_t)N * d * 2);
+  p->off_vt = take((size_t)N * d * 2);
+  p->off_o = take((size_t)N * d * 2);
+  p->off_f = take((size_t)N * std::max<int64_t>(p->mlp_pad, d) * 2);
+  p->off_pix = take(px);
+  p->off_out = take((size_t)p->n_units * c.out_dim * 4);
+  p->ws_bytes = off;
+  return VIT_OK;
+}
+
+}  // namespace vitmi

@@ -1,0 +1,195 @@
+// Internal declarations shared by the host planner, the weight packer, the
+// launch sequence and the HIP kernels of the vision-tower library.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/vit.h"
+
+namespace vitmi {
+
+// ---------------------------------------------------------------- errors
+
+void set_error(const char* fmt, ...);
+
+// ---------------------------------------------------------------- fixed shape facts
+
+constexpr int kPatch = 14;
+constexpr int kTemporal = 2;
+constexpr int kMerge = 2;
+constexpr int kFeat = 3 * kTemporal * kPatch * kPatch;   // 1176 features per patch row
+constexpr int kFeatPad = 1216;                            // padded to the GEMM K tile (64)
+constexpr int kUnitPx = kMerge * kPatch;                  // 28-pixel side of a merge unit
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// bfloat16 round-to-nearest-even of a float, as raw bits (host side).
+uint16_t f32_to_bf16_bits(float f);
+
+// ---------------------------------------------------------------- device-side records
+
+// One merge unit = a 2x2 block of patches = a 28x28 pixel block in each of the
+// two temporal frames.  Byte offsets into the caller's packed pixel buffer.
+struct UnitDesc {
+  int64_t px_off;   // first byte of (frame slot 0, top-left pixel, channel 0)
+  int32_t pitch;    // bytes per pixel row (W * 3)
+  int32_t fstride;  // bytes from frame slot 0 to slot 1 (0: image, frame reused)
+};
+static_assert(sizeof(UnitDesc) == 16, "UnitDesc layout");
+
+// One attention work unit: a block of queries of one segment (all heads via grid.y).
+struct AttnWork {
+  int32_t seg_start;  // first internal row of the segment
+  int32_t seg_len;    // rows in the segment
+  int32_t q0;         // first query (relative to seg_start) of this unit
+  int32_t pad;
+};
+static_assert(sizeof(AttnWork) == 16, "AttnWork layout");
+
+// Work lists for one kind of attention layer (item segments or windows).
+struct AttnLists {
+  int64_t off_long = 0;   // byte offset in the metadata blob
+  int32_t n_long = 0;     // units of 256 queries (4-wave workgroups)
+  int64_t off_short = 0;
+  int32_t n_short = 0;    // units of 64 queries (1-wave workgroups)
+  double sq_long = 0.0;   // sum of segment_length^2 over segments in each list
+  double sq_short = 0.0;
+};
+
+// ---------------------------------------------------------------- weights
+
+struct HostTensor {
+  std::vector<int64_t> shape;
+  std::vector<float> data;   // float32 values (exact copies of bf16 input if given as bf16)
+};
+
+struct LayerW {
+  const float *n1g = nullptr, *n1b = nullptr, *n2g = nullptr, *n2b = nullptr;
+  const uint16_t* qkv_w = nullptr;  const float* qkv_b = nullptr;   // [3d][d], q/k in RoPE pair order
+  const uint16_t* proj_w = nullptr; const float* proj_b = nullptr;  // [d][d]
+  const uint16_t* fc1_w = nullptr;  const float* fc1_b = nullptr;   // GELU [mlp_pad][d]; SwiGLU [2*mlp_pad][d]
+  const uint16_t* fc2_w = nullptr;  const float* fc2_b = nullptr;   // [d][mlp_pad]
+};
+
+struct DeviceWeights {
+  void* arena = nullptr;
+  size_t bytes = 0;
+  const uint16_t* lut = nullptr;     // [3][256] bf16 normalise table
+  const uint16_t* pe_w = nullptr;    // [d][kFeatPad]
+  std::vector<LayerW> layers;
+  const float *mq_g = nullptr, *mq_b = nullptr;
+  const uint16_t* m1_w = nullptr; const float* m1_b = nullptr;   // [4d][4d]
+  const uint16_t* m2_w = nullptr; const float* m2_b = nullptr;   // [out][4d]
+};
+
+}  // namespace vitmi
+
+struct vit_ctx {
+  vit_config cfg{};
+  int head_dim = 0;
+  int mlp_pad = 0;       // mlp_dim rounded up to 64
+  uint16_t lut[3][256];  // bf16 bits of ((x/255) - mean_c) / std_c, exactly rounded
+  std::map<std::string, vitmi::HostTensor> host;
+  bool finalized = false;
+  int device = -1;
+  vitmi::DeviceWeights w;
+  bool is_full_layer(int l) const;
+};
+
+struct vit_plan {
+  vit_config cfg{};
+  int head_dim = 0, mlp_pad = 0;
+  int32_t n_items = 0;
+  std::vector<int32_t> grid;      // [n][3]
+  std::vector<int32_t> nframes;   // [n]
+  int64_t n_rows = 0;             // N patches
+  int64_t n_units = 0;            // N / 4
+  size_t pixel_bytes = 0;
+  size_t pixel_read_bytes = 0;    // bytes the patchify reads (an image's frame once, video frames once)
+  int32_t max_pos = 0;            // rows of the cos/sin cache
+  int32_t nfreq = 0;              // head_dim / 4 frequencies per axis
+  int32_t max_seg_full = 0, max_seg_win = 0;
+  std::vector<int32_t> row_order; // internal row -> merge-order row
+
+  // metadata blob uploaded to ws at offset 0
+  std::vector<uint8_t> meta;
+  int64_t off_units = 0, off_rowpos = 0, off_unitdst = 0, off_cos = 0, off_sin = 0;
+  vitmi::AttnLists full, win;
+
+  // workspace layout (byte offsets; all 256-byte aligned)
+  size_t off_x = 0, off_r = 0, off_h = 0, off_q = 0, off_k = 0, off_vt = 0, off_o = 0, off_f = 0;
+  size_t off_pix = 0, off_out = 0, ws_bytes = 0;
+};
+
+struct vit_graph {
+  const vit_ctx* ctx = nullptr;
+  const vit_plan* plan = nullptr;
+  void* ws = nullptr;
+  void* graph = nullptr;   // hipGraph_t
+  void* exec = nullptr;    // hipGraphExec_t
+};
+
+namespace vitmi {
+
+// Builds plan metadata and layout (pure host).  Returns VIT_OK or an error.
+vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t* n_frames,
+                      int32_t n_items, vit_plan* p);
+
+// Weight packing + upload (weights.cpp)
+vit_status finalize_weights(vit_ctx* ctx, void* stream);
+vit_status store_weight(vit_ctx* ctx, const char* name, int32_t dtype, const int64_t* shape,
+                        int32_t ndim, const void* host_ptr);
+
+// ---------------------------------------------------------------- kernel launchers
+
+enum GemmEpi : int {
+  EPI_F32 = 0,     // out f32 = acc
+  EPI_RES = 1,     // out f32 += acc + bias
+  EPI_GELU = 2,    // out bf16 = gelu(acc + bias)
+  EPI_SWIGLU = 3,  // out bf16 [.][N/2] = silu(gate + bg) * (up + bu), gate/up interleaved per 32 columns
+  EPI_QKV = 4,     // RoPE'd q, k -> [heads][rows][head_dim]; v -> [heads][head_dim][rows]
+  EPI_OUT = 5,     // out f32 [row_map[m]][n] = acc + bias
+};
+
+struct GemmArgs {
+  const uint16_t* A = nullptr; int64_t lda = 0;   // [M][K] bf16
+  const uint16_t* B = nullptr; int64_t ldb = 0;   // [N][K] bf16
+  int M = 0, N = 0, K = 0;
+  const float* bias = nullptr;
+  void* out = nullptr; int64_t ldo = 0;
+  // QKV epilogue
+  uint16_t* q = nullptr; uint16_t* k = nullptr; uint16_t* vt = nullptr;
+  int64_t n_tok = 0;
+  const int32_t* row_pos = nullptr;
+  const float* cos_tab = nullptr; const float* sin_tab = nullptr;
+  int nfreq = 0, head_dim = 0, hidden = 0;
+  // output scatter
+  const int32_t* row_map = nullptr;
+};
+
+vit_status launch_gemm(int epi, const GemmArgs& a, void* stream);
+// Raises the dynamic-LDS limit of every GEMM instantiation (call once per process/device).
+vit_status prepare_gemm_kernels();
+
+vit_status launch_normpatch(const uint8_t* pixels, const UnitDesc* units, int64_t n_units,
+                            const uint16_t* lut, uint16_t* x, void* stream);
+vit_status launch_normrows_u8(const uint8_t* patches, int64_t n_rows, const uint16_t* lut,
+                              uint16_t* x, void* stream);
+vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
+                          const float* b, float eps, uint16_t* out, void* stream);
+
+struct AttnArgs {
+  const uint16_t* q = nullptr; const uint16_t* k = nullptr; const uint16_t* vt = nullptr;
+  uint16_t* o = nullptr;
+  int64_t n_tok = 0;
+  int heads = 0, head_dim = 0;
+  const AttnWork* work_long = nullptr; int n_long = 0;
+  const AttnWork* work_short = nullptr; int n_short = 0;
+};
+vit_status launch_attention(const AttnArgs& a, void* stream);
+
+}  // namespace vitmi

@@ -1,0 +1,281 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on
+identical seeded inputs.
+
+* normalise + patchify: bit-exact on all five workloads;
+* every kernel of a block, layer-local: each step's oracle input is the
+  GPU's own previous-stage output, so a mismatch names the kernel;
+* the whole tower: max |g - r| <= 2e-2 and sum|g - r| / sum|r| <= 5e-3
+  against the oracle (float64), on full workloads where the oracle finishes
+  in seconds and on sampled items of the big ones (items are independent);
+* isolation between items, run-to-run determinism, graph replay == eager,
+  the uint8 flatten_patches entry point, and degenerate batches.
+"""
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import vit_oracle as O
+from workloads import TowerConfig, make_custom_workload, make_workload, pack_pixels, tower_config
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_support import GpuRun, assert_close_bf16, assert_encoder_tolerance  # noqa: E402
+
+_RUNS = {}
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def get_run(idx: int, layers=None) -> GpuRun:
+    key = (idx, layers)
+    if key not in _RUNS:
+        say(f"building workload {idx} layers={layers}")
+        _RUNS.clear()
+        torch.cuda.empty_cache()
+        _RUNS[key] = GpuRun(make_workload(idx, layers=layers))
+    return _RUNS[key]
+
+
+def W64(run, name):
+    """A weight as the library holds it: matrices in bfloat16 (exact for the bf16-weight
+    workloads, rounded for the float32 one), norm parameters and biases in float32."""
+    w = run.wl.weights[name].astype(np.float64)
+    return O.bf16_round(w) if name.endswith(".w") else w
+
+
+# ------------------------------------------------------------------ normpatch
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_normpatch_bit_exact(idx):
+    run = get_run(idx, layers=1)
+    say(f"normpatch workload {idx} N={run.n}")
+    got = run.stage(-1, 0)
+    table = O.normalize_table(run.cfg.mean, run.cfg.std)
+    ref = O.patchify([it.frames for it in run.wl.items], run.wl.grid_thw, table)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} elements differ"
+
+
+# ------------------------------------------------------------------ layer-local kernels
+
+
+def _sample_rows(run, k=384, seed=0):
+    n = run.n
+    if n <= 4096:
+        return None
+    g = np.random.default_rng(seed)
+    return np.sort(g.choice(n, size=k, replace=False))
+
+
+def check_block(run, layer):
+    c = run.cfg
+    d, H, hd = c.hidden, c.heads, c.head_dim
+    p = f"blk{layer}"
+    rows = _sample_rows(run)
+    sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    pos = O.patch_positions(run.wl.grid_thw)
+    ang = O.rope_angles(pos["hpos"], pos["wpos"], hd)
+    segs = O.layer_segments(layer, c, pos)
+
+    r_in = run.stage(layer - 1, 9) if layer > 0 else run.stage(-1, 1)
+    h1 = run.stage(layer, 1)
+    ref = O.norm(r_in, run.wl.weights, p + ".n1", c.norm_kind, c.norm_eps)
+    assert_close_bf16(h1, ref, rel=2.0 ** -8, abs_=1e-5, what=f"L{layer} norm1")
+
+    qg, kg, vg = run.stage(layer, 2), run.stage(layer, 3), run.stage(layer, 4)
+    qkv = h1 @ W64(run, p + ".qkv.w").T + W64(run, p + ".qkv.b")
+    q = O.apply_rope(qkv[:, :d].reshape(-1, H, hd), ang)
+    k = O.apply_rope(qkv[:, d:2 * d].reshape(-1, H, hd), ang)
+    v = qkv[:, 2 * d:].reshape(-1, H, hd)
+    for nm, got, want in (("q", qg, q), ("k", kg, k), ("v", vg, v)):
+        assert_close_bf16(got, want, rel=2.0 ** -8, abs_=2e-4, what=f"L{layer} {nm}+rope")
+
+    og = run.stage(layer, 5)
+    o = O.attention(qg, kg, vg, segs, rows=rows).reshape(-1, d)
+    vscale = float(np.sqrt((vg ** 2).mean()))
+    assert_close_bf16(sel(og), o, rel=2.0 ** -6, abs_=4e-3 * vscale, what=f"L{layer} attention")
+
+    r1g = run.stage(layer, 6)
+    r1 = r_in + og @ W64(run, p + ".proj.w").T + W64(run, p + ".proj.b")
+    assert_close_bf16(r1g, r1, rel=1e-5, abs_=2e-4, what=f"L{layer} out-proj+residual")
+
+    h2 = run.stage(layer, 7)
+    assert_close_bf16(h2, O.norm(r1g, run.wl.weights, p + ".n2", c.norm_kind, c.norm_eps),
+                      rel=2.0 ** -8, abs_=1e-5, what=f"L{layer} norm2")
+
+    ag = run.stage(layer, 8)
+    if c.mlp_kind == "gelu":
+        a = O.gelu(h2 @ W64(run, p + ".fc1.w").T + W64(run, p + ".fc1.b"))
+        w2, b2 = W64(run, p + ".fc2.w"), W64(run, p + ".fc2.b")
+    else:
+        a = O.silu(h2 @ W64(run, p + ".gate.w").T + W64(run, p + ".gate.b")) * \
+            (h2 @ W64(run, p + ".up.w").T + W64(run, p + ".up.b"))
+        w2, b2 = W64(run, p + ".down.w"), W64(run, p + ".down.b")
+    assert_close_bf16(ag, a, rel=2.0 ** -7, abs_=2e-4, what=f"L{layer} mlp activation")
+
+    r2g = run.stage(layer, 9)
+    assert_close_bf16(r2g, r1g + ag @ w2.T + b2, rel=1e-5, abs_=2e-4, what=f"L{layer} mlp out+residual")
+
+
+@pytest.mark.parametrize("idx,layer", [(1, 0), (2, 0), (2, 3), (3, 0), (5, 0), (5, 7)])
+def test_block_kernels_layer_local(idx, layer):
+    run = get_run(idx, layers=max(1, layer + 1) if idx >= 3 else None)
+    say(f"block kernels workload {idx} layer {layer}")
+    check_block(run, layer)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 5])
+def test_patch_embed_and_merger_layer_local(idx):
+    run = get_run(idx, layers=1 if idx >= 3 else None)
+    c = run.cfg
+    say(f"patch embed + merger workload {idx}")
+    x = run.stage(-1, 0)
+    r0 = run.stage(-1, 1)
+    assert_close_bf16(r0, x @ W64(run, "pe.w").reshape(c.hidden, -1).T, rel=1e-5, abs_=2e-4,
+                      what="patch embed")
+    rl = run.stage(c.layers - 1, 9)
+    u = run.stage(c.layers, 1)
+    assert_close_bf16(u, O.norm(rl, run.wl.weights, "mrg.nq", c.norm_kind, c.norm_eps),
+                      rel=2.0 ** -8, abs_=1e-5, what="merger norm")
+    z1 = run.stage(c.layers, 2)
+    ref1 = O.gelu(u.reshape(-1, 4 * c.hidden) @ W64(run, "mrg.fc1.w").T + W64(run, "mrg.fc1.b"))
+    assert_close_bf16(z1, ref1, rel=2.0 ** -7, abs_=2e-4, what="merger fc1+gelu")
+    out = run.encode()
+    ref2 = z1 @ W64(run, "mrg.fc2.w").T + W64(run, "mrg.fc2.b")
+    assert_close_bf16(out, ref2, rel=1e-5, abs_=2e-4, what="merger fc2 (item order)")
+
+
+# ------------------------------------------------------------------ whole tower
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_encoder_full_workload(idx):
+    run = get_run(idx)
+    say(f"encoder workload {idx} N={run.n} layers={run.cfg.layers}")
+    got = run.encode()
+    ref = O.forward_workload(run.wl)
+    assert_encoder_tolerance(got, ref, what=f"workload {idx}")
+
+
+@pytest.mark.parametrize("idx", [3, 5])
+def test_encoder_full_depth_sampled_items(idx):
+    """32-layer tower on the whole batch; the oracle recomputes the smallest item(s) alone."""
+    run = get_run(idx)
+    say(f"encoder workload {idx} N={run.n} (32 layers), oracle on the smallest item")
+    got = run.encode()
+    sizes = [it.n_patches for it in run.wl.items]
+    pick = [int(np.argmin(sizes))]
+    ref = O.forward_workload(run.wl, items=pick)
+    start = sum(sizes[:pick[0]]) // 4
+    assert_encoder_tolerance(got[start:start + sizes[pick[0]] // 4], ref, what=f"workload {idx} item {pick[0]}")
+
+
+def test_video_workload_last_block_and_merger():
+    """The 18432-patch single-segment video at full depth: last block (sampled rows) and merger."""
+    run = get_run(4)
+    say("video workload: 32 layers, last block + merger")
+    c = run.cfg
+    check_block(run, c.layers - 1)
+    out = run.encode()
+    ref = O.merger(run.stage(c.layers - 1, 9), run.wl.weights, c)
+    assert_encoder_tolerance(out, ref, max_abs=2e-2, mean_rel=5e-3, what="video merger from GPU residual")
+
+
+def test_video_shaped_short_clip_end_to_end():
+    cfg = tower_config(4).with_layers(2)
+    wl = make_custom_workload(cfg, [(4, 504, 896)], seed=41)
+    run = GpuRun(wl)
+    say(f"short video clip N={run.n}")
+    assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="video 4 frames, 2 layers")
+
+
+def test_edge_items_end_to_end():
+    """One-unit items, ragged segment lengths, a 2-frame video and a wide strip."""
+    cfg = tower_config(2).with_layers(2)
+    sizes = [(1, 28, 28), (1, 56, 28), (2, 28, 84), (1, 28, 28 * 19), (1, 196, 140)]
+    wl = make_custom_workload(cfg, sizes, seed=43)
+    run = GpuRun(wl)
+    say(f"edge items N={run.n} segments={wl.seg_lengths}")
+    assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="edge items")
+
+
+def test_qwen25_windows_small_end_to_end():
+    cfg = dataclasses.replace(tower_config(5).with_layers(3), full_attn_layers=(1,))
+    sizes = [(1, 28 * 9, 28 * 5), (1, 56, 28 * 7), (4, 28 * 6, 28 * 5)]
+    wl = make_custom_workload(cfg, sizes, seed=47)
+    run = GpuRun(wl)
+    say(f"window tower N={run.n}")
+    assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="windows + full layer")
+
+
+# ------------------------------------------------------------------ properties
+
+
+def test_isolation_between_items():
+    cfg = tower_config(3).with_layers(2)
+    sizes = [(1, 56, 84), (1, 112, 56), (1, 84, 84)]
+    wl = make_custom_workload(cfg, sizes, seed=53)
+    run = GpuRun(wl)
+    say("isolation")
+    a = run.encode()
+    px = pack_pixels(wl.items)
+    n0 = wl.items[0].frames.size
+    n1 = wl.items[1].frames.size
+    px[n0:n0 + n1] = 255 - px[n0:n0 + n1]
+    run.pixels.copy_(torch.from_numpy(px))
+    b = run.encode()
+    u0, u1 = wl.items[0].n_patches // 4, wl.items[1].n_patches // 4
+    assert np.array_equal(a[:u0], b[:u0]) and np.array_equal(a[u0 + u1:], b[u0 + u1:])
+    assert not np.allclose(a[u0:u0 + u1], b[u0:u0 + u1])
+
+
+def test_determinism_and_graph_replay_match_eager():
+    run = get_run(5, layers=8)
+    say("determinism + graph replay")
+    a = run.encode()
+    b = run.encode()
+    assert np.array_equal(a, b)
+    gws = torch.empty(run.plan.ws_bytes, dtype=torch.uint8, device="cuda")
+    g = run.tower.capture(run.plan, gws)
+    # write pixels into the graph's own input region
+    src = run.pixels
+    off = g.pixels_ptr - gws.data_ptr()
+    gws[off:off + src.numel()].copy_(src)
+    out_off = g.out_ptr - gws.data_ptr()
+    for rep in range(3):
+        g.launch()
+        torch.cuda.synchronize()
+        got = gws[out_off:out_off + a.size * 4].view(torch.float32).reshape(a.shape).cpu().numpy()
+        assert np.array_equal(got, a), f"replay {rep} differs from eager"
+        run.encode()                      # eager work between replays
+    g.close()
+
+
+def test_patches_u8_entry_matches_frames_entry():
+    run = get_run(2)
+    say("uint8 flatten_patches entry")
+    ident = np.tile(np.arange(256, dtype=np.float64), (3, 1))
+    rows = O.patchify([it.frames for it in run.wl.items], run.wl.grid_thw, ident).astype(np.uint8)
+    pt = torch.from_numpy(np.ascontiguousarray(rows)).cuda()
+    out2 = torch.empty_like(run.out)
+    run.tower.encode_patches_u8(run.plan, pt, run.ws, out2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.cpu().numpy(), run.encode().astype(np.float32))
+
+
+def test_empty_batch_enqueues_nothing():
+    run = get_run(1)
+    p = run.tower.plan(np.zeros((0, 3), np.int32), np.zeros(0, np.int32))
+    run.tower.encode(p, None, None, None)
+    torch.cuda.synchronize()

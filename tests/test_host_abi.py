@@ -1,0 +1,120 @@
+"""CPU tests of the C ABI's host side: the library loads and exports every
+symbol the header declares; configuration, weight and batch validation fail
+with the documented status before anything is enqueued; the planner's sizes,
+row order and window permutation agree with index sets derived independently
+(from the oracle's window partition).  No GPU call is made."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from multimodal_vlm_vision_amd import binding as B
+from oracle import vit_oracle as O
+from workloads import TowerConfig, tower_config
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_library_exports_every_header_symbol(lib):
+    names = B.header_symbols()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B._SIGS), "binding signatures must cover the header exactly"
+
+
+def _status(fn):
+    try:
+        fn()
+    except B.VitError as e:
+        return e.status
+    return B.VIT_OK
+
+
+def test_config_validation(lib):
+    import dataclasses
+    cfg = tower_config(2)
+    assert _status(lambda: B.VisionTower(cfg, lib)) == B.VIT_OK
+    bad = [dataclasses.replace(cfg, patch=16), dataclasses.replace(cfg, heads=3),
+           dataclasses.replace(cfg, hidden=1280, heads=10),          # head_dim 128 unsupported
+           dataclasses.replace(cfg, std=(0.27, 0.0, 0.28)), dataclasses.replace(cfg, out_dim=100),
+           dataclasses.replace(cfg, window_px=100), dataclasses.replace(cfg, layers=-1)]
+    for b in bad:
+        assert _status(lambda: B.VisionTower(b, lib)) == B.VIT_E_ARG, b
+    assert lib.vit_create(None, ctypes.byref(B._P())) == B.VIT_E_ARG
+    assert b"NULL" in lib.vit_last_error()
+
+
+def test_weight_validation_and_state(lib):
+    t = B.VisionTower(tower_config(1), lib)
+    t.load_weight("pe.w", np.zeros((64, 1176), np.float32))
+    assert _status(lambda: t.load_weight("pe.w", np.zeros((64, 1176), np.float32))) == B.VIT_E_WEIGHTS
+    assert _status(lambda: t.load_weight("x", np.zeros((0,), np.float32))) == B.VIT_E_SHAPE
+    # encode before finalize is a state error, detected before any GPU work
+    p = t.plan([[1, 4, 4]], [1])
+    st = lib.vit_encode(t.handle, p.handle, 1, 256, 1 << 30, 256, None)
+    assert st == B.VIT_E_STATE
+
+
+@pytest.mark.parametrize("grid,frames,status", [
+    ([[1, 3, 4]], [1], B.VIT_E_SHAPE),           # odd h
+    ([[0, 4, 4]], [1], B.VIT_E_SHAPE),           # t = 0
+    ([[2, 4, 4]], [1], B.VIT_E_SHAPE),           # image with t > 1
+    ([[2, 4, 4]], [3], B.VIT_E_SHAPE),           # frames != 2t
+    ([[1, 4, 4], [2, 6, 8]], [1, 4], B.VIT_OK),
+])
+def test_plan_validation(lib, grid, frames, status):
+    t = B.VisionTower(tower_config(1), lib)
+    assert _status(lambda: t.plan(grid, frames)) == status
+
+
+def test_empty_batch_is_a_noop(lib):
+    t = B.VisionTower(tower_config(1), lib)
+    p = t.plan(np.zeros((0, 3), np.int32), np.zeros(0, np.int32))
+    assert p.n_patches == 0 and p.out_rows == 0 and p.pixel_bytes == 0
+
+
+def test_plan_sizes_and_identity_row_order(lib):
+    t = B.VisionTower(tower_config(3), lib)
+    grid = [[1, 82, 22], [1, 30, 34], [3, 6, 8]]
+    p = t.plan(grid, [1, 1, 6])
+    n = 82 * 22 + 30 * 34 + 3 * 6 * 8
+    assert p.n_patches == n and p.out_rows == n // 4 and p.out_cols == 3584
+    assert p.pixel_bytes == 3 * (82 * 14 * 22 * 14 + 30 * 14 * 34 * 14 + 6 * 6 * 14 * 8 * 14)
+    assert np.array_equal(p.row_order(), np.arange(n))
+    small = t.plan(grid[:1], [1])
+    assert small.ws_bytes < p.ws_bytes
+
+
+def test_window_order_matches_oracle_window_partition(lib):
+    cfg = tower_config(5)
+    t = B.VisionTower(cfg, lib)
+    grid = np.array([[1, 24, 48], [1, 18, 28], [4, 18, 30]])
+    frames = [1, 1, 8]
+    p = t.plan(grid, frames)
+    order = p.row_order()
+    n = int((grid[:, 0] * grid[:, 1] * grid[:, 2]).sum())
+    assert np.array_equal(np.sort(order), np.arange(n))          # a permutation
+    # merge units stay whole and in (dh, dw) order
+    assert np.all(order[0::4] % 4 == 0) and np.all(np.diff(order.reshape(-1, 4), axis=1) == 1)
+    pos = O.patch_positions(grid)
+    wins = O.window_segments(pos, cfg.window_px // cfg.patch)
+    win_id = np.empty(n, np.int64)
+    for i, s in enumerate(wins):
+        win_id[s] = i
+    ids = win_id[order]
+    # each window is one contiguous run of internal rows
+    runs = ids[np.r_[True, ids[1:] != ids[:-1]]]
+    assert len(runs) == len(wins) and len(set(runs.tolist())) == len(wins)
+    # items stay contiguous and in order
+    assert np.all(np.diff(pos["item"][order]) >= 0)
+
+
+def test_workspace_grows_with_batch(lib):
+    t = B.VisionTower(tower_config(2), lib)
+    sizes = [t.plan([[1, 2 * k, 2 * k]], [1]).ws_bytes for k in (2, 8, 16, 32)]
+    assert sizes == sorted(sizes) and len(set(sizes)) == 4

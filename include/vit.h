@@ -68,6 +68,9 @@ typedef int32_t vit_status;
 #define VIT_F32          0
 #define VIT_BF16         1
 
+#define VIT_ACT_BF16     0  /* GEMM activation operands rounded once to bfloat16 */
+#define VIT_ACT_BF16X2   1  /* norm, MLP and merger activations kept as hi+lo bfloat16 pairs */
+
 #define VIT_MAX_FULL_LAYERS 64
 
 /* Tower hyper-parameters.  Fixed by this build: patch 14, temporal_patch 2,
@@ -91,6 +94,13 @@ typedef struct vit_config {
   int32_t window_px;        /* 0: no window attention; else window side in pixels (multiple of 28) */
   int32_t n_full_attn_layers;
   int32_t full_attn_layers[VIT_MAX_FULL_LAYERS]; /* 0-based layers that attend over whole items */
+  /* VIT_ACT_BF16X2: each norm output, MLP activation and merger activation x is
+   * stored as hi = bf16(x), lo = bf16(x - hi) and the GEMM that consumes it runs
+   * over both halves against the same bf16 weights (twice the MFMA work of the
+   * qkv, MLP and merger products), which removes their activation rounding;
+   * q, k, v, the attention probabilities and the attention output stay
+   * single bf16.  VIT_ACT_BF16 rounds every GEMM activation once. */
+  int32_t activation_precision;
 } vit_config;
 
 typedef struct vit_ctx vit_ctx;
@@ -201,13 +211,16 @@ vit_status vit_encode_profiled(const vit_ctx* ctx, const vit_plan* plan, const u
  *   layer = -1: step 0 normalised patches bf16 [N][1176];
  *               step 1 patch embedding f32 [N][hidden]
  *   0 <= layer < layers:
- *               1 norm1 bf16 [N][hidden]; 2 q bf16 [heads][N][head_dim];
+ *               1 norm1 bf16 [N][S*hidden]; 2 q bf16 [heads][N][head_dim];
  *               3 k bf16 [heads][N][head_dim]; 4 v bf16 [heads][head_dim][N];
  *               5 attention bf16 [N][hidden]; 6 residual after out-proj f32 [N][hidden];
- *               7 norm2 bf16 [N][hidden]; 8 MLP activation bf16 [N][mlp_dim];
+ *               7 norm2 bf16 [N][S*hidden]; 8 MLP activation bf16 [N][S*mlp_pad];
  *               9 block output f32 [N][hidden]
- *   layer = layers: 1 merger norm bf16 [N][hidden]; 2 merger hidden bf16 [N/4][4*hidden];
+ *   layer = layers: 1 merger norm bf16 [N][S*hidden]; 2 merger hidden bf16 [N/4][S*4*hidden];
  *               3 output f32 [N/4][out_dim] (item order)
+ * where S = 2 with VIT_ACT_BF16X2 (each row holds hi then lo halves; for the
+ * merger norm each patch row is [hi | lo]) and 1 otherwise, and mlp_pad is
+ * mlp_dim rounded up to a multiple of 64 (columns past mlp_dim are zero).
  * dst_bytes must cover the tensor; VIT_E_WORKSPACE otherwise. */
 vit_status vit_debug_stage(const vit_ctx* ctx, const vit_plan* plan, const uint8_t* pixels_u8,
                            void* ws, size_t ws_bytes, int32_t layer, int32_t step, void* dst,

@@ -24,6 +24,7 @@ VIT_OK, VIT_E_ARG, VIT_E_SHAPE, VIT_E_WEIGHTS, VIT_E_WORKSPACE, VIT_E_STATE, VIT
 VIT_MLP_GELU, VIT_MLP_SWIGLU = 0, 1
 VIT_NORM_LAYER, VIT_NORM_RMS = 0, 1
 VIT_F32, VIT_BF16 = 0, 1
+VIT_ACT_BF16, VIT_ACT_BF16X2 = 0, 1
 MAX_FULL_LAYERS = 64
 
 _STATUS_NAMES = {0: "VIT_OK", 1: "VIT_E_ARG", 2: "VIT_E_SHAPE", 3: "VIT_E_WEIGHTS",
@@ -44,6 +45,7 @@ class vit_config(ctypes.Structure):
         ("merge", ctypes.c_int32), ("out_dim", ctypes.c_int32), ("rope_theta", ctypes.c_float),
         ("mean", ctypes.c_float * 3), ("std", ctypes.c_float * 3), ("window_px", ctypes.c_int32),
         ("n_full_attn_layers", ctypes.c_int32), ("full_attn_layers", ctypes.c_int32 * MAX_FULL_LAYERS),
+        ("activation_precision", ctypes.c_int32),
     ]
 
 
@@ -111,9 +113,13 @@ def _check(lib, status: int):
         raise VitError(status, lib.vit_last_error().decode())
 
 
-def make_config(cfg) -> vit_config:
-    """vit_config from any object with the tower fields (e.g. workloads.TowerConfig)."""
+def make_config(cfg, activation_precision: str = "bf16x2") -> vit_config:
+    """vit_config from any object with the tower fields (e.g. workloads.TowerConfig).
+
+    activation_precision: "bf16x2" (hi+lo activation pairs for the norm, MLP and
+    merger GEMM inputs; the default) or "bf16"."""
     c = vit_config()
+    c.activation_precision = {"bf16": VIT_ACT_BF16, "bf16x2": VIT_ACT_BF16X2}[activation_precision]
     c.hidden, c.heads, c.layers, c.mlp_dim = cfg.hidden, cfg.heads, cfg.layers, cfg.mlp_dim
     c.mlp_kind = VIT_MLP_GELU if cfg.mlp_kind == "gelu" else VIT_MLP_SWIGLU
     c.norm_kind = VIT_NORM_LAYER if cfg.norm_kind == "layer" else VIT_NORM_RMS
@@ -216,10 +222,12 @@ class Graph:
 class VisionTower:
     """Owns one vit_ctx: configuration, weights (host copies until finalize, then a device arena)."""
 
-    def __init__(self, cfg, lib: Optional[ctypes.CDLL] = None):
+    def __init__(self, cfg, lib: Optional[ctypes.CDLL] = None, activation_precision: str = "bf16x2"):
         self.lib = lib or load_library()
         self.cfg = cfg
-        c = make_config(cfg)
+        self.activation_precision = activation_precision
+        self.split = 2 if activation_precision == "bf16x2" else 1
+        c = make_config(cfg, activation_precision)
         self.handle = _P()
         _check(self.lib, self.lib.vit_create(ctypes.byref(c), ctypes.byref(self.handle)))
 

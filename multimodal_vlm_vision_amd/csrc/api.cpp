@@ -75,7 +75,8 @@ vit_status check_common(const vit_ctx* ctx, const vit_plan* plan, const void* ws
     return VIT_E_STATE;
   }
   if (plan->cfg.hidden != ctx->cfg.hidden || plan->cfg.layers != ctx->cfg.layers ||
-      plan->cfg.window_px != ctx->cfg.window_px || plan->head_dim != ctx->head_dim) {
+      plan->cfg.window_px != ctx->cfg.window_px || plan->head_dim != ctx->head_dim ||
+      plan->split != ctx->split) {
     set_error("plan was built for a different tower configuration");
     return VIT_E_ARG;
   }
@@ -141,6 +142,8 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   const DeviceWeights& W = ctx->w;
   const int64_t N = pl->n_rows;
   const int d = c.hidden, hd = ctx->head_dim, mp = ctx->mlp_pad;
+  const int S = ctx->split;            // 2: activations stored as [hi | lo] rows
+  const bool split = S == 2;
   const double Nd = (double)N, dd = (double)d;
   if (N == 0) return VIT_OK;
   if (prof) prof->st = st;
@@ -185,12 +188,12 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   for (int l = 0; l < c.layers; ++l) {
     const LayerW& L = W.layers[l];
     LAUNCH("rownorm", 0, norm_bytes, false,
-           launch_rownorm(c.norm_kind, R, N, d, L.n1g, L.n1b, c.norm_eps, H, st));
-    if (stop.hit(l, 1)) return copy_out(stop, H, (size_t)N * d * 2, st);
+           launch_rownorm(c.norm_kind, R, N, d, L.n1g, L.n1b, c.norm_eps, H, split, st));
+    if (stop.hit(l, 1)) return copy_out(stop, H, (size_t)N * S * d * 2, st);
 
     GemmArgs q;
-    q.A = H; q.lda = d; q.B = L.qkv_w; q.ldb = d;
-    q.M = (int)N; q.N = 3 * d; q.K = d; q.bias = L.qkv_b;
+    q.A = H; q.lda = S * d; q.B = L.qkv_w; q.ldb = S * d;
+    q.M = (int)N; q.N = 3 * d; q.K = S * d; q.bias = L.qkv_b;
     q.q = Q; q.k = K; q.vt = VT; q.n_tok = N;
     q.row_pos = rowpos; q.cos_tab = cos_t; q.sin_tab = sin_t;
     q.nfreq = pl->nfreq; q.head_dim = hd; q.hidden = d;
@@ -224,12 +227,13 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     if (stop.hit(l, 6)) return copy_out(stop, R, (size_t)N * d * 4, st);
 
     LAUNCH("rownorm", 0, norm_bytes, false,
-           launch_rownorm(c.norm_kind, R, N, d, L.n2g, L.n2b, c.norm_eps, H, st));
-    if (stop.hit(l, 7)) return copy_out(stop, H, (size_t)N * d * 2, st);
+           launch_rownorm(c.norm_kind, R, N, d, L.n2g, L.n2b, c.norm_eps, H, split, st));
+    if (stop.hit(l, 7)) return copy_out(stop, H, (size_t)N * S * d * 2, st);
 
     GemmArgs f1;
-    f1.A = H; f1.lda = d; f1.B = L.fc1_w; f1.ldb = d;
-    f1.M = (int)N; f1.K = d; f1.bias = L.fc1_b; f1.out = F; f1.ldo = mp;
+    f1.A = H; f1.lda = S * d; f1.B = L.fc1_w; f1.ldb = S * d;
+    f1.M = (int)N; f1.K = S * d; f1.bias = L.fc1_b; f1.out = F; f1.ldo = S * mp;
+    f1.split_off = split ? mp : 0;
     if (c.mlp_kind == VIT_MLP_GELU) {
       f1.N = mp;
       LAUNCH("gemm_fc1_gelu", 2.0 * Nd * c.mlp_dim * dd, 0, true, launch_gemm(EPI_GELU, f1, st));
@@ -238,17 +242,11 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
       LAUNCH("gemm_gateup_swiglu", 4.0 * Nd * c.mlp_dim * dd, 0, true,
              launch_gemm(EPI_SWIGLU, f1, st));
     }
-    if (stop.hit(l, 8)) {
-      if (stop.dst_bytes < (size_t)N * c.mlp_dim * 2)
-        return copy_out(stop, F, (size_t)N * c.mlp_dim * 2, st);
-      HIP_TRY(hipMemcpy2DAsync(stop.dst, (size_t)c.mlp_dim * 2, F, (size_t)mp * 2,
-                               (size_t)c.mlp_dim * 2, N, hipMemcpyDeviceToDevice, st));
-      return VIT_OK;
-    }
+    if (stop.hit(l, 8)) return copy_out(stop, F, (size_t)N * S * mp * 2, st);
 
     GemmArgs f2;
-    f2.A = F; f2.lda = mp; f2.B = L.fc2_w; f2.ldb = mp;
-    f2.M = (int)N; f2.N = d; f2.K = mp; f2.bias = L.fc2_b; f2.out = R; f2.ldo = d;
+    f2.A = F; f2.lda = S * mp; f2.B = L.fc2_w; f2.ldb = S * mp;
+    f2.M = (int)N; f2.N = d; f2.K = S * mp; f2.bias = L.fc2_b; f2.out = R; f2.ldo = d;
     LAUNCH("gemm_fc2_residual", 2.0 * Nd * dd * c.mlp_dim, 0, true, launch_gemm(EPI_RES, f2, st));
     if (stop.hit(l, 9)) return copy_out(stop, R, (size_t)N * d * 4, st);
   }
@@ -256,18 +254,19 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   // merger: per-patch norm, 4 rows -> one 4d vector (free: rows are adjacent), MLP
   const int L = c.layers;
   LAUNCH("rownorm", 0, norm_bytes, false,
-         launch_rownorm(c.norm_kind, R, N, d, W.mq_g, W.mq_b, c.norm_eps, H, st));
-  if (stop.hit(L, 1)) return copy_out(stop, H, (size_t)N * d * 2, st);
+         launch_rownorm(c.norm_kind, R, N, d, W.mq_g, W.mq_b, c.norm_eps, H, split, st));
+  if (stop.hit(L, 1)) return copy_out(stop, H, (size_t)N * S * d * 2, st);
   const int64_t U = pl->n_units;
   const double Ud = (double)U;
   GemmArgs m1;
-  m1.A = H; m1.lda = 4 * d; m1.B = W.m1_w; m1.ldb = 4 * d;
-  m1.M = (int)U; m1.N = 4 * d; m1.K = 4 * d; m1.bias = W.m1_b; m1.out = F; m1.ldo = 4 * d;
+  m1.A = H; m1.lda = S * 4 * d; m1.B = W.m1_w; m1.ldb = S * 4 * d;
+  m1.M = (int)U; m1.N = 4 * d; m1.K = S * 4 * d; m1.bias = W.m1_b; m1.out = F; m1.ldo = S * 4 * d;
+  m1.split_off = split ? 4 * d : 0;
   LAUNCH("gemm_merger_fc1_gelu", 2.0 * Ud * 16 * dd * dd, 0, true, launch_gemm(EPI_GELU, m1, st));
-  if (stop.hit(L, 2)) return copy_out(stop, F, (size_t)U * 4 * d * 2, st);
+  if (stop.hit(L, 2)) return copy_out(stop, F, (size_t)U * S * 4 * d * 2, st);
   GemmArgs m2;
-  m2.A = F; m2.lda = 4 * d; m2.B = W.m2_w; m2.ldb = 4 * d;
-  m2.M = (int)U; m2.N = c.out_dim; m2.K = 4 * d; m2.bias = W.m2_b; m2.out = out; m2.ldo = c.out_dim;
+  m2.A = F; m2.lda = S * 4 * d; m2.B = W.m2_w; m2.ldb = S * 4 * d;
+  m2.M = (int)U; m2.N = c.out_dim; m2.K = S * 4 * d; m2.bias = W.m2_b; m2.out = out; m2.ldo = c.out_dim;
   m2.row_map = unitdst;
   LAUNCH("gemm_merger_fc2", 2.0 * Ud * c.out_dim * 4 * dd, 0, true, launch_gemm(EPI_OUT, m2, st));
   if (stop.hit(L, 3)) return copy_out(stop, out, (size_t)U * c.out_dim * 4, st);
@@ -317,6 +316,10 @@ vit_status validate_config(const vit_config* c, int* head_dim) {
     }
   if (c->window_px < 0 || (c->window_px % kUnitPx)) {
     set_error("window_px must be 0 or a positive multiple of 28");
+    return VIT_E_ARG;
+  }
+  if (c->activation_precision != VIT_ACT_BF16 && c->activation_precision != VIT_ACT_BF16X2) {
+    set_error("activation_precision must be VIT_ACT_BF16 or VIT_ACT_BF16X2");
     return VIT_E_ARG;
   }
   if (c->n_full_attn_layers < 0 || c->n_full_attn_layers > VIT_MAX_FULL_LAYERS) {
@@ -384,6 +387,7 @@ vit_status vit_create(const vit_config* cfg, vit_ctx** out) {
   ctx->cfg = *cfg;
   ctx->head_dim = hd;
   ctx->mlp_pad = (int)round_up(cfg->mlp_dim, 64);
+  ctx->split = cfg->activation_precision == VIT_ACT_BF16X2 ? 2 : 1;
   build_lut(*cfg, ctx->lut);
   *out = ctx;
   return VIT_OK;

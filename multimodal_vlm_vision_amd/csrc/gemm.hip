@@ -72,6 +72,18 @@ __device__ __forceinline__ float4 f4add(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
+// bf16 activation store: hi = bf16(y) at column n; with split_off, lo = bf16(y - hi) at n + split_off
+__device__ __forceinline__ void store_act(const GemmArgs& p, int m, int n, float4 y) {
+  uint16_t* o = static_cast<uint16_t*>(p.out) + (int64_t)m * p.ldo + n;
+  const uint2 hi = pack4(y);
+  *reinterpret_cast<uint2*>(o) = hi;
+  if (p.split_off) {
+    const float4 h = make_float4(__builtin_bit_cast(float, hi.x << 16), __builtin_bit_cast(float, hi.x & 0xffff0000u),
+                                 __builtin_bit_cast(float, hi.y << 16), __builtin_bit_cast(float, hi.y & 0xffff0000u));
+    *reinterpret_cast<uint2*>(o + p.split_off) = pack4(make_float4(y.x - h.x, y.y - h.y, y.z - h.z, y.w - h.w));
+  }
+}
+
 template <int BM, int BN, int WM, int WN>
 struct Tile {
   static constexpr int NW = WM * WN;
@@ -111,10 +123,9 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
           *o = f4add(*o, f4add(v, b));
         } else if (EPI == EPI_OUT) {
           *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)p.row_map[m] * p.ldo + n) = f4add(v, b);
-        } else {   // GELU -> bf16
+        } else {   // GELU -> bf16 (hi, and lo when split)
           const float4 x = f4add(v, b);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (int64_t)m * p.ldo + n) =
-              pack4(make_float4(gelu(x.x), gelu(x.y), gelu(x.z), gelu(x.w)));
+          store_act(p, m, n, make_float4(gelu(x.x), gelu(x.y), gelu(x.z), gelu(x.w)));
         }
       }
     }
@@ -134,7 +145,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
       if (EPI == EPI_SWIGLU) {
         const int oc = (n - (n & 63)) / 2 + (n & 31);
         const float4 y = make_float4(silu(a.x) * b.x, silu(a.y) * b.y, silu(a.z) * b.z, silu(a.w) * b.w);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (int64_t)m * p.ldo + oc) = pack4(y);
+        store_act(p, m, oc, y);
       } else {
         // RoPE on 4 consecutive rotary pairs of one head (head_dim/2 is a multiple of 4)
         const int d = p.hidden, hd = p.head_dim, rr = hd / 2, nf = p.nfreq;

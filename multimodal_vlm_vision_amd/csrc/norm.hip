@@ -28,8 +28,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-// VPL = float4 chunks per lane (d = 256 * VPL)
-template <int KIND, int VPL>
+__device__ __forceinline__ float bf16_lo(float x) {
+  return x - (float)(__bf16)x;
+}
+
+// VPL = float4 chunks per lane (d <= 256 * VPL).  SPLIT: each output row is
+// [hi | lo] with hi = bf16(y) and lo = bf16(y - hi), row stride 2d.
+template <int KIND, int VPL, bool SPLIT>
 __global__ void __launch_bounds__(kThreads)
 rownorm_kernel(const float* __restrict__ r, int64_t rows, int d, const float* __restrict__ g,
                const float* __restrict__ b, float eps, uint16_t* __restrict__ out) {
@@ -58,7 +63,8 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, int d, const float* __
     }
   }
   const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
-  uint2* dst = reinterpret_cast<uint2*>(out + row * d);
+  uint2* dst = reinterpret_cast<uint2*>(out + row * d * (SPLIT ? 2 : 1));
+  uint2* dst_lo = reinterpret_cast<uint2*>(out + row * d * 2 + d);
   const float4* g4 = reinterpret_cast<const float4*>(g);
   const float4* b4 = reinterpret_cast<const float4*>(b);
 #pragma unroll
@@ -76,23 +82,25 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, int d, const float* __
         y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
       }
       dst[c] = make_uint2(pack_bf16(y.x, y.y), pack_bf16(y.z, y.w));
+      if (SPLIT)
+        dst_lo[c] = make_uint2(pack_bf16(bf16_lo(y.x), bf16_lo(y.y)), pack_bf16(bf16_lo(y.z), bf16_lo(y.w)));
     }
   }
 }
 
-template <int KIND>
+template <int KIND, bool SPLIT>
 vit_status launch_kind(const float* r, int64_t rows, int d, const float* g, const float* b,
                        float eps, uint16_t* out, hipStream_t st) {
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   const int vpl = (d / 4 + 63) / 64;
   if (vpl <= 1)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 1>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 1, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
   else if (vpl <= 2)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 2>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 2, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
   else if (vpl <= 5)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 5>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 5, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
   else if (vpl <= 8)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 8>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 8, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
   else {
     set_error("rownorm: hidden %d too wide (max 2048)", d);
     return VIT_E_ARG;
@@ -103,11 +111,16 @@ vit_status launch_kind(const float* r, int64_t rows, int d, const float* g, cons
 }  // namespace
 
 vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
-                          const float* b, float eps, uint16_t* out, void* stream) {
+                          const float* b, float eps, uint16_t* out, bool split, void* stream) {
   if (rows <= 0) return VIT_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  vit_status s = kind == VIT_NORM_LAYER ? launch_kind<VIT_NORM_LAYER>(r, rows, d, g, b, eps, out, st)
-                                        : launch_kind<VIT_NORM_RMS>(r, rows, d, g, b, eps, out, st);
+  vit_status s;
+  if (kind == VIT_NORM_LAYER)
+    s = split ? launch_kind<VIT_NORM_LAYER, true>(r, rows, d, g, b, eps, out, st)
+              : launch_kind<VIT_NORM_LAYER, false>(r, rows, d, g, b, eps, out, st);
+  else
+    s = split ? launch_kind<VIT_NORM_RMS, true>(r, rows, d, g, b, eps, out, st)
+              : launch_kind<VIT_NORM_RMS, false>(r, rows, d, g, b, eps, out, st);
   if (s != VIT_OK) return s;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -67,6 +67,7 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   p->cfg = c;
   p->head_dim = ctx->head_dim;
   p->mlp_pad = ctx->mlp_pad;
+  p->split = ctx->split;
   if (n_items < 0) {
     set_error("n_items must be >= 0 (got %d)", n_items);
     return VIT_E_ARG;
@@ -197,12 +198,13 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   };
   p->off_x = take((size_t)N * kFeatPad * 2);
   p->off_r = take((size_t)N * d * 4);
-  p->off_h = take((size_t)N * d * 2);
+  const int64_t S = p->split;
+  p->off_h = take((size_t)N * S * d * 2);
   p->off_q = take((size_t)N * d * 2);
   p->off_k = take((size_t)N * d * 2);
   p->off_vt = take((size_t)N * d * 2);
   p->off_o = take((size_t)N * d * 2);
-  p->off_f = take((size_t)N * std::max<int64_t>(p->mlp_pad, d) * 2);
+  p->off_f = take((size_t)N * S * std::max<int64_t>(p->mlp_pad, d) * 2);
   p->off_pix = take(px);
   p->off_out = take((size_t)p->n_units * c.out_dim * 4);
   p->ws_bytes = off;

@@ -92,6 +92,7 @@ struct vit_ctx {
   vit_config cfg{};
   int head_dim = 0;
   int mlp_pad = 0;       // mlp_dim rounded up to 64
+  int split = 1;         // 2 with hi+lo activation pairs, else 1
   uint16_t lut[3][256];  // bf16 bits of ((x/255) - mean_c) / std_c, exactly rounded
   std::map<std::string, vitmi::HostTensor> host;
   bool finalized = false;
@@ -102,7 +103,7 @@ struct vit_ctx {
 
 struct vit_plan {
   vit_config cfg{};
-  int head_dim = 0, mlp_pad = 0;
+  int head_dim = 0, mlp_pad = 0, split = 1;
   int32_t n_items = 0;
   std::vector<int32_t> grid;      // [n][3]
   std::vector<int32_t> nframes;   // [n]
@@ -169,6 +170,8 @@ struct GemmArgs {
   int nfreq = 0, head_dim = 0, hidden = 0;
   // output scatter
   const int32_t* row_map = nullptr;
+  // GELU / SwiGLU: when nonzero, also store lo = bf16(y - bf16(y)) at column + split_off
+  int split_off = 0;
 };
 
 vit_status launch_gemm(int epi, const GemmArgs& a, void* stream);
@@ -179,8 +182,9 @@ vit_status launch_normpatch(const uint8_t* pixels, const UnitDesc* units, int64_
                             const uint16_t* lut, uint16_t* x, void* stream);
 vit_status launch_normrows_u8(const uint8_t* patches, int64_t n_rows, const uint16_t* lut,
                               uint16_t* x, void* stream);
+// Row norm of fp32 rows [rows][d] into bf16; split: output rows [hi(d) | lo(d)] (stride 2d).
 vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
-                          const float* b, float eps, uint16_t* out, void* stream);
+                          const float* b, float eps, uint16_t* out, bool split, void* stream);
 
 struct AttnArgs {
   const uint16_t* q = nullptr; const uint16_t* k = nullptr; const uint16_t* vt = nullptr;

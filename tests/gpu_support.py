@@ -18,11 +18,13 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 
 class GpuRun:
-    def __init__(self, wl):
+    def __init__(self, wl, activation_precision: str = "bf16x2"):
         self.wl = wl
         cfg = wl.cfg
         self.cfg = cfg
-        self.tower = VisionTower(cfg)
+        self.S = 2 if activation_precision == "bf16x2" else 1
+        self.mlp_pad = (cfg.mlp_dim + 63) // 64 * 64
+        self.tower = VisionTower(cfg, activation_precision=activation_precision)
         self.tower.load_weights(wl.weights)
         self.tower.finalize()
         self.plan = self.tower.plan(wl.grid_thw, wl.n_frames)
@@ -38,26 +40,38 @@ class GpuRun:
         torch.cuda.synchronize()
         return self.out[: self.plan.out_rows].cpu().numpy().astype(np.float64)
 
+    def _join(self, a: np.ndarray, width: int, keep: int) -> np.ndarray:
+        """[rows][S*width] stored activations -> values (hi + lo when split), first `keep` columns."""
+        if self.S == 2:
+            return a[:, :keep] + a[:, width:width + keep]
+        return a[:, :keep]
+
     def stage(self, layer: int, step: int) -> np.ndarray:
-        """An intermediate, reshaped, rows in *merge order* (token-major)."""
-        c, n = self.cfg, self.n
+        """An intermediate as values (hi + lo joined), rows in *merge order* (token-major)."""
+        c, n, S = self.cfg, self.n, self.S
         d, h, hd = c.hidden, c.heads, c.head_dim
         L = c.layers
         if layer == -1:
             shape, dt = ((n, 1176), torch.bfloat16) if step == 0 else ((n, d), torch.float32)
         elif layer == L:
-            shape, dt = {1: ((n, d), torch.bfloat16), 2: ((n // 4, 4 * d), torch.bfloat16),
+            shape, dt = {1: ((n, S * d), torch.bfloat16), 2: ((n // 4, S * 4 * d), torch.bfloat16),
                          3: ((n // 4, c.out_dim), torch.float32)}[step]
         else:
-            shape, dt = {1: ((n, d), torch.bfloat16), 2: ((h, n, hd), torch.bfloat16),
+            shape, dt = {1: ((n, S * d), torch.bfloat16), 2: ((h, n, hd), torch.bfloat16),
                          3: ((h, n, hd), torch.bfloat16), 4: ((h, hd, n), torch.bfloat16),
                          5: ((n, d), torch.bfloat16), 6: ((n, d), torch.float32),
-                         7: ((n, d), torch.bfloat16), 8: ((n, c.mlp_dim), torch.bfloat16),
+                         7: ((n, S * d), torch.bfloat16), 8: ((n, S * self.mlp_pad), torch.bfloat16),
                          9: ((n, d), torch.float32)}[step]
         dst = torch.empty(shape, dtype=dt, device="cuda")
         self.tower.debug_stage(self.plan, self.pixels, self.ws, layer, step, dst)
         torch.cuda.synchronize()
         a = to_np(dst)
+        if (layer == L and step == 1) or (0 <= layer < L and step in (1, 7)):
+            a = self._join(a, d, d)
+        elif 0 <= layer < L and step == 8:
+            a = self._join(a, self.mlp_pad, c.mlp_dim)
+        elif layer == L and step == 2:
+            a = self._join(a, 4 * d, 4 * d)
         if layer != -1 and layer != c.layers and step in (2, 3):
             a = a.transpose(1, 0, 2)                  # -> [n][heads][hd]
         if layer != -1 and layer != c.layers and step == 4:

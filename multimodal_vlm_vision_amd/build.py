@@ -39,10 +39,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# attention keeps its MFMA accumulators in architectural VGPRs: its softmax
+# reads and rescales them, and AGPR <-> VGPR copies would cost more VALU than
+# the softmax itself
+PER_FILE = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *PER_FILE.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)

@@ -13,15 +13,24 @@
 // probabilities are already the B operand of O^T = V^T P^T (the 32-key
 // reduction slots of a lane are its 4 keys of each of two 16-key tiles; V^T
 // fragments are read with the same key permutation), so P never leaves
-// registers, and each lane owns the running max / sum of the one query its
-// O^T columns belong to.  Online softmax in fp32 with exp2 and the 1/sqrt(d)
-// scale folded into the exponent; P is rounded to bf16 for the MFMA.
+// registers, and each lane owns the running max of the one query its O^T
+// columns belong to.  The softmax denominator comes out of the same MFMA
+// chain: one extra 16-row tile of O^T multiplies P by an all-ones operand.
+// Online softmax in fp32 with exp2 and the 1/sqrt(d) scale folded into the
+// exponent; P is rounded to bf16 for the MFMA.  The running max is only
+// raised (and O, l rescaled) when a block's max exceeds it by more than 2^8,
+// which keeps the rescale off the common path without changing the math.
 //
-// K tiles (64 keys x head_dim, row stride head_dim + 8 elements) and V^T
-// tiles (head_dim x 64 keys, row stride 68) are staged in a double-buffered
-// LDS ring.  Long segments use 4-wave workgroups (256 queries share each
-// K/V tile, next tile prefetched into registers); short segments (windows)
-// use 1-wave workgroups of 64 queries.
+// Per-score VALU work is what bounds this kernel on CDNA4 (exp runs at a
+// quarter of the FMA rate), so a step is 32 keys x 64 queries per wave, the
+// whole state fits in 256 registers and two waves share each SIMD, letting
+// one wave's MFMAs run under the other's softmax.  K tiles (32 keys x head_dim,
+// row stride head_dim + 8) and V^T tiles (head_dim x 32 keys, row stride 36)
+// move global -> LDS with gfx950's direct loads into a double-buffered ring.
+// Work units are laid out so each XCD (workgroups are dispatched round-robin
+// over 8 XCDs) runs contiguous (head, segment) ranges and shares their K/V in
+// its L2.  Long segments use 4-wave workgroups (256 queries share each K/V
+// tile); short segments (windows) use 1-wave workgroups of 64 queries.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -36,29 +45,38 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-constexpr int KB = 64;   // keys per step
+constexpr int KB = 32;   // keys per step
 constexpr int QT = 4;    // 16-query tiles per wave (64 queries)
 
 template <int HD, int NW>
-__global__ void __launch_bounds__(NW * 64)
-attn_kernel(AttnArgs a, const AttnWork* __restrict__ work) {
-  constexpr int KS = HD + 8;
-  constexpr int VS = KB + 4;
-  constexpr int NC = HD / 32;
+__global__ void __launch_bounds__(NW * 64, 2)
+attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
+  constexpr int KS = HD + 8;             // K tile row stride (elements): 16-byte chunks
+  constexpr int KCH = KS / 8;            // chunks per LDS row (the last one is padding)
+  constexpr int KLOADS = (KB * KCH + 63) / 64;     // 1 KB direct loads per K tile
+  constexpr int VS = KB + 4;             // V^T tile row stride (elements)
+  constexpr int VDW = VS / 2;            // dwords per V^T row
+  constexpr int VLOADS = (HD * VDW + 63) / 64;     // 256 B direct loads per V^T tile
+  // 32-wide reduction chunks of the head dim; with head_dim = 16 (mod 32) the last chunk
+  // holds 16 dims in its first two lane groups and zeros in the other two (a 16x16x16 MFMA
+  // costs as many cycles as a 16x16x32 one, so the padding is free)
+  constexpr int NC = (HD + 31) / 32;
   constexpr bool TAIL = (HD % 32) == 16;
   constexpr int ND = HD / 16;
-  constexpr int NT = NW * 64;
-  constexpr int KCH = KB * HD / 8;   // 16-byte chunks per K tile
-  constexpr int VCH = HD * KB / 4;   // 8-byte chunks per V^T tile
-  constexpr int KPT = (KCH + NT - 1) / NT;
-  constexpr int VPT = (VCH + NT - 1) / NT;
-  static_assert(HD % 16 == 0, "head_dim must be a multiple of 16");
+  static_assert(HD % 16 == 0 && (KS * 2) % 16 == 0, "head_dim must be a multiple of 16");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KB * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][HD * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KLOADS * 64 * 8];
+  __shared__ __attribute__((aligned(16))) uint32_t sV[2][VLOADS * 64];
 
-  const AttnWork wk = work[blockIdx.x];
-  const int head = blockIdx.y;
+  // ---- work unit: XCD-contiguous ranges of (head, unit), units of a segment adjacent
+  const int G = n_work * a.heads;
+  const int pid = blockIdx.x;
+  const int xcd = pid & 7, local = pid >> 3;
+  const int per = G >> 3, rem = G & 7;
+  const int logical = xcd * per + min(xcd, rem) + local;
+  const int head = logical / n_work;
+  const AttnWork wk = work[logical % n_work];
+
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int seg0 = wk.seg_start, n = wk.seg_len;
@@ -69,7 +87,6 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work) {
 
   // ---- this wave's query fragments (B operand of S^T = K Q^T)
   bf16x8 qa[QT][NC];
-  bf16x4 qt4[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int q = qbase + 16 * t + l16;
@@ -77,92 +94,76 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work) {
     const uint16_t* qr = Qh + (int64_t)(seg0 + (ok ? q : 0)) * HD;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + c * 32 + g4 * 8);
-      qa[t][c] = ok ? v : bf16x8{};
-    }
-    if constexpr (TAIL) {
-      bf16x4 v = *reinterpret_cast<const bf16x4*>(qr + NC * 32 + g4 * 4);
-      qt4[t] = ok ? v : bf16x4{};
+      const bool live = ok && (!TAIL || c < NC - 1 || g4 < 2);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + (live ? c * 32 + g4 * 8 : 0));
+      qa[t][c] = live ? v : bf16x8{};
     }
   }
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
 
-  f32x4 O[ND][QT];
-  float m[QT], l[QT];
+  f32x4 O[ND][QT], Ls[QT];   // O^T tiles and the row-sum tile (every row holds l)
+  float m[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    m[t] = -INFINITY;
-    l[t] = 0.f;
+    m[t] = 0.f;
+    Ls[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) O[dt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sc = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(head_dim)
   const int nkb = (n + KB - 1) / KB;
 
-  uint4 rk[KPT];
-  uint2 rv[VPT];
-  auto gload = [&](int kb) {
+  // Direct global -> LDS tile loads.  Keys past the segment end read the last key (K) or
+  // the last key pair (V^T): their scores are masked to -inf, so they contribute P = 0.
+  auto dload = [&](int kb, int buf) {
     const int key0 = kb * KB;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int id = tid + i * NT;
-      if (id < KCH) {
-        const int r = id / (HD / 8), c = id % (HD / 8), key = key0 + r;
-        rk[i] = key < n ? *reinterpret_cast<const uint4*>(Kh + (int64_t)(seg0 + key) * HD + c * 8)
-                        : make_uint4(0, 0, 0, 0);
-      }
+    for (int j = 0; j < (KLOADS + NW - 1) / NW; ++j) {
+      const int i = wv + j * NW;
+      if (i >= KLOADS) break;
+      const int id = i * 64 + lane, r = id / KCH, c = id % KCH;
+      const int key = min(key0 + r, n - 1);
+      const uint16_t* src = Kh + (int64_t)(seg0 + key) * HD + (c < HD / 8 ? c * 8 : 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(&sK[buf][i * 64 * 8]), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int id = tid + i * NT;
-      if (id < VCH) {
-        const int dd = id / (KB / 4), c = id % (KB / 4), key = key0 + 4 * c;
-        rv[i] = key < n ? *reinterpret_cast<const uint2*>(Vh + (int64_t)dd * a.n_tok + seg0 + key)
-                        : make_uint2(0, 0);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int id = tid + i * NT;
-      if (id < KCH) {
-        const int r = id / (HD / 8), c = id % (HD / 8);
-        *reinterpret_cast<uint4*>(&sK[buf][r * KS + c * 8]) = rk[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int id = tid + i * NT;
-      if (id < VCH) {
-        const int dd = id / (KB / 4), c = id % (KB / 4);
-        *reinterpret_cast<uint2*>(&sV[buf][dd * VS + 4 * c]) = rv[i];
-      }
+    for (int j = 0; j < (VLOADS + NW - 1) / NW; ++j) {
+      const int i = wv + j * NW;
+      if (i >= VLOADS) break;
+      const int id = i * 64 + lane, dd = id / VDW, c = id % VDW;
+      const int key = min(key0 + 2 * c, n - 2);
+      const uint16_t* src = (dd < HD && c < KB / 2) ? Vh + (int64_t)dd * a.n_tok + seg0 + key : Vh;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(&sV[buf][i * 64]), 4, 0, 0);
     }
   };
 
-  gload(0);
-  sstore(0);
+  dload(0, 0);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
-    if (NW > 1 && kb + 1 < nkb) gload(kb + 1);
+    if (kb + 1 < nkb) dload(kb + 1, buf ^ 1);
     if (qbase < n) {
-      // ---- S^T tiles: 4 key tiles x QT query tiles
-      f32x4 S[4][QT];
+      const uint16_t* Kt = sK[buf];
+      const uint16_t* Vt = reinterpret_cast<const uint16_t*>(sV[buf]);
+      // ---- S^T tiles: 2 key tiles x QT query tiles
+      f32x4 S[2][QT];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const uint16_t* kr = &sK[buf][(kt * 16 + l16) * KS];
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint16_t* kr = Kt + (kt * 16 + l16) * KS;
         bf16x8 ka[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) ka[c] = *reinterpret_cast<const bf16x8*>(kr + c * 32 + g4 * 8);
-        bf16x4 kb4{};
-        if constexpr (TAIL) kb4 = *reinterpret_cast<const bf16x4*>(kr + NC * 32 + g4 * 4);
+        // upper lane groups of a half chunk read the row padding and the next row: zero them
+        if constexpr (TAIL) ka[NC - 1] = g4 < 2 ? ka[NC - 1] : bf16x8{};
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
           f32x4 s{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < NC; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qa[t][c], s, 0, 0, 0);
-          if constexpr (TAIL) s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kb4, qt4[t], s, 0, 0, 0);
           S[kt][t] = s;
         }
       }
@@ -170,65 +171,54 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work) {
       const int key_base = kb * KB;
       if (key_base + KB > n) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (key_base + kt * 16 + g4 * 4 + i >= n)
 #pragma unroll
               for (int t = 0; t < QT; ++t) S[kt][t][i] = -INFINITY;
       }
-      // ---- online softmax per query column
+      // ---- online softmax per query column (lazy offset: raised only by > 2^8)
+      bf16x8 pb[QT];
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
-        float mx = S[0][t][0];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kt][t][i]);
+        float mx = fmaxf(fmaxf(fmaxf(S[0][t][0], S[0][t][1]), fmaxf(S[0][t][2], S[0][t][3])),
+                         fmaxf(fmaxf(S[1][t][0], S[1][t][1]), fmaxf(S[1][t][2], S[1][t][3])));
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m[t], mx * sc);
-        const float alpha = __builtin_amdgcn_exp2f(m[t] - mnew);
-        m[t] = mnew;
-        float ls = l[t] * alpha;
+        const float bm = mx * sc;
+        if (kb == 0) {
+          m[t] = bm;
+        } else {
+          const bool need = bm > m[t] + 8.0f;
+          if (__builtin_amdgcn_ballot_w64(need)) {
+            const float mn = need ? bm : m[t];
+            const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
+            m[t] = mn;
+            Ls[t] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) O[dt][t] *= alpha;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(S[kt][t][i] * sc - mnew);
-            S[kt][t][i] = pv;
-            ls += pv;
-          }
-        l[t] = ls;
-      }
-      // ---- O^T += V^T P^T over two 32-key chunks
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8 pb[QT];
-#pragma unroll
-        for (int t = 0; t < QT; ++t) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pb[t][i] = (__bf16)S[2 * j][t][i];
-            pb[t][4 + i] = (__bf16)S[2 * j + 1][t][i];
+            for (int dt = 0; dt < ND; ++dt) O[dt][t] *= alpha;
           }
         }
+        const float mo = m[t];
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-          const uint16_t* vr = &sV[buf][(dt * 16 + l16) * VS + 32 * j + g4 * 4];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int t = 0; t < QT; ++t) O[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[t], O[dt][t], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          pb[t][i] = (__bf16)__builtin_amdgcn_exp2f(S[0][t][i] * sc - mo);
+          pb[t][4 + i] = (__bf16)__builtin_amdgcn_exp2f(S[1][t][i] * sc - mo);
         }
       }
-    }
-    if (kb + 1 < nkb) {
-      if (NW == 1) gload(kb + 1);
-      sstore((kb + 1) & 1);
+      // ---- O^T += V^T P^T (and l += 1^T P^T) over the 32 keys
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const uint16_t* vr = Vt + (dt * 16 + l16) * VS + g4 * 4;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int t = 0; t < QT; ++t) O[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[t], O[dt][t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < QT; ++t) Ls[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t], Ls[t], 0, 0, 0);
     }
     __syncthreads();
   }
@@ -237,12 +227,9 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work) {
   const int ld = a.heads * HD;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    float ls = l[t];
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
     const int q = qbase + 16 * t + l16;
     if (q < n) {
-      const float inv = 1.0f / ls;
+      const float inv = 1.0f / Ls[t][0];
       uint16_t* orow = a.o + (int64_t)(seg0 + q) * ld + head * HD + g4 * 4;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
@@ -260,9 +247,11 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work) {
 template <int HD>
 hipError_t run_hd(const AttnArgs& a, hipStream_t st) {
   if (a.n_long > 0)
-    hipLaunchKernelGGL((attn_kernel<HD, 4>), dim3(a.n_long, a.heads), dim3(256), 0, st, a, a.work_long);
+    hipLaunchKernelGGL((attn_kernel<HD, 4>), dim3(a.n_long * a.heads), dim3(256), 0, st, a, a.work_long,
+                       a.n_long);
   if (a.n_short > 0)
-    hipLaunchKernelGGL((attn_kernel<HD, 1>), dim3(a.n_short, a.heads), dim3(64), 0, st, a, a.work_short);
+    hipLaunchKernelGGL((attn_kernel<HD, 1>), dim3(a.n_short * a.heads), dim3(64), 0, st, a, a.work_short,
+                       a.n_short);
   return hipGetLastError();
 }
 

@@ -192,8 +192,8 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     if (stop.hit(l, 1)) return copy_out(stop, H, (size_t)N * S * d * 2, st);
 
     GemmArgs q;
-    q.A = H; q.lda = S * d; q.B = L.qkv_w; q.ldb = S * d;
-    q.M = (int)N; q.N = 3 * d; q.K = S * d; q.bias = L.qkv_b;
+    q.A = H; q.lda = S * d; q.B = L.qkv_w; q.ldb = d; q.a_group = split ? d : 0;
+    q.M = (int)N; q.N = 3 * d; q.K = d; q.bias = L.qkv_b;
     q.q = Q; q.k = K; q.vt = VT; q.n_tok = N;
     q.row_pos = rowpos; q.cos_tab = cos_t; q.sin_tab = sin_t;
     q.nfreq = pl->nfreq; q.head_dim = hd; q.hidden = d;
@@ -231,8 +231,8 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     if (stop.hit(l, 7)) return copy_out(stop, H, (size_t)N * S * d * 2, st);
 
     GemmArgs f1;
-    f1.A = H; f1.lda = S * d; f1.B = L.fc1_w; f1.ldb = S * d;
-    f1.M = (int)N; f1.K = S * d; f1.bias = L.fc1_b; f1.out = F; f1.ldo = S * mp;
+    f1.A = H; f1.lda = S * d; f1.B = L.fc1_w; f1.ldb = d; f1.a_group = split ? d : 0;
+    f1.M = (int)N; f1.K = d; f1.bias = L.fc1_b; f1.out = F; f1.ldo = S * mp;
     f1.split_off = split ? mp : 0;
     if (c.mlp_kind == VIT_MLP_GELU) {
       f1.N = mp;
@@ -245,8 +245,8 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     if (stop.hit(l, 8)) return copy_out(stop, F, (size_t)N * S * mp * 2, st);
 
     GemmArgs f2;
-    f2.A = F; f2.lda = S * mp; f2.B = L.fc2_w; f2.ldb = S * mp;
-    f2.M = (int)N; f2.N = d; f2.K = S * mp; f2.bias = L.fc2_b; f2.out = R; f2.ldo = d;
+    f2.A = F; f2.lda = S * mp; f2.B = L.fc2_w; f2.ldb = mp; f2.a_group = split ? mp : 0;
+    f2.M = (int)N; f2.N = d; f2.K = mp; f2.bias = L.fc2_b; f2.out = R; f2.ldo = d;
     LAUNCH("gemm_fc2_residual", 2.0 * Nd * dd * c.mlp_dim, 0, true, launch_gemm(EPI_RES, f2, st));
     if (stop.hit(l, 9)) return copy_out(stop, R, (size_t)N * d * 4, st);
   }
@@ -259,14 +259,14 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   const int64_t U = pl->n_units;
   const double Ud = (double)U;
   GemmArgs m1;
-  m1.A = H; m1.lda = S * 4 * d; m1.B = W.m1_w; m1.ldb = S * 4 * d;
-  m1.M = (int)U; m1.N = 4 * d; m1.K = S * 4 * d; m1.bias = W.m1_b; m1.out = F; m1.ldo = S * 4 * d;
+  m1.A = H; m1.lda = S * 4 * d; m1.B = W.m1_w; m1.ldb = 4 * d; m1.a_group = split ? d : 0;
+  m1.M = (int)U; m1.N = 4 * d; m1.K = 4 * d; m1.bias = W.m1_b; m1.out = F; m1.ldo = S * 4 * d;
   m1.split_off = split ? 4 * d : 0;
   LAUNCH("gemm_merger_fc1_gelu", 2.0 * Ud * 16 * dd * dd, 0, true, launch_gemm(EPI_GELU, m1, st));
   if (stop.hit(L, 2)) return copy_out(stop, F, (size_t)U * S * 4 * d * 2, st);
   GemmArgs m2;
-  m2.A = F; m2.lda = S * 4 * d; m2.B = W.m2_w; m2.ldb = S * 4 * d;
-  m2.M = (int)U; m2.N = c.out_dim; m2.K = S * 4 * d; m2.bias = W.m2_b; m2.out = out; m2.ldo = c.out_dim;
+  m2.A = F; m2.lda = S * 4 * d; m2.B = W.m2_w; m2.ldb = 4 * d; m2.a_group = split ? 4 * d : 0;
+  m2.M = (int)U; m2.N = c.out_dim; m2.K = 4 * d; m2.bias = W.m2_b; m2.out = out; m2.ldo = c.out_dim;
   m2.row_map = unitdst;
   LAUNCH("gemm_merger_fc2", 2.0 * Ud * c.out_dim * 4 * dd, 0, true, launch_gemm(EPI_OUT, m2, st));
   if (stop.hit(L, 3)) return copy_out(stop, out, (size_t)U * c.out_dim * 4, st);

@@ -10,16 +10,28 @@
 // exact-erf GELU, SiLU(gate)*up, residual add into the fp32 stream, the 2D
 // RoPE of q and k (section 3.3), and the merger's row scatter.
 //
-// Main loop: BM x BN workgroup tile, BK = 64, WM x WN waves, each wave owning
-// (BM/WM) x (BN/WN) as 32x32 MFMA tiles.  Tiles move global -> LDS with
-// gfx950's direct loads (global_load_lds_dwordx4: no VGPR staging, no
-// ds_write), double-buffered; each wave's 1 KB load covers 8 tile rows and
-// its lanes fetch the 16-byte chunks in the XOR-swizzled order the fragment
-// reads expect (chunk ^ ((row >> 1) & 7), so 16 consecutive rows hit
-// distinct banks).  MFMA operand fragments are double-buffered in registers
-// one 16-wide K step ahead.  Workgroups are remapped so each XCD (dispatch is
-// round-robin over 8 XCDs) runs a contiguous range of tiles, grouped 8
-// row-tiles deep, to keep A and B panels in its L2.
+// Split activations: an A row may hold each activation as a pair
+// hi = bf16(x), lo = bf16(x - hi), laid out in groups of g columns
+// ([hi(g) | lo(g)] repeated).  The kernel then accumulates hi*w + lo*w
+// against ONE copy of the weight tile: every B fragment read from LDS feeds
+// two MFMAs, so the pair costs twice the MFMA work but not twice the B
+// traffic.
+//
+// Main loop (per workgroup tile BM x BN, 2x2 waves of (BM/2) x (BN/2)):
+//  * K advances 32 columns per stage.  Tiles move global -> LDS with gfx950's
+//    buffer loads into LDS (no VGPR staging): every lane keeps one fixed
+//    32-bit row offset per load and the K advance rides in the scalar
+//    offset.  LDS rows are 64 bytes; the four 16-byte chunks of row r sit
+//    at chunk ^ (((r >> 1) ^ (r >> 3)) & 3), so the 32x32x16 fragment reads
+//    (32 rows, one chunk) touch distinct banks in every 8- and 16-lane group.
+//  * A ring of 3-4 stages: the loads for stage kt+S-1 are issued while stage
+//    kt is multiplied; one barrier per stage, preceded by an exact vmcnt
+//    wait for the next stage only, so later stages stay in flight.
+//  * MFMA operand fragments are double-buffered in registers: the reads for
+//    the next 16-wide K step are interleaved with the current step's MFMAs.
+//  * Workgroups are remapped so each XCD (dispatch is round-robin over 8
+//    XCDs) runs a contiguous range of tiles, grouped 8 row-tiles deep, to
+//    keep A and B panels in its L2.
 //
 // Epilogue: the accumulators are staged through LDS one 32-row slice at a
 // time, so every global access of the epilogue is a 16-byte (fp32) or 8-byte
@@ -38,10 +50,22 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int BK = 64;
+constexpr int BK = 32;             // logical K per stage: LDS rows of 64 bytes
+constexpr int CPR = BK / 8;        // 16-byte chunks per LDS row
+constexpr int RPL = 64 / CPR;      // LDS rows filled by one 64-lane 16-byte load
 constexpr int kGroupM = 8;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit dword format, no swizzle
+constexpr int kLdsBytes = 160 * 1024;
 
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+
+// s_waitcnt vmcnt(n) with lgkm and exp counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
@@ -84,21 +108,30 @@ __device__ __forceinline__ void store_act(const GemmArgs& p, int m, int n, float
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-struct Tile {
+template <int BM, int BN, int WM, int WN, bool SPLIT>
+struct Geo {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = BN / WN / 32;
-  static constexpr int kStage = (BM + BN) * BK;            // elements per LDS stage
-  static constexpr int LPW = (BM + BN) / 8 / NW;            // 1 KB direct loads per wave per stage
-  static constexpr int SST = TN * 32 + 8;                   // epilogue slice row stride (floats)
-  static constexpr size_t kStageBytes = 2 * (size_t)kStage * 2;       // double-buffered stages
-  static constexpr size_t kSliceBytes = (size_t)NW * 32 * SST * 4;    // one fp32 slice per wave
-  static constexpr size_t kSmem = kStageBytes > kSliceBytes ? kStageBytes : kSliceBytes;
+  static constexpr int AR = SPLIT ? 2 * BM : BM;        // A rows per stage: hi rows, then lo rows
+  static constexpr int ROWS = AR + BN;
+  static constexpr int kStage = ROWS * BK;               // elements per stage
+  static constexpr int kStageBytes = kStage * 2;
+  static constexpr int LA = AR / RPL / NW;               // A loads per wave per stage
+  static constexpr int LB = BN / RPL / NW;               // B loads per wave per stage
+  static constexpr int LPW = LA + LB;
+  static constexpr int kFit = kLdsBytes / kStageBytes;
+  static constexpr int STAGES = kFit >= 4 ? 4 : 3;
+  static constexpr int SST = TN * 32 + 8;                // epilogue slice row stride (floats)
+  static constexpr int kSliceBytes = NW * 32 * SST * 4;  // one fp32 slice per wave
+  static constexpr int kRing = STAGES * kStageBytes;
+  static constexpr int kSmem = kRing > kSliceBytes ? kRing : kSliceBytes;
   static_assert(TM >= 1 && TN >= 2 && TN % 2 == 0, "wave tile must hold column pairs");
-  static_assert((BM + BN) % (8 * NW) == 0, "direct-load split");
-  static_assert(kSmem <= 160 * 1024, "LDS budget");
+  static_assert(AR % (RPL * NW) == 0 && BN % (RPL * NW) == 0, "load split");
+  static_assert(kFit >= 3, "three stages must fit in LDS");
+  static_assert(kSmem <= kLdsBytes, "LDS budget");
+  static_assert((STAGES - 2) * LPW < 64, "vmcnt range");
 };
 
 // Applies the epilogue to one staged 32-row slice (rows m_base.., columns n_base.., width W = TN*32).
@@ -183,28 +216,73 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ void __launch_bounds__(WM * WN * 64)
+template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI>
+__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_kernel(GemmArgs p) {
-  using T = Tile<BM, BN, WM, WN>;
-  constexpr int TM = T::TM, TN = T::TN, LPW = T::LPW, SST = T::SST;
+  using G = Geo<BM, BN, WM, WN, SPLIT>;
+  constexpr int TM = G::TM, TN = G::TN, LA = G::LA, LB = G::LB, S = G::STAGES, AR = G::AR;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wv % WM, wn = wv / WM;
 
   // ---- tile index: XCD-contiguous ranges, then grouped row-major order
   const int gm = (p.M + BM - 1) / BM, gn = (p.N + BN - 1) / BN;
-  const int G = gm * gn;
+  const int Gt = gm * gn;
   const int pid = blockIdx.x;
   const int xcd = pid & 7, local = pid >> 3;
-  const int per = G >> 3, rem = G & 7;
+  const int per = Gt >> 3, rem = Gt & 7;
   const int logical = xcd * per + min(xcd, rem) + local;
   const int in_group = kGroupM * gn;
   const int grp = logical / in_group, first_m = grp * kGroupM;
   const int gsz = min(gm - first_m, kGroupM);
   const int li = logical % in_group;
   const int m0 = (first_m + li % gsz) * BM, n0 = (li / gsz) * BN;
+
+  // ---- load plan: wave wv fills A rows [(wv*LA + j)*RPL, +RPL) and B rows likewise; lane ->
+  // row lane / CPR, physical chunk lane % CPR, which holds logical chunk swz(row, lane % CPR).
+  // Rows past M / N read the last valid row; those results are never stored.
+  const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.A), (short)0, (int)p.a_bytes,
+                                                    kRsrcWord3);
+  const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.B), (short)0, (int)p.b_bytes,
+                                                    kRsrcWord3);
+  // (fixed-size arrays: a dependent bound here fails the host-side instantiation of the split
+  // variants with this clang; only the first LA / LB entries are used)
+  static_assert(LA <= 16 && LB <= 16, "load plan");
+  uint32_t offa[16], offb[16];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int r = (wv * LA + j) * RPL + lane / CPR;
+    const int rr = r % BM;
+    const int m = min(m0 + rr, p.M - 1);
+    const int c = swz(r, lane % CPR);
+    offa[j] = (uint32_t)(((int64_t)m * p.lda + c * 8 + (r >= BM ? p.a_group : 0)) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int r = (wv * LB + j) * RPL + lane / CPR;
+    const int n = min(n0 + r, p.N - 1);
+    const int c = swz(AR + r, lane % CPR);
+    offb[j] = (uint32_t)(((int64_t)n * p.ldb + c * 8) * 2);
+  }
+  const int nk = p.K / BK;
+  auto issue = [&](int kt, int buf) {
+    kt = min(kt, nk - 1);   // past the end: reload the last stage into a free slot (never read)
+    const int k0 = kt * BK;
+    const uint32_t ka = (uint32_t)(SPLIT ? (k0 / p.a_group) * 2 * p.a_group + k0 % p.a_group : k0) * 2;
+    const uint32_t kb = (uint32_t)k0 * 2;
+    uint16_t* st = smem + buf * G::kStage;
+#pragma unroll
+    for (int j = 0; j < LA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(st + (wv * LA + j) * RPL * BK), 16, offa[j], ka, 0, 0);
+#pragma unroll
+    for (int j = 0; j < LB; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(st + (AR + (wv * LB + j) * RPL) * BK), 16, offb[j], kb,
+          0, 0);
+  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -214,65 +292,91 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // direct-load sources: wave wv fills stage rows [(wv*LPW + j)*8, +8); lane -> row lane/8,
-  // physical chunk lane%8, which holds logical chunk (lane%8) ^ ((row >> 1) & 7).
-  // Rows past M / N read the last valid row; those results are never stored.
-  const uint16_t* src[LPW];
-#pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int r = (wv * LPW + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    src[j] = r < BM ? p.A + (int64_t)min(m0 + r, p.M - 1) * p.lda + c * 8
-                    : p.B + (int64_t)min(n0 + r - BM, p.N - 1) * p.ldb + c * 8;
-  }
-  auto dload = [&](int kt, int buf) {
-#pragma unroll
-    for (int j = 0; j < LPW; ++j)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src[j] + kt * BK),
-          (__attribute__((address_space(3))) void*)(smem + buf * T::kStage + (wv * LPW + j) * 8 * BK), 16, 0, 0);
-  };
-  bf16x8 fa[2][TM], fb[2][TN];
-  auto lfrag = [&](int buf, int kk, bf16x8 (&xa)[TM], bf16x8 (&xb)[TN]) {
-    const uint16_t* sA = smem + buf * T::kStage;
-    const uint16_t* sB = sA + BM * BK;
+  // fragment reads: 32x32x16 operand = 32 rows x 16 K; lane -> row lane & 31, chunk 2*kk + lane/32
+  bf16x8 fa[2][TM], fl[2][TM], fb[2][TN];
+  auto lfrag = [&](int buf, int kk, bf16x8 (&xa)[TM], bf16x8 (&xl)[TM], bf16x8 (&xb)[TN]) {
+    const uint16_t* st = smem + buf * G::kStage;
     const int c = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wm * TM * 32 + i * 32 + (lane & 31);
-      xa[i] = *reinterpret_cast<const bf16x8*>(sA + r * BK + swz(r, c) * 8);
+      xa[i] = *reinterpret_cast<const bf16x8*>(st + r * BK + swz(r, c) * 8);
+      if constexpr (SPLIT) {
+        const int rl = BM + r;
+        xl[i] = *reinterpret_cast<const bf16x8*>(st + rl * BK + swz(rl, c) * 8);
+      }
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int r = wn * TN * 32 + j * 32 + (lane & 31);
-      xb[j] = *reinterpret_cast<const bf16x8*>(sB + r * BK + swz(r, c) * 8);
+      const int r = AR + wn * TN * 32 + j * 32 + (lane & 31);
+      xb[j] = *reinterpret_cast<const bf16x8*>(st + r * BK + swz(r, c) * 8);
     }
   };
-
-  const int nk = p.K / BK;
-  dload(0, 0);
-  __syncthreads();
-  lfrag(0, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) dload(kt + 1, cur ^ 1);
+  auto mfma_step = [&](const bf16x8 (&xa)[TM], const bf16x8 (&xl)[TM], const bf16x8 (&xb)[TN]) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int s = kk & 1;
-      if (kk < BK / 16 - 1) lfrag(cur, kk + 1, fa[s ^ 1], fb[s ^ 1]);
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+    if constexpr (SPLIT) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl[i], xb[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
-    if (kt + 1 < nk) lfrag(cur ^ 1, 0, fa[0], fb[0]);
+  };
+  constexpr int NMF = TM * TN * (SPLIT ? 2 : 1);   // MFMAs per 16-wide K step
+  constexpr int NDS = TM * (SPLIT ? 2 : 1) + TN;    // fragment reads per K step
+
+  // ---- prologue: stages 0 .. S-2 in flight, stage 0 landed everywhere
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s, s);
+  wait_vm<(S - 2) * G::LPW>();
+  __builtin_amdgcn_s_barrier();
+  lfrag(0, 0, fa[0], fl[0], fb[0]);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt % S;
+    // step 0: MFMAs on K columns [0,16) of stage kt; read [16,32); refill the slot of stage kt-1
+    issue(kt + S - 1, (kt + S - 1) % S);
+    lfrag(buf, 1, fa[1], fl[1], fb[1]);
+    mfma_step(fa[0], fl[0], fb[0]);
+#pragma unroll
+    for (int i = 0; i < G::LPW; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (buffer load -> LDS)
+      if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
+#pragma unroll
+    for (int i = G::LPW; i < NDS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1: stage kt+1 must have landed (own loads), and every wave must be done with
+    // stage kt's reads before its slot is refilled next iteration
+    wait_vm<(S - 2) * G::LPW>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    lfrag((kt + 1) % S, 0, fa[0], fl[0], fb[0]);
+    mfma_step(fa[1], fl[1], fb[1]);
+#pragma unroll
+    for (int i = 0; i < NDS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // drain the (redundant) trailing loads before the ring is reused for the epilogue
+  wait_vm<0>();
+  __syncthreads();
 
   // ---- epilogue through LDS, one 32-row slice of the wave tile at a time.  Accumulator
   // layout: lane holds column (lane & 31) and rows 8g + 4*(lane >> 5) + e of each 32x32 tile.
-  float* sc = reinterpret_cast<float*>(smem) + wv * 32 * SST;
+  float* sc = reinterpret_cast<float*>(smem) + wv * 32 * G::SST;
   const int lc = lane & 31, lr = (lane >> 5) * 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -280,50 +384,57 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc[(8 * (e / 4) + lr + (e % 4)) * SST + j * 32 + lc] = acc[i][j][e];
+      for (int e = 0; e < 16; ++e) sc[(8 * (e / 4) + lr + (e % 4)) * G::SST + j * 32 + lc] = acc[i][j][e];
     __syncthreads();
     epilogue_slice<EPI, TN * 32>(p, sc, m0 + wm * TM * 32 + i * 32, n0 + wn * TN * 32, lane);
   }
 }
 
-// Tile configurations: L 256x256 (8 waves of 64x128), M 128x128 (4 waves of 64x64),
-// S 64x64 (2 waves of 32x64).
-enum Cfg { CFG_L, CFG_M, CFG_S };
+// Tile configurations (all 2x2 or 2x1 waves, one workgroup per CU):
+//   L 256x256 (waves of 128x128), T 192x256 (96x128), H 128x256 (64x128), S 64x64 (2 waves of 32x64).
+enum Cfg { CFG_L, CFG_T, CFG_H, CFG_S };
 struct CfgInfo {
   int cfg, bm, bn, wave_n;
-  double eff;   // measured relative MFMA efficiency of the main loop
+  double eff;   // relative MFMA efficiency of the main loop (larger wave tiles read less LDS per MFMA)
 };
-constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 128, 1.0}, {CFG_M, 128, 128, 64, 0.85}, {CFG_S, 64, 64, 64, 0.35}};
+// (efficiencies fitted to measured times of the tower's products on MI355X)
+constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 128, 1.0},
+                             {CFG_T, 192, 256, 128, 0.95},
+                             {CFG_H, 128, 256, 128, 0.85},
+                             {CFG_S, 64, 64, 64, 0.3}};
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI>
 hipError_t run(const GemmArgs& a, hipStream_t st) {
-  using T = Tile<BM, BN, WM, WN>;
+  using G = Geo<BM, BN, WM, WN, SPLIT>;
   const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI>), dim3((unsigned)tiles), dim3(T::NT), T::kSmem, st, a);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, SPLIT, EPI>), dim3((unsigned)tiles), dim3(G::NT), G::kSmem, st,
+                     a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI>
 hipError_t allow_smem() {
-  using T = Tile<BM, BN, WM, WN>;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, EPI>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::kSmem);
+  using G = Geo<BM, BN, WM, WN, SPLIT>;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, SPLIT, EPI>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
 }
 
-template <int EPI>
+template <bool SPLIT, int EPI>
 hipError_t allow_smem_all() {
-  hipError_t e = allow_smem<256, 256, 4, 2, EPI>();
-  if (e == hipSuccess) e = allow_smem<128, 128, 2, 2, EPI>();
-  if (e == hipSuccess) e = allow_smem<64, 64, 2, 1, EPI>();
+  hipError_t e = allow_smem<256, 256, 2, 2, SPLIT, EPI>();
+  if (e == hipSuccess) e = allow_smem<192, 256, 2, 2, SPLIT, EPI>();
+  if (e == hipSuccess) e = allow_smem<128, 256, 2, 2, SPLIT, EPI>();
+  if (e == hipSuccess) e = allow_smem<64, 64, 2, 1, SPLIT, EPI>();
   return e;
 }
 
-template <int EPI>
+template <bool SPLIT, int EPI>
 hipError_t run_cfg(int cfg, const GemmArgs& a, hipStream_t st) {
   switch (cfg) {
-    case CFG_L: return run<256, 256, 4, 2, EPI>(a, st);
-    case CFG_M: return run<128, 128, 2, 2, EPI>(a, st);
-    default: return run<64, 64, 2, 1, EPI>(a, st);
+    case CFG_L: return run<256, 256, 2, 2, SPLIT, EPI>(a, st);
+    case CFG_T: return run<192, 256, 2, 2, SPLIT, EPI>(a, st);
+    case CFG_H: return run<128, 256, 2, 2, SPLIT, EPI>(a, st);
+    default: return run<64, 64, 2, 1, SPLIT, EPI>(a, st);
   }
 }
 
@@ -344,15 +455,35 @@ int pick_cfg(int epi, const GemmArgs& a) {
   return best;
 }
 
+template <bool SPLIT>
+hipError_t dispatch(int epi, int cfg, const GemmArgs& a, hipStream_t st, bool* bad_epi) {
+  switch (epi) {
+    case EPI_F32: return run_cfg<SPLIT, EPI_F32>(cfg, a, st);
+    case EPI_RES: return run_cfg<SPLIT, EPI_RES>(cfg, a, st);
+    case EPI_GELU: return run_cfg<SPLIT, EPI_GELU>(cfg, a, st);
+    case EPI_SWIGLU: return run_cfg<SPLIT, EPI_SWIGLU>(cfg, a, st);
+    case EPI_QKV: return run_cfg<SPLIT, EPI_QKV>(cfg, a, st);
+    case EPI_OUT: return run_cfg<SPLIT, EPI_OUT>(cfg, a, st);
+    default: *bad_epi = true; return hipSuccess;
+  }
+}
+
+template <bool SPLIT>
+hipError_t allow_all() {
+  hipError_t e = allow_smem_all<SPLIT, EPI_F32>();
+  if (e == hipSuccess) e = allow_smem_all<SPLIT, EPI_RES>();
+  if (e == hipSuccess) e = allow_smem_all<SPLIT, EPI_GELU>();
+  if (e == hipSuccess) e = allow_smem_all<SPLIT, EPI_SWIGLU>();
+  if (e == hipSuccess) e = allow_smem_all<SPLIT, EPI_QKV>();
+  if (e == hipSuccess) e = allow_smem_all<SPLIT, EPI_OUT>();
+  return e;
+}
+
 }  // namespace
 
 vit_status prepare_gemm_kernels() {
-  hipError_t e = allow_smem_all<EPI_F32>();
-  if (e == hipSuccess) e = allow_smem_all<EPI_RES>();
-  if (e == hipSuccess) e = allow_smem_all<EPI_GELU>();
-  if (e == hipSuccess) e = allow_smem_all<EPI_SWIGLU>();
-  if (e == hipSuccess) e = allow_smem_all<EPI_QKV>();
-  if (e == hipSuccess) e = allow_smem_all<EPI_OUT>();
+  hipError_t e = allow_all<false>();
+  if (e == hipSuccess) e = allow_all<true>();
   if (e != hipSuccess) {
     set_error("gemm LDS attribute: %s", hipGetErrorString(e));
     return VIT_E_HIP;
@@ -360,29 +491,37 @@ vit_status prepare_gemm_kernels() {
   return VIT_OK;
 }
 
-vit_status launch_gemm(int epi, const GemmArgs& a, void* stream) {
-  if (a.M <= 0) return VIT_OK;
-  if (a.N % 64 || a.K % BK || a.K <= 0 || a.lda % 8 || a.ldb % 8 || a.ldo % 4) {
-    set_error("gemm: unsupported shape M=%d N=%d K=%d (N, K must be multiples of 64)", a.M, a.N, a.K);
+vit_status launch_gemm(int epi, const GemmArgs& in, void* stream) {
+  if (in.M <= 0) return VIT_OK;
+  GemmArgs a = in;
+  const bool split = a.a_group > 0;
+  if (a.N % 64 || a.K % BK || a.K <= 0 || a.lda % 8 || a.ldb % 8 || a.ldo % 4 ||
+      (split && (a.a_group % BK || a.K % a.a_group))) {
+    set_error("gemm: unsupported shape M=%d N=%d K=%d group=%d (N a multiple of 64, K and the hi/lo group "
+              "multiples of 32)", a.M, a.N, a.K, a.a_group);
     return VIT_E_ARG;
   }
+  // byte extents of the operands, addressed with 32-bit buffer offsets
+  const int64_t a_cols = split ? 2 * (int64_t)a.K : a.K;
+  const int64_t a_bytes = ((int64_t)(a.M - 1) * a.lda + a_cols) * 2;
+  const int64_t b_bytes = ((int64_t)(a.N - 1) * a.ldb + a.K) * 2;
+  if (a_bytes >= (int64_t)1 << 31 || b_bytes >= (int64_t)1 << 31) {
+    set_error("gemm: operand larger than 2 GiB (M=%d N=%d K=%d)", a.M, a.N, a.K);
+    return VIT_E_ARG;
+  }
+  a.a_bytes = (uint32_t)a_bytes;
+  a.b_bytes = (uint32_t)b_bytes;
   const int cfg = pick_cfg(epi, a);
   if (cfg < 0) {
     set_error("gemm: no tile configuration for N=%d (epilogue %d)", a.N, epi);
     return VIT_E_ARG;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  switch (epi) {
-    case EPI_F32: e = run_cfg<EPI_F32>(cfg, a, st); break;
-    case EPI_RES: e = run_cfg<EPI_RES>(cfg, a, st); break;
-    case EPI_GELU: e = run_cfg<EPI_GELU>(cfg, a, st); break;
-    case EPI_SWIGLU: e = run_cfg<EPI_SWIGLU>(cfg, a, st); break;
-    case EPI_QKV: e = run_cfg<EPI_QKV>(cfg, a, st); break;
-    case EPI_OUT: e = run_cfg<EPI_OUT>(cfg, a, st); break;
-    default:
-      set_error("gemm: bad epilogue %d", epi);
-      return VIT_E_ARG;
+  bool bad_epi = false;
+  const hipError_t e = split ? dispatch<true>(epi, cfg, a, st, &bad_epi) : dispatch<false>(epi, cfg, a, st, &bad_epi);
+  if (bad_epi) {
+    set_error("gemm: bad epilogue %d", epi);
+    return VIT_E_ARG;
   }
   if (e != hipSuccess) {
     set_error("gemm launch (epi %d, M=%d N=%d K=%d): %s", epi, a.M, a.N, a.K, hipGetErrorString(e));

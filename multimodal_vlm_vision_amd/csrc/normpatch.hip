@@ -11,8 +11,8 @@
 //
 // One workgroup handles kUnitsPerBlock merge units.  Each unit's 2 slots x 28
 // pixel rows x 84 bytes are staged in LDS with dword loads, then every thread
-// emits 16-byte chunks of the 4 output rows (1216 bf16 each; columns
-// 1176..1215 are zero so the patch-embed GEMM needs no K tail).
+// emits 16-byte chunks of the 4 output rows (1184 bf16 each; columns
+// 1176..1183 are zero so the patch-embed GEMM needs no K tail).
 #include <hip/hip_runtime.h>
 
 #include "vit_internal.h"
@@ -26,7 +26,7 @@ constexpr int kUnitsPerBlock = 4;
 constexpr int kRowBytes = kUnitPx * 3;                        // 84
 constexpr int kUnitBytes = kTemporal * kUnitPx * kRowBytes;   // 4704
 constexpr int kUnitDwords = kUnitBytes / 4;                   // 1176
-constexpr int kChunksPerRow = kFeatPad / 8;                   // 152
+constexpr int kChunksPerRow = kFeatPad / 8;                   // 148
 constexpr int kChunksPerUnit = 4 * kChunksPerRow;             // 608
 
 __global__ void __launch_bounds__(kThreads)
@@ -79,7 +79,7 @@ normpatch_kernel(const uint8_t* __restrict__ pixels, const UnitDesc* __restrict_
   }
 }
 
-// uint8 flatten_patches rows [N][1176] -> bf16 [N][1216]; 8 features per thread
+// uint8 flatten_patches rows [N][1176] -> bf16 [N][1184]; 8 features per thread
 // (1176 = 147 * 8 and 392 = 49 * 8, so a chunk never straddles a channel).
 __global__ void __launch_bounds__(kThreads)
 normrows_kernel(const uint8_t* __restrict__ patches, int64_t n_rows,

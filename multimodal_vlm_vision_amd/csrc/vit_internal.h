@@ -22,7 +22,7 @@ constexpr int kPatch = 14;
 constexpr int kTemporal = 2;
 constexpr int kMerge = 2;
 constexpr int kFeat = 3 * kTemporal * kPatch * kPatch;   // 1176 features per patch row
-constexpr int kFeatPad = 1216;                            // padded to the GEMM K tile (64)
+constexpr int kFeatPad = 1184;                            // padded to the GEMM K stage (32)
 constexpr int kUnitPx = kMerge * kPatch;                  // 28-pixel side of a merge unit
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -157,9 +157,13 @@ enum GemmEpi : int {
 };
 
 struct GemmArgs {
-  const uint16_t* A = nullptr; int64_t lda = 0;   // [M][K] bf16
+  const uint16_t* A = nullptr; int64_t lda = 0;   // [M][K] bf16 (split: [M][2K], see a_group)
   const uint16_t* B = nullptr; int64_t ldb = 0;   // [N][K] bf16
-  int M = 0, N = 0, K = 0;
+  int M = 0, N = 0, K = 0;                        // K = logical reduction length
+  // Split activations: when a_group > 0, each A row holds hi/lo pairs in groups of a_group
+  // columns, [hi(g) | lo(g)] repeated, and the product is sum_k (hi + lo)[k] * B[n][k].
+  int a_group = 0;
+  uint32_t a_bytes = 0, b_bytes = 0;              // operand extents (set by launch_gemm)
   const float* bias = nullptr;
   void* out = nullptr; int64_t ldo = 0;
   // QKV epilogue

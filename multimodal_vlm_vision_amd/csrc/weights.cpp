@@ -130,9 +130,6 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
   const int64_t d = c.hidden, hd = ctx->head_dim, mlp = c.mlp_dim, mp = ctx->mlp_pad;
   const int64_t md = 4 * d, od = c.out_dim;
   const int64_t r = hd / 2;   // rotary pairs per head
-  // With hi+lo activation pairs a consuming GEMM sees K' = S*K columns: the
-  // activation row is [hi | lo] and the weight row is repeated, [w | w].
-  const int64_t S = ctx->split;
   Packer P{ctx, {}, {}};
 
   struct LayerOff {
@@ -194,7 +191,7 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
       const int64_t head = pair / r, kk = pair % r;
       return part * d + head * hd + kk + (s < 32 ? 0 : r);
     };
-    L.qkv_w = P.mat(3 * d, S * d, [&](int64_t j, int64_t k) { return wq[src_row(j) * d + k % d]; });
+    L.qkv_w = P.mat(3 * d, d, [&](int64_t j, int64_t k) { return wq[src_row(j) * d + k]; });
     L.qkv_b = P.vec(3 * d, [&](int64_t j) { return bq[src_row(j)]; });
 
     const HostTensor* pw = P.get(p + "proj.w", {d, d});
@@ -209,12 +206,9 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
       const HostTensor* w2 = P.get(p + "fc2.w", {d, mlp});
       const HostTensor* b2 = P.get(p + "fc2.b", {d});
       if (!w1 || !b1 || !w2 || !b2) goto fail;
-      L.fc1_w = P.mat(mp, S * d, [&](int64_t o, int64_t k) { return o < mlp ? w1->data[o * d + k % d] : 0.f; });
+      L.fc1_w = P.mat(mp, d, [&](int64_t o, int64_t k) { return o < mlp ? w1->data[o * d + k] : 0.f; });
       L.fc1_b = P.vec(mp, [&](int64_t o) { return o < mlp ? b1->data[o] : 0.f; });
-      L.fc2_w = P.mat(d, S * mp, [&](int64_t o, int64_t k) {
-        k %= mp;
-        return k < mlp ? w2->data[o * mlp + k] : 0.f;
-      });
+      L.fc2_w = P.mat(d, mp, [&](int64_t o, int64_t k) { return k < mlp ? w2->data[o * mlp + k] : 0.f; });
       L.fc2_b = P.vec(d, [&](int64_t i) { return b2->data[i]; });
     } else {
       const HostTensor* wg = P.get(p + "gate.w", {mlp, d});
@@ -230,11 +224,11 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
         is_up = s >= 32;
         return 32 * (j / 64) + s % 32;
       };
-      L.fc1_w = P.mat(2 * mp, S * d, [&](int64_t j, int64_t k) {
+      L.fc1_w = P.mat(2 * mp, d, [&](int64_t j, int64_t k) {
         bool up;
         const int64_t o = gu(j, up);
         if (o >= mlp) return 0.f;
-        return (up ? wu : wg)->data[o * d + k % d];
+        return (up ? wu : wg)->data[o * d + k];
       });
       L.fc1_b = P.vec(2 * mp, [&](int64_t j) {
         bool up;
@@ -242,10 +236,7 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
         if (o >= mlp) return 0.f;
         return (up ? bu : bg)->data[o];
       });
-      L.fc2_w = P.mat(d, S * mp, [&](int64_t o, int64_t k) {
-        k %= mp;
-        return k < mlp ? wd->data[o * mlp + k] : 0.f;
-      });
+      L.fc2_w = P.mat(d, mp, [&](int64_t o, int64_t k) { return k < mlp ? wd->data[o * mlp + k] : 0.f; });
       L.fc2_b = P.vec(d, [&](int64_t i) { return bd->data[i]; });
     }
   }
@@ -267,13 +258,11 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
     const HostTensor* w2 = P.get("mrg.fc2.w", {od, md});
     const HostTensor* b2 = P.get("mrg.fc2.b", {od});
     if (!w1 || !b1 || !w2 || !b2) goto fail;
-    // merger input row = the merge unit's 4 patch rows, each [hi(d) | lo(d)] when split
-    m1w = P.mat(md, S * md, [&](int64_t o, int64_t k) {
-      const int64_t q = k / (S * d), t = k % d;
-      return w1->data[o * md + q * d + t];
-    });
+    // merger input row = the merge unit's 4 patch rows concatenated (each stored as
+    // [hi(d) | lo(d)] when split; the GEMM maps logical columns onto that layout)
+    m1w = P.mat(md, md, [&](int64_t o, int64_t k) { return w1->data[o * md + k]; });
     m1b = P.vec(md, [&](int64_t i) { return b1->data[i]; });
-    m2w = P.mat(od, S * md, [&](int64_t o, int64_t k) { return w2->data[o * md + k % md]; });
+    m2w = P.mat(od, md, [&](int64_t o, int64_t k) { return w2->data[o * md + k]; });
     m2b = P.vec(od, [&](int64_t i) { return b2->data[i]; });
   }
 

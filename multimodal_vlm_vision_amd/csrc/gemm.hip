@@ -338,20 +338,22 @@ gemm_kernel(GemmArgs p) {
 
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt % S;
-    // step 0: MFMAs on K columns [0,16) of stage kt; read [16,32); refill the slot of stage kt-1
-    issue(kt + S - 1, (kt + S - 1) % S);
+    // step 0: MFMAs on K columns [0,16) of stage kt; read [16,32); refill the slot of stage kt-1.
+    // The fragment reads are issued before the loads into LDS: the compiler cannot prove that
+    // the two touch different stages, so reads placed after the loads could not move past
+    // them and the loads would issue as one burst instead of one per MFMA.
     lfrag(buf, 1, fa[1], fl[1], fb[1]);
+    issue(kt + S - 1, (kt + S - 1) % S);
     mfma_step(fa[0], fl[0], fb[0]);
+#pragma unroll
+    for (int i = 0; i < NDS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
 #pragma unroll
     for (int i = 0; i < G::LPW; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (buffer load -> LDS)
-      if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-    }
-#pragma unroll
-    for (int i = G::LPW; i < NDS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -374,18 +376,18 @@ gemm_kernel(GemmArgs p) {
   wait_vm<0>();
   __syncthreads();
 
-  // ---- epilogue through LDS, one 32-row slice of the wave tile at a time.  Accumulator
-  // layout: lane holds column (lane & 31) and rows 8g + 4*(lane >> 5) + e of each 32x32 tile.
+  // ---- epilogue through LDS, one 32-row slice of the wave tile at a time, in a region only
+  // this wave touches (LDS operations of one wave complete in order, so no barrier is needed
+  // between slices).  Accumulator layout: lane holds column (lane & 31) and rows
+  // 8g + 4*(lane >> 5) + e of each 32x32 tile.
   float* sc = reinterpret_cast<float*>(smem) + wv * 32 * G::SST;
   const int lc = lane & 31, lr = (lane >> 5) * 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    if (i > 0) __syncthreads();
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sc[(8 * (e / 4) + lr + (e % 4)) * G::SST + j * 32 + lc] = acc[i][j][e];
-    __syncthreads();
     epilogue_slice<EPI, TN * 32>(p, sc, m0 + wm * TM * 32 + i * 32, n0 + wn * TN * 32, lane);
   }
 }
@@ -399,8 +401,8 @@ struct CfgInfo {
 };
 // (efficiencies fitted to measured times of the tower's products on MI355X)
 constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 128, 1.0},
-                             {CFG_T, 192, 256, 128, 0.95},
-                             {CFG_H, 128, 256, 128, 0.85},
+                             {CFG_T, 192, 256, 128, 0.98},
+                             {CFG_H, 128, 256, 128, 0.9},
                              {CFG_S, 64, 64, 64, 0.3}};
 
 template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI>

@@ -54,6 +54,48 @@ def cpu_baseline(wl, n_items=3):
                       f"float64 NumPy, {dt:.1f} s"}
 
 
+def normpatch_stream(n_images=48, side=1344, reps=5):
+    """normpatch alone on a >= 1 GB streaming batch (48 images of 1344 x 1344): the
+    per-forward traffic of the bench batch (~52 MB) fits in the 256 MB last-level cache,
+    so HBM bandwidth is measured on a batch several times larger than that cache.
+    A zero-layer tower of width 64 keeps the rest of the forward negligible."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from multimodal_vlm_vision_amd import VisionTower
+    from workloads import make_weights, tower_config
+
+    cfg = dataclasses.replace(tower_config(1), name="normpatch-stream", layers=0, mlp_dim=64, out_dim=64)
+    tower = VisionTower(cfg)
+    tower.load_weights(make_weights(99, cfg))
+    tower.finalize()
+    g = side // 14
+    grid = np.array([[1, g, g]] * n_images, dtype=np.int32)
+    plan = tower.plan(grid, np.ones(n_images, dtype=np.int32))
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    pixels = torch.randint(0, 256, (plan.pixel_bytes,), dtype=torch.uint8, device=dev, generator=gen)
+    ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(plan.out_rows, plan.out_cols, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    tower.encode(plan, pixels, ws, out, stream)
+    tot_ms, by, n = 0.0, 0.0, 0
+    for _ in range(reps):
+        for k in tower.encode_profiled(plan, pixels, ws, out, stream):
+            if k["name"] == "normpatch":
+                tot_ms += k["total_ms"]
+                by += k["bytes"]
+                n += k["launches"]
+    torch.cuda.synchronize()
+    gbs = by / (tot_ms * 1e-3) / 1e9
+    res = {"images": n_images, "side_px": side, "patches": int(grid[:, 1].sum() * g),
+           "bytes_per_launch": by / n, "avg_us": tot_ms / n * 1e3, "gbs": gbs,
+           "hbm_frac": gbs / PEAK_HBM_GBS}
+    tower.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +212,11 @@ def main():
         "kernels": kern,
     }
     graph.close()
+    log("normpatch streaming measurement ...")
+    line["normpatch_stream"] = normpatch_stream()
+    ns = line["normpatch_stream"]
+    log(f"normpatch stream: {ns['patches']} patches, {ns['bytes_per_launch'] / 1e9:.2f} GB/launch, "
+        f"{ns['avg_us']:.1f} us, {ns['gbs']:.0f} GB/s ({100 * ns['hbm_frac']:.1f}% of HBM peak)")
     if not args.no_cpu:
         log("CPU oracle baseline ...")
         line["cpu_baseline"] = cpu_baseline(wl)

@@ -10,6 +10,7 @@
 // ("GPUModelRunner.execute_model" notes, limits section).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -167,7 +168,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   const double np_bytes = (double)pl->pixel_read_bytes + Nd * kFeat * 2;
   if (pixels)
     LAUNCH("normpatch", 0, np_bytes, false,
-           launch_normpatch(pixels, units, pl->n_units, W.lut, X, st));
+           launch_normpatch(pixels, units, pl->n_units, W.lut, ctx->norm_affine ? &ctx->affine : nullptr, X, st));
   else
     LAUNCH("normrows_u8", 0, Nd * kFeat * 3, false, launch_normrows_u8(patches, N, W.lut, X, st));
   if (stop.hit(-1, 0)) {
@@ -356,6 +357,23 @@ void build_lut(const vit_config& c, uint16_t (&lut)[3][256]) {
   }
 }
 
+// The same quotient as one float32 fused multiply-add, x * (1 / (255 s)) + (-m / s), with
+// both constants rounded to float32; accepted only if its bf16 rounding equals the exact
+// table entry for every byte of every channel (checked here with the host's IEEE fmaf,
+// which rounds exactly as the GPU's v_fma_f32).
+bool verify_affine(const vit_config& c, const uint16_t (&lut)[3][256], NormAffine* out) {
+  for (int ch = 0; ch < 3; ++ch) {
+    const long double m = (long double)c.mean[ch], s = (long double)c.std[ch];
+    const float a = (float)(1.0L / (255.0L * s));
+    const float b = (float)(-m / s);
+    for (int x = 0; x < 256; ++x)
+      if (f32_to_bf16_bits(std::fma((float)x, a, b)) != lut[ch][x]) return false;
+    out->a[ch] = a;
+    out->b[ch] = b;
+  }
+  return true;
+}
+
 }  // namespace
 }  // namespace vitmi
 
@@ -389,6 +407,7 @@ vit_status vit_create(const vit_config* cfg, vit_ctx** out) {
   ctx->mlp_pad = (int)round_up(cfg->mlp_dim, 64);
   ctx->split = cfg->activation_precision == VIT_ACT_BF16X2 ? 2 : 1;
   build_lut(*cfg, ctx->lut);
+  ctx->norm_affine = verify_affine(*cfg, ctx->lut, &ctx->affine);
   *out = ctx;
   return VIT_OK;
 }

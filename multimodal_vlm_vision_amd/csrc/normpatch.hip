@@ -7,12 +7,24 @@
 // ("vLLM multimodal inference | ViT performance optimisation", sections 2.2
 // and 3.2).  The normalised value of every (channel, byte) pair is taken from
 // a 3x256 table of exactly rounded bfloat16 values, so the result is the
-// correctly rounded quotient bit for bit.
+// correctly rounded quotient bit for bit; when the library has verified on the
+// host that one float32 fma per byte rounds to the same 768 values, the
+// kernel evaluates that fma instead of the table (fewer LDS lookups).
 //
-// One workgroup handles kUnitsPerBlock merge units.  Each unit's 2 slots x 28
-// pixel rows x 84 bytes are staged in LDS with dword loads, then every thread
-// emits 16-byte chunks of the 4 output rows (1184 bf16 each; columns
-// 1176..1183 are zero so the patch-embed GEMM needs no K tail).
+// HBM-bound streaming kernel.  One workgroup handles kUnitsPerBlock merge
+// units that are consecutive in row order, so both sides stream:
+//  * input: each unit's 28 pixel rows x 84 bytes per temporal slot are staged
+//    in LDS with 12-byte loads ordered (slot, pixel row, unit, piece), so
+//    adjacent lanes read adjacent bytes of one image row, all issued before
+//    the first LDS store; an image's single frame is read once and serves
+//    both temporal slots;
+//  * output: the block's 4 * kUnitsPerBlock rows of 1184 bf16 (columns
+//    1176..1183 zero, so the patch-embed GEMM needs no K tail) are one
+//    contiguous run, written as 16-byte nontemporal stores by consecutive
+//    lanes.
+// A per-block table maps each output feature to its staged byte (offset,
+// channel, temporal slot), so a 16-byte output chunk costs one table read and
+// 8 pairs of LDS lookups instead of per-element index division.
 #include <hip/hip_runtime.h>
 
 #include "vit_internal.h"
@@ -21,61 +33,138 @@ namespace vitmi {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnitsPerBlock = 4;
-constexpr int kRowBytes = kUnitPx * 3;                        // 84
-constexpr int kUnitBytes = kTemporal * kUnitPx * kRowBytes;   // 4704
+constexpr int kThreads = 512;
+constexpr int kUnitsPerBlock = 8;
+constexpr int kRowBytes = kUnitPx * 3;                        // 84 bytes of one unit pixel row
+constexpr int kRowDwords = kRowBytes / 4;                     // 21
+constexpr int kSlotBytes = kUnitPx * kRowBytes;               // 2352 bytes of one temporal slot
+constexpr int kUnitBytes = kTemporal * kSlotBytes;            // 4704
 constexpr int kUnitDwords = kUnitBytes / 4;                   // 1176
 constexpr int kChunksPerRow = kFeatPad / 8;                   // 148
-constexpr int kChunksPerUnit = 4 * kChunksPerRow;             // 608
+constexpr int kChunksPerUnit = 4 * kChunksPerRow;             // 592
+constexpr uint16_t kPadFeature = 0x8000;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+constexpr int kRowPieces = kRowBytes / 12;                    // 7 pieces of 12 bytes per unit row
+constexpr int kPieceIds = kUnitsPerBlock * kTemporal * kUnitPx * kRowPieces;
+constexpr int kLoadsPerThread = (kPieceIds + kThreads - 1) / kThreads;
 
+// 12 bytes of a pixel row (4-byte aligned: unit rows start at multiples of 84 bytes)
+struct alignas(4) Piece {
+  uint32_t a, b, c;
+};
+
+static_assert(kFeatPad % 8 == 0 && kFeatPad >= kFeat, "row padding");
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+// feature f = ((c * 2 + tau) * 14 + i) * 14 + j of the unit's top-left patch ->
+// staged byte (tau * 28 + i) * 84 + 3 * j + c, packed as offset | c << 12 | tau << 14.
+__device__ __forceinline__ uint16_t feature_entry(int f) {
+  if (f >= kFeat) return kPadFeature;
+  const int c = f / 392, r1 = f - c * 392;
+  const int tau = r1 / 196, r2 = r1 - tau * 196;
+  const int i = r2 / 14, j = r2 - i * 14;
+  const int off = (tau * kUnitPx + i) * kRowBytes + 3 * j + c;
+  return (uint16_t)(off | (c << 12) | (tau << 14));
+}
+
+template <bool AFFINE>
 __global__ void __launch_bounds__(kThreads)
 normpatch_kernel(const uint8_t* __restrict__ pixels, const UnitDesc* __restrict__ units,
-                 int64_t n_units, const uint16_t* __restrict__ lut_g, uint16_t* __restrict__ x) {
-  __shared__ uint32_t stage[kUnitsPerBlock][kUnitDwords];
+                 int64_t n_units, const uint16_t* __restrict__ lut_g, NormAffine na, uint16_t* __restrict__ x) {
+  __shared__ uint32_t stage[kUnitsPerBlock * kUnitDwords];
+  __shared__ __attribute__((aligned(16))) uint16_t tab[kFeatPad];
   __shared__ uint16_t lut[3 * 256];
+  __shared__ UnitDesc sud[kUnitsPerBlock];
   const int tid = threadIdx.x;
-  for (int i = tid; i < 3 * 256; i += kThreads) lut[i] = lut_g[i];
-
   const int64_t u0 = (int64_t)blockIdx.x * kUnitsPerBlock;
   const int nu = (int)min<int64_t>(kUnitsPerBlock, n_units - u0);
-  // stage: dword j of a unit -> slot = j / (28*21), row = (j / 21) % 28, dword-in-row = j % 21
-  for (int j = tid; j < nu * kUnitDwords; j += kThreads) {
-    const int u = j / kUnitDwords, jj = j % kUnitDwords;
-    const UnitDesc ud = units[u0 + u];
-    const int slot = jj / (kUnitPx * 21), rem = jj % (kUnitPx * 21);
-    const int row = rem / 21, dw = rem % 21;
-    const uint8_t* src = pixels + ud.px_off + (int64_t)slot * ud.fstride + (int64_t)row * ud.pitch + 4 * dw;
-    stage[u][jj] = *reinterpret_cast<const uint32_t*>(src);
-  }
+  if (!AFFINE)
+    for (int i = tid; i < 3 * 256; i += kThreads) lut[i] = lut_g[i];
+  for (int f = tid; f < kFeatPad; f += kThreads) tab[f] = feature_entry(f);
+  if (tid < nu) sud[tid] = units[u0 + tid];
   __syncthreads();
 
-  for (int j = tid; j < nu * kChunksPerUnit; j += kThreads) {
-    const int u = j / kChunksPerUnit, jj = j % kChunksPerUnit;
-    const int rr = jj / kChunksPerRow, k8 = jj % kChunksPerRow;   // row in unit (dh, dw), chunk
-    const int dh = rr >> 1, dwc = rr & 1;
-    const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage[u]);
-    uint16_t v[8];
+  // stage: piece id -> (slot, pixel row, unit, 12-byte piece of the row); images skip slot 1.
+  // Every load of the block is issued before the first LDS store, so a thread waits for
+  // one memory latency, not one per load.
+  Piece v[kLoadsPerThread];
+  int dst[kLoadsPerThread];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int f = 8 * k8 + e;
-      if (f < kFeat) {
-        const int c = f / 392, r1 = f % 392;
-        const int tau = r1 / 196, r2 = r1 % 196;
-        const int i = r2 / 14, jx = r2 % 14;
-        const int y = kPatch * dh + i, xx = kPatch * dwc + jx;
-        v[e] = lut[c * 256 + sb[(tau * kUnitPx + y) * kRowBytes + xx * 3 + c]];
-      } else {
-        v[e] = 0;
+  for (int k = 0; k < kLoadsPerThread; ++k) {
+    const int id = tid + k * kThreads;
+    const int pc = id % kRowPieces, t = id / kRowPieces;
+    const int u = t % kUnitsPerBlock, rest = t / kUnitsPerBlock;
+    const int row = rest % kUnitPx, slot = rest / kUnitPx;
+    dst[k] = -1;
+    if (id < kPieceIds && u < nu && !(slot == 1 && sud[u].fstride == 0)) {
+      const UnitDesc ud = sud[u];
+      const uint8_t* src = pixels + ud.px_off + (int64_t)slot * ud.fstride + (int64_t)row * ud.pitch + 12 * pc;
+      v[k] = *reinterpret_cast<const Piece*>(src);
+      dst[k] = u * kUnitDwords + (slot * kUnitPx + row) * kRowDwords + 3 * pc;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kLoadsPerThread; ++k)
+    if (dst[k] >= 0) {
+      stage[dst[k]] = v[k].a;
+      stage[dst[k] + 1] = v[k].b;
+      stage[dst[k] + 2] = v[k].c;
+    }
+  __syncthreads();
+
+  const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
+  uint16_t* xb = x + u0 * 4 * kFeatPad;
+  for (int q = tid; q < nu * kChunksPerUnit; q += kThreads) {
+    const int u = q / kChunksPerUnit, rem = q - u * kChunksPerUnit;
+    const int rr = rem / kChunksPerRow, k8 = rem - rr * kChunksPerRow;   // row in unit (dh, dw), chunk
+    const int shift = (rr >> 1) * (kPatch * kRowBytes) + (rr & 1) * (kPatch * 3);
+    const bool image = sud[u].fstride == 0;
+    const uint8_t* ub = sb + u * kUnitBytes + shift;
+    const uint4 t4 = *reinterpret_cast<const uint4*>(tab + 8 * k8);
+    const uint32_t tw[4] = {t4.x, t4.y, t4.z, t4.w};
+    uint32_t packed[4];
+    if constexpr (AFFINE) {
+      // one channel per chunk (392 = 49 * 8); pad chunks (features >= 1176) are all pad
+      const int ch = (t4.x >> 12) & 3;
+      const float a = ch == 0 ? na.a[0] : ch == 1 ? na.a[1] : na.a[2];
+      const float b = ch == 0 ? na.b[0] : ch == 1 ? na.b[1] : na.b[2];
+      const bool pad = t4.x & kPadFeature;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        float y[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const uint32_t t = (tw[h] >> (16 * s)) & 0xffffu;
+          const int tau = (t >> 14) & 1;
+          const int off = (int)(t & 0xfff) - (image && tau ? kSlotBytes : 0);
+          y[s] = pad ? 0.f : __builtin_fmaf((float)ub[off], a, b);
+        }
+        packed[h] = pack_bf16(y[0], y[1]);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        uint32_t pair = 0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const uint32_t t = (tw[h] >> (16 * s)) & 0xffffu;
+          uint32_t v = 0;
+          if (!(t & kPadFeature)) {
+            const int tau = (t >> 14) & 1;
+            const int off = (int)(t & 0xfff) - (image && tau ? kSlotBytes : 0);
+            v = lut[((t >> 12) & 3) * 256 + ub[off]];
+          }
+          pair |= v << (16 * s);
+        }
+        packed[h] = pair;
       }
     }
-    uint4 pk;
-    pk.x = v[0] | ((uint32_t)v[1] << 16);
-    pk.y = v[2] | ((uint32_t)v[3] << 16);
-    pk.z = v[4] | ((uint32_t)v[5] << 16);
-    pk.w = v[6] | ((uint32_t)v[7] << 16);
-    const int64_t row = 4 * (u0 + u) + rr;
-    *reinterpret_cast<uint4*>(x + row * kFeatPad + 8 * k8) = pk;
+    // streaming output: nontemporal stores (the rows are read once, by the next kernel)
+    __builtin_nontemporal_store(u32x4{packed[0], packed[1], packed[2], packed[3]},
+                                reinterpret_cast<u32x4*>(xb + (int64_t)q * 8));
   }
 }
 
@@ -107,11 +196,15 @@ normrows_kernel(const uint8_t* __restrict__ patches, int64_t n_rows,
 }  // namespace
 
 vit_status launch_normpatch(const uint8_t* pixels, const UnitDesc* units, int64_t n_units,
-                            const uint16_t* lut, uint16_t* x, void* stream) {
+                            const uint16_t* lut, const NormAffine* affine, uint16_t* x, void* stream) {
   if (n_units <= 0) return VIT_OK;
   const int64_t blocks = (n_units + kUnitsPerBlock - 1) / kUnitsPerBlock;
-  hipLaunchKernelGGL(normpatch_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), pixels, units, n_units, lut, x);
+  if (affine)
+    hipLaunchKernelGGL(normpatch_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), pixels, units, n_units, lut, *affine, x);
+  else
+    hipLaunchKernelGGL(normpatch_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), pixels, units, n_units, lut, NormAffine{}, x);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("normpatch launch: %s", hipGetErrorString(e));

@@ -60,6 +60,13 @@ struct AttnLists {
   double sq_short = 0.0;
 };
 
+// Per-channel affine form of the normalisation, y = fma(x, a_c, b_c) in float32 then
+// bf16 round-to-nearest-even.  Used only when the host has verified that it reproduces
+// the exactly rounded table for all 768 (channel, byte) pairs.
+struct NormAffine {
+  float a[3], b[3];
+};
+
 // ---------------------------------------------------------------- weights
 
 struct HostTensor {
@@ -94,6 +101,8 @@ struct vit_ctx {
   int mlp_pad = 0;       // mlp_dim rounded up to 64
   int split = 1;         // 2 with hi+lo activation pairs, else 1
   uint16_t lut[3][256];  // bf16 bits of ((x/255) - mean_c) / std_c, exactly rounded
+  bool norm_affine = false;     // fma(x, a_c, b_c) verified equal to lut for every byte
+  vitmi::NormAffine affine{};
   std::map<std::string, vitmi::HostTensor> host;
   bool finalized = false;
   int device = -1;
@@ -182,8 +191,9 @@ vit_status launch_gemm(int epi, const GemmArgs& a, void* stream);
 // Raises the dynamic-LDS limit of every GEMM instantiation (call once per process/device).
 vit_status prepare_gemm_kernels();
 
+// affine == nullptr: table lookups (always exact)
 vit_status launch_normpatch(const uint8_t* pixels, const UnitDesc* units, int64_t n_units,
-                            const uint16_t* lut, uint16_t* x, void* stream);
+                            const uint16_t* lut, const NormAffine* affine, uint16_t* x, void* stream);
 vit_status launch_normrows_u8(const uint8_t* patches, int64_t n_rows, const uint16_t* lut,
                               uint16_t* x, void* stream);
 // Row norm of fp32 rows [rows][d] into bf16; split: output rows [hi(d) | lo(d)] (stride 2d).

@@ -67,6 +67,25 @@ def test_normpatch_bit_exact(idx):
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} elements differ"
 
 
+# The library evaluates the normalisation as one float32 fma per byte when that is verified
+# (on the host, for all 768 values) to round exactly like the table, and uses the table
+# otherwise.  These mean/std make the fma path differ in one value (pinned on the CPU in
+# test_host_abi.py), so this workload runs the table kernel; the workloads above run the
+# fma kernel.
+TABLE_PATH_MEAN, TABLE_PATH_STD = (0.1, 0.2, 0.3), (0.11, 0.13, 0.17)
+
+
+def test_normpatch_bit_exact_table_path():
+    cfg = dataclasses.replace(tower_config(1).with_layers(1), mean=TABLE_PATH_MEAN, std=TABLE_PATH_STD)
+    wl = make_custom_workload(cfg, [(1, 84, 140), (4, 56, 112), (1, 224, 168)], seed=61)
+    run = GpuRun(wl)
+    say(f"normpatch table path N={run.n}")
+    got = run.stage(-1, 0)
+    table = O.normalize_table(cfg.mean, cfg.std)
+    ref = O.patchify([it.frames for it in wl.items], wl.grid_thw, table)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} elements differ"
+
+
 # ------------------------------------------------------------------ layer-local kernels
 
 

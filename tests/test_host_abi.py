@@ -118,3 +118,52 @@ def test_workspace_grows_with_batch(lib):
     t = B.VisionTower(tower_config(2), lib)
     sizes = [t.plan([[1, 2 * k, 2 * k]], [1]).ws_bytes for k in (2, 8, 16, 32)]
     assert sizes == sorted(sizes) and len(set(sizes)) == 4
+
+
+# ---- premise of the two normalisation kernels (table vs one float32 fma per byte)
+
+def _round_fraction(q, mant_bits):
+    """Round a rational to the nearest binary float with `mant_bits` fraction bits (ties to even)."""
+    from fractions import Fraction
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    q = abs(q)
+    e = 0
+    while q >= 2:
+        q /= 2
+        e += 1
+    while q < 1:
+        q *= 2
+        e -= 1
+    m = q * 2 ** mant_bits
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * Fraction(fl) * Fraction(2) ** (e - mant_bits)
+
+
+def _fma_path_mismatches(mean, std):
+    """Bytes whose bf16(fp32 fma(x, fp32(1/(255 s)), fp32(-m/s))) differs from bf16 of the exact
+    quotient ((x/255) - m)/s, with m and s the float32 values of the configured mean/std."""
+    from fractions import Fraction
+    bad = 0
+    for c in range(3):
+        m = Fraction(float(np.float32(mean[c])))
+        s = Fraction(float(np.float32(std[c])))
+        a = _round_fraction(1 / (255 * s), 23)
+        b = _round_fraction(-m / s, 23)
+        for x in range(256):
+            exact = _round_fraction((Fraction(x, 255) - m) / s, 7)
+            if _round_fraction(_round_fraction(x * a + b, 23), 7) != exact:
+                bad += 1
+    return bad
+
+
+def test_normalisation_fma_path_premise():
+    # the workloads' mean/std: the fma form rounds exactly like the table (fma kernel runs)
+    cfg = tower_config(3)
+    assert _fma_path_mismatches(cfg.mean, cfg.std) == 0
+    # the table-path GPU test's mean/std: one byte differs, so the library keeps the table
+    assert _fma_path_mismatches((0.1, 0.2, 0.3), (0.11, 0.13, 0.17)) >= 1

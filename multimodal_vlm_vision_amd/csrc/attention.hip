@@ -46,6 +46,19 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int KB = 32;   // keys per step
+
+// max over lanes l and l ^ 16 (rows of 16 lanes swapped pairwise in registers, no LDS trip)
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+// max over lanes l and l ^ 32
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
 constexpr int QT = 4;    // 16-query tiles per wave (64 queries)
 
 template <int HD, int NW>
@@ -184,8 +197,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
       for (int t = 0; t < QT; ++t) {
         float mx = fmaxf(fmaxf(fmaxf(S[0][t][0], S[0][t][1]), fmaxf(S[0][t][2], S[0][t][3])),
                          fmaxf(fmaxf(S[1][t][0], S[1][t][1]), fmaxf(S[1][t][2], S[1][t][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = max_xor32(max_xor16(mx));
         const float bm = mx * sc;
         if (kb == 0) {
           m[t] = bm;

@@ -7,30 +7,34 @@
 // by the planner (section 3.3).  A tile never spans two segments: every work
 // unit names its segment and the kernel only reads that segment's keys.
 //
-// Formulation: the wave computes S^T = K Q^T (keys as MFMA rows, queries as
-// columns) with v_mfma_f32_16x16x32_bf16 (+16x16x16 for a 16-wide head_dim
-// tail), so each lane ends up holding 4 consecutive keys of one query.  Those
-// probabilities are already the B operand of O^T = V^T P^T (the 32-key
-// reduction slots of a lane are its 4 keys of each of two 16-key tiles; V^T
-// fragments are read with the same key permutation), so P never leaves
-// registers, and each lane owns the running max of the one query its O^T
-// columns belong to.  The softmax denominator comes out of the same MFMA
-// chain: one extra 16-row tile of O^T multiplies P by an all-ones operand.
-// Online softmax in fp32 with exp2 and the 1/sqrt(d) scale folded into the
-// exponent; P is rounded to bf16 for the MFMA.  The running max is only
-// raised (and O, l rescaled) when a block's max exceeds it by more than 2^8,
-// which keeps the rescale off the common path without changing the math.
+// Formulation (v_mfma_f32_32x32x16_bf16 throughout): a wave owns 64 queries as
+// two 32-query tiles and walks the segment's keys 32 at a time.
+//  * S^T = K Q^T: keys are MFMA rows, queries columns, head_dim the reduction
+//    (80 = 5 x 16, no padded chunk).  Each lane ends up with 16 keys
+//    (rows 8g + 4h + e, h = lane / 32) of one query (lane % 32), so the row
+//    max is 15 in-lane maxima and one permlane32 swap with the lane holding
+//    the other 16 keys.
+//  * O^T = V^T P^T: the lane's 16 probabilities are directly its B operands
+//    for the two 16-key reduction chunks (chunk c takes rows g = 2c, 2c + 1),
+//    provided V^T fragments list keys in the same order, which the V^T reads
+//    do (keys 16c + 4h + 0..3 and 16c + 8 + 4h + 0..3).  P never leaves
+//    registers.
+//  * The softmax denominator comes from the padding of the last O^T row tile:
+//    row head_dim of the V^T tile holds ones (and the rows after it zeros), so
+//    O^T row head_dim accumulates sum_k P.
+// Online softmax in fp32 with exp2 and the 1/sqrt(d) scale folded into one
+// FMA; P is rounded to bf16 for the MFMA.  The running max is only raised (and
+// O rescaled) when a block's max exceeds it by more than 2^8, which keeps the
+// rescale off the common path without changing the math.
 //
-// Per-score VALU work is what bounds this kernel on CDNA4 (exp runs at a
-// quarter of the FMA rate), so a step is 32 keys x 64 queries per wave, the
-// whole state fits in 256 registers and two waves share each SIMD, letting
-// one wave's MFMAs run under the other's softmax.  K tiles (32 keys x head_dim,
-// row stride head_dim + 8) and V^T tiles (head_dim x 32 keys, row stride 36)
-// move global -> LDS with gfx950's direct loads into a double-buffered ring.
-// Work units are laid out so each XCD (workgroups are dispatched round-robin
-// over 8 XCDs) runs contiguous (head, segment) ranges and shares their K/V in
-// its L2.  Long segments use 4-wave workgroups (256 queries share each K/V
-// tile); short segments (windows) use 1-wave workgroups of 64 queries.
+// K tiles (32 keys x head_dim, row stride head_dim + 8 so 16-byte fragment
+// reads of 16 consecutive rows hit distinct banks) and V^T tiles (head_dim
+// rows x 32 keys, row stride 36) move global -> LDS with gfx950's buffer loads
+// into LDS, into a double-buffered ring.  Work units are laid out so each XCD
+// (workgroups are dispatched round-robin over 8 XCDs) runs contiguous
+// (head, segment) ranges and shares their K/V in its L2.  Long segments use
+// 4-wave workgroups (256 queries share each K/V tile); short segments
+// (windows) use 1-wave workgroups of 64 queries.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -43,43 +47,60 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int KB = 32;   // keys per step
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit dword format, no swizzle
+constexpr int QT = 2;    // 32-query tiles per wave (64 queries)
 
-// max over lanes l and l ^ 16 (rows of 16 lanes swapped pairwise in registers, no LDS trip)
-__device__ __forceinline__ float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
-                                                  false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
-}
-// max over lanes l and l ^ 32
+// the value held by lanes l and l ^ 32: both halves of x are swapped into place in registers
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
                                                   false, false);
   return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
 }
-constexpr int QT = 4;    // 16-query tiles per wave (64 queries)
+// x of lane l & 31 (lower half) in every lane
+__device__ __forceinline__ float from_lower_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, r[0]);
+}
+// x of lane (l & 31) + 32 (upper half) in every lane
+__device__ __forceinline__ float from_upper_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, r[1]);
+}
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
 
 template <int HD, int NW>
 __global__ void __launch_bounds__(NW * 64, 2)
 attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
-  constexpr int KS = HD + 8;             // K tile row stride (elements): 16-byte chunks
-  constexpr int KCH = KS / 8;            // chunks per LDS row (the last one is padding)
-  constexpr int KLOADS = (KB * KCH + 63) / 64;     // 1 KB direct loads per K tile
-  constexpr int VS = KB + 4;             // V^T tile row stride (elements)
-  constexpr int VDW = VS / 2;            // dwords per V^T row
-  constexpr int VLOADS = (HD * VDW + 63) / 64;     // 256 B direct loads per V^T tile
-  // 32-wide reduction chunks of the head dim; with head_dim = 16 (mod 32) the last chunk
-  // holds 16 dims in its first two lane groups and zeros in the other two (a 16x16x16 MFMA
-  // costs as many cycles as a 16x16x32 one, so the padding is free)
-  constexpr int NC = (HD + 31) / 32;
-  constexpr bool TAIL = (HD % 32) == 16;
-  constexpr int ND = HD / 16;
-  static_assert(HD % 16 == 0 && (KS * 2) % 16 == 0, "head_dim must be a multiple of 16");
+  constexpr int NCH = HD / 16;               // 16-wide reduction chunks of S^T = K Q^T
+  constexpr int DT = (HD + 1 + 31) / 32;     // 32-row tiles of O^T, incl. the row of ones
+  constexpr int KS = HD + 8;                 // K tile row stride (elements)
+  constexpr int KCH = KS / 8;                // 16-byte chunks per K row (the last is padding)
+  constexpr int KLOADS = (KB * KCH + 63) / 64;      // 1 KB direct loads per K tile
+  constexpr int VS = KB + 4;                 // V^T tile row stride (elements)
+  constexpr int VDW = VS / 2;                // dwords per V^T row
+  constexpr int VROWS = DT * 32;             // rows HD.. are constant (ones, then zeros)
+  constexpr int VLOADS = (HD * VDW + 63) / 64;      // 256 B direct loads per V^T tile
+  constexpr int LROW = HD - 32 * (DT - 1);   // row of the sums inside the last O^T tile
+  constexpr int LIDX = 4 * (LROW / 8) + (LROW % 4), LHALF = (LROW % 8) / 4;
+  static_assert(HD % 16 == 0 && KCH % 2 == 1, "head_dim must be a multiple of 16");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KLOADS * 64 * 8];
-  __shared__ __attribute__((aligned(16))) uint32_t sV[2][VLOADS * 64];
+  // two ring slots as separate objects: every access below names its slot statically, so
+  // the compiler can tell the prefetch into one slot from the reads of the other and does
+  // not make those reads wait for the prefetch
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[KLOADS * 64 * 8], sK1[KLOADS * 64 * 8];
+  __shared__ __attribute__((aligned(16))) uint32_t sV0[VROWS * VDW], sV1[VROWS * VDW];
 
   // ---- work unit: XCD-contiguous ranges of (head, unit), units of a segment adjacent
   const int G = n_work * a.heads;
@@ -91,113 +112,125 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
   const AttnWork wk = work[logical % n_work];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
+  const int l32 = lane & 31, h = lane >> 5;
   const int seg0 = wk.seg_start, n = wk.seg_len;
   const int qbase = wk.q0 + wv * 64;
   const uint16_t* Qh = a.q + (int64_t)head * a.n_tok * HD;
   const uint16_t* Kh = a.k + (int64_t)head * a.n_tok * HD;
   const uint16_t* Vh = a.vt + (int64_t)head * HD * a.n_tok;
 
-  // ---- this wave's query fragments (B operand of S^T = K Q^T)
-  bf16x8 qa[QT][NC];
+  // constant V^T rows: HD = ones (softmax denominator), the rest zeros; never overwritten
+  for (int i = tid; i < (VROWS - HD) * VDW; i += NW * 64) {
+    const uint32_t v = i < VDW ? 0x3f803f80u : 0u;   // bf16 1.0 pairs
+    sV0[HD * VDW + i] = v;
+    sV1[HD * VDW + i] = v;
+  }
+
+  // ---- this wave's query fragments (B operand of S^T = K Q^T): query 32t + l32, dims 16c + 8h
+  bf16x8 qf[QT][NCH];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    const int q = qbase + 16 * t + l16;
+    const int q = qbase + 32 * t + l32;
     const bool ok = q < n;
-    const uint16_t* qr = Qh + (int64_t)(seg0 + (ok ? q : 0)) * HD;
+    const uint16_t* qr = Qh + (int64_t)(seg0 + (ok ? q : 0)) * HD + 8 * h;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const bool live = ok && (!TAIL || c < NC - 1 || g4 < 2);
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + (live ? c * 32 + g4 * 8 : 0));
-      qa[t][c] = live ? v : bf16x8{};
+    for (int c = 0; c < NCH; ++c) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
+      qf[t][c] = ok ? v : bf16x8{};
     }
   }
-  bf16x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
 
-  f32x4 O[ND][QT], Ls[QT];   // O^T tiles and the row-sum tile (every row holds l)
+  f32x16 O[QT][DT];
   float m[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     m[t] = 0.f;
-    Ls[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) O[dt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) O[t][dt][e] = 0.f;
   }
   const float sc = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(head_dim)
   const int nkb = (n + KB - 1) / KB;
 
-  // Direct global -> LDS tile loads.  Keys past the segment end read the last key (K) or
-  // the last key pair (V^T): their scores are masked to -inf, so they contribute P = 0.
-  auto dload = [&](int kb, int buf) {
-    const int key0 = kb * KB;
+  // Direct global -> LDS tile loads through buffer resources over this head's K and V^T:
+  // each lane keeps one 32-bit offset per load and the block's key offset rides in the
+  // scalar offset.  Keys past the segment end read the next segment's keys (or zeros past
+  // the end of the buffer); their scores are masked to -inf, so they contribute P = 0.
+  constexpr int KLW = (KLOADS + NW - 1) / NW, VLW = (VLOADS + NW - 1) / NW;
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kh), (short)0,
+                                                    (int)(a.n_tok * HD * 2), kRsrcWord3);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vh), (short)0,
+                                                    (int)(a.n_tok * HD * 2), kRsrcWord3);
+  // (fixed-size arrays: a dependent bound here fails the host-side instantiation with this
+  // clang; only the first KLW / VLW entries are used)
+  static_assert(KLW <= 8 && VLW <= 24, "load plan");
+  uint32_t koff[8], voff[24];
 #pragma unroll
-    for (int j = 0; j < (KLOADS + NW - 1) / NW; ++j) {
+  for (int j = 0; j < KLW; ++j) {
+    const int id = (wv + j * NW) * 64 + lane, r = id / KCH, c = id % KCH;
+    koff[j] = (uint32_t)(r * HD + (c < HD / 8 ? c * 8 : 0)) * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < VLW; ++j) {
+    const int id = (wv + j * NW) * 64 + lane, dd = id / VDW, c = id % VDW;
+    voff[j] = dd < HD ? (uint32_t)(dd * a.n_tok + (c < KB / 2 ? 2 * c : 0)) * 2 : 0u;
+  }
+  auto dload = [&](int kb, uint16_t* dK, uint32_t* dV) {
+    const uint32_t key0 = (uint32_t)(seg0 + kb * KB);
+#pragma unroll
+    for (int j = 0; j < KLW; ++j) {
       const int i = wv + j * NW;
       if (i >= KLOADS) break;
-      const int id = i * 64 + lane, r = id / KCH, c = id % KCH;
-      const int key = min(key0 + r, n - 1);
-      const uint16_t* src = Kh + (int64_t)(seg0 + key) * HD + (c < HD / 8 ? c * 8 : 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(&sK[buf][i * 64 * 8]), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dK + i * 64 * 8), 16,
+                                               koff[j], key0 * HD * 2, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < (VLOADS + NW - 1) / NW; ++j) {
+    for (int j = 0; j < VLW; ++j) {
       const int i = wv + j * NW;
       if (i >= VLOADS) break;
-      const int id = i * 64 + lane, dd = id / VDW, c = id % VDW;
-      const int key = min(key0 + 2 * c, n - 2);
-      const uint16_t* src = (dd < HD && c < KB / 2) ? Vh + (int64_t)dd * a.n_tok + seg0 + key : Vh;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(&sV[buf][i * 64]), 4, 0, 0);
+      if ((i * 64 + lane) / VDW < HD)   // lanes past the real rows must not touch the constant rows
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dV + i * 64), 4,
+                                                 voff[j], key0 * 2, 0, 0);
     }
   };
 
-  dload(0, 0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) dload(kb + 1, buf ^ 1);
+  // one key block: prefetch block kb + 1 into (nK, nV) while computing on (cK, cV)
+  auto block = [&](int kb, const uint16_t* cK, const uint32_t* cV, uint16_t* nK, uint32_t* nV) {
+    if (kb + 1 < nkb) dload(kb + 1, nK, nV);
     if (qbase < n) {
-      const uint16_t* Kt = sK[buf];
-      const uint16_t* Vt = reinterpret_cast<const uint16_t*>(sV[buf]);
-      // ---- S^T tiles: 2 key tiles x QT query tiles
-      f32x4 S[2][QT];
+      const uint16_t* Kt = cK;
+      const uint16_t* Vt = reinterpret_cast<const uint16_t*>(cV);
+      // ---- S^T = K Q^T for both query tiles: rows = 32 keys, columns = 32 queries
+      f32x16 S[QT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const uint16_t* kr = Kt + (kt * 16 + l16) * KS;
-        bf16x8 ka[NC];
+      for (int t = 0; t < QT; ++t)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) ka[c] = *reinterpret_cast<const bf16x8*>(kr + c * 32 + g4 * 8);
-        // upper lane groups of a half chunk read the row padding and the next row: zero them
-        if constexpr (TAIL) ka[NC - 1] = g4 < 2 ? ka[NC - 1] : bf16x8{};
+        for (int e = 0; e < 16; ++e) S[t][e] = 0.f;
+      const uint16_t* kr = Kt + l32 * KS + 8 * h;
 #pragma unroll
-        for (int t = 0; t < QT; ++t) {
-          f32x4 s{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < NCH; ++c) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * c);
 #pragma unroll
-          for (int c = 0; c < NC; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qa[t][c], s, 0, 0, 0);
-          S[kt][t] = s;
-        }
+        for (int t = 0; t < QT; ++t) S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][c], S[t], 0, 0, 0);
       }
-      // ---- mask keys past the segment end (last step only)
+      // ---- mask keys past the segment end (last step only); lane's keys are 8g + 4h + e
       const int key_base = kb * KB;
       if (key_base + KB > n) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int e = 0; e < 16; ++e)
+          if (key_base + 8 * (e / 4) + 4 * h + (e % 4) >= n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (key_base + kt * 16 + g4 * 4 + i >= n)
-#pragma unroll
-              for (int t = 0; t < QT; ++t) S[kt][t][i] = -INFINITY;
+            for (int t = 0; t < QT; ++t) S[t][e] = -INFINITY;
       }
-      // ---- online softmax per query column (lazy offset: raised only by > 2^8)
-      bf16x8 pb[QT];
+      // ---- online softmax per query (lazy offset: raised only by > 2^8)
+      bf16x8 pb[QT][2];
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
-        float mx = fmaxf(fmaxf(fmaxf(S[0][t][0], S[0][t][1]), fmaxf(S[0][t][2], S[0][t][3])),
-                         fmaxf(fmaxf(S[1][t][0], S[1][t][1]), fmaxf(S[1][t][2], S[1][t][3])));
-        mx = max_xor32(max_xor16(mx));
+        float mx = S[t][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[t][e]);
+        mx = max_xor32(mx);
         const float bm = mx * sc;
         if (kb == 0) {
           m[t] = bm;
@@ -207,51 +240,64 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
             const float mn = need ? bm : m[t];
             const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
             m[t] = mn;
-            Ls[t] *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < ND; ++dt) O[dt][t] *= alpha;
+            for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
           }
         }
         const float mo = m[t];
+        uint32_t pw[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[t][i] = (__bf16)__builtin_amdgcn_exp2f(S[0][t][i] * sc - mo);
-          pb[t][4 + i] = (__bf16)__builtin_amdgcn_exp2f(S[1][t][i] * sc - mo);
+        for (int i = 0; i < 8; ++i)
+          pw[i] = pack_bf16(__builtin_amdgcn_exp2f(S[t][2 * i] * sc - mo), __builtin_amdgcn_exp2f(S[t][2 * i + 1] * sc - mo));
+        pb[t][0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        pb[t][1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+      }
+      // ---- O^T += V^T P^T over the 32 keys; V^T fragment of chunk c lists keys
+      //      16c + 4h + 0..3, 16c + 8 + 4h + 0..3 (the order of the lane's probabilities)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* vr = Vt + (32 * dt + l32) * VS + 4 * h;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + 16 * c);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16 * c + 8);
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int t = 0; t < QT; ++t) O[t][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][c], O[t][dt], 0, 0, 0);
         }
       }
-      // ---- O^T += V^T P^T (and l += 1^T P^T) over the 32 keys
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        const uint16_t* vr = Vt + (dt * 16 + l16) * VS + g4 * 4;
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int t = 0; t < QT; ++t) O[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[t], O[dt][t], 0, 0, 0);
-      }
-#pragma unroll
-      for (int t = 0; t < QT; ++t) Ls[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t], Ls[t], 0, 0, 0);
     }
     __syncthreads();
+  };
+
+  dload(0, sK0, sV0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; kb += 2) {
+    block(kb, sK0, sV0, sK1, sV1);
+    if (kb + 1 < nkb) block(kb + 1, sK1, sV1, sK0, sV0);
   }
 
   if (qbase >= n) return;
   const int ld = a.heads * HD;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    const int q = qbase + 16 * t + l16;
+    const int q = qbase + 32 * t + l32;
+    // the row sum sits in the lanes of one half: bring it to both halves
+    const float lsum_own = O[t][DT - 1][LIDX];
+    const float lsum = LHALF == 0 ? from_lower_half(lsum_own) : from_upper_half(lsum_own);
     if (q < n) {
-      const float inv = 1.0f / Ls[t][0];
-      uint16_t* orow = a.o + (int64_t)(seg0 + q) * ld + head * HD + g4 * 4;
+      const float inv = 1.0f / lsum;
+      uint16_t* orow = a.o + (int64_t)(seg0 + q) * ld + head * HD + 4 * h;
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        uint2 pk;
-        pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(O[dt][t][0] * inv)) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(O[dt][t][1] * inv)) << 16);
-        pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(O[dt][t][2] * inv)) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(O[dt][t][3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(orow + dt * 16) = pk;
-      }
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * dt + 8 * g;   // + 4h + e
+          if (d + 8 > HD) continue;
+          const f32x16& o = O[t][dt];
+          *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16(o[4 * g] * inv, o[4 * g + 1] * inv),
+                                                           pack_bf16(o[4 * g + 2] * inv, o[4 * g + 3] * inv));
+        }
     }
   }
 }
@@ -271,6 +317,10 @@ hipError_t run_hd(const AttnArgs& a, hipStream_t st) {
 
 vit_status launch_attention(const AttnArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.n_tok * a.head_dim * 2 >= ((int64_t)1 << 31)) {
+    set_error("attention: %lld tokens exceed the 2 GiB per-head operand limit", (long long)a.n_tok);
+    return VIT_E_ARG;
+  }
   hipError_t e;
   switch (a.head_dim) {
     case 32: e = run_hd<32>(a, st); break;

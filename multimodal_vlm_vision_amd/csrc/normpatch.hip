@@ -55,8 +55,12 @@ struct alignas(4) Piece {
 
 static_assert(kFeatPad % 8 == 0 && kFeatPad >= kFeat, "row padding");
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // feature f = ((c * 2 + tau) * 14 + i) * 14 + j of the unit's top-left patch ->

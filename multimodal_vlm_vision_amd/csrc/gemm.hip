@@ -111,7 +111,7 @@ __device__ __forceinline__ void store_act(const GemmArgs& p, int m, int n, float
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT>
+template <int BM, int BN, int WM, int WN, bool SPLIT, int OCC = 1>
 struct Geo {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
@@ -124,16 +124,17 @@ struct Geo {
   static constexpr int LA = AR / RPL / NW;               // A loads per wave per stage
   static constexpr int LB = BN / RPL / NW;               // B loads per wave per stage
   static constexpr int LPW = LA + LB;
-  static constexpr int kFit = kLdsBytes / kStageBytes;
-  static constexpr int STAGES = kFit >= 4 ? 4 : 3;
+  static constexpr int kBudget = kLdsBytes / OCC;          // OCC workgroups share a CU's LDS
+  static constexpr int kFit = kBudget / kStageBytes;
+  static constexpr int STAGES = kFit >= 4 ? 4 : kFit;
   static constexpr int SST = TN * 32 + 8;                // epilogue slice row stride (floats)
   static constexpr int kSliceBytes = NW * 32 * SST * 4;  // one fp32 slice per wave
   static constexpr int kRing = STAGES * kStageBytes;
   static constexpr int kSmem = kRing > kSliceBytes ? kRing : kSliceBytes;
   static_assert(TM >= 1 && TN >= 2 && TN % 2 == 0, "wave tile must hold column pairs");
   static_assert(AR % (RPL * NW) == 0 && BN % (RPL * NW) == 0, "load split");
-  static_assert(kFit >= 3, "three stages must fit in LDS");
-  static_assert(kSmem <= kLdsBytes, "LDS budget");
+  static_assert(kFit >= 2, "two stages must fit in LDS");
+  static_assert(kSmem <= kBudget, "LDS budget");
   static_assert((STAGES - 2) * LPW < 64, "vmcnt range");
 };
 
@@ -219,10 +220,10 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI>
-__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI, int OCC>
+__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_kernel(GemmArgs p) {
-  using G = Geo<BM, BN, WM, WN, SPLIT>;
+  using G = Geo<BM, BN, WM, WN, SPLIT, OCC>;
   constexpr int TM = G::TM, TN = G::TN, LA = G::LA, LB = G::LB, S = G::STAGES, AR = G::AR;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
@@ -395,32 +396,35 @@ gemm_kernel(GemmArgs p) {
   }
 }
 
-// Tile configurations (all 2x2 or 2x1 waves, one workgroup per CU):
-//   L 256x256 (waves of 128x128), T 192x256 (96x128), H 128x256 (64x128), S 64x64 (2 waves of 32x64).
-enum Cfg { CFG_L, CFG_T, CFG_H, CFG_S };
+// Tile configurations (2x2 or 2x1 waves):
+//   L 256x256 (waves of 128x128), T 192x256 (96x128), H 128x256 (64x128), S 64x64 (2 waves of
+//   32x64), one workgroup per CU; O 128x256 with two workgroups per CU, so one workgroup's
+//   epilogue (residual read-modify-write, activation stores) runs under the other's main loop.
+enum Cfg { CFG_L, CFG_T, CFG_H, CFG_O, CFG_S };
 struct CfgInfo {
-  int cfg, bm, bn, wave_n;
-  double eff;   // relative MFMA efficiency of the main loop (larger wave tiles read less LDS per MFMA)
+  int cfg, bm, bn, wave_n, occ;
+  double eff;   // relative efficiency (larger wave tiles read less LDS per MFMA)
 };
 // (efficiencies fitted to measured times of the tower's products on MI355X)
-constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 128, 1.0},
-                             {CFG_T, 192, 256, 128, 0.98},
-                             {CFG_H, 128, 256, 128, 0.9},
-                             {CFG_S, 64, 64, 64, 0.3}};
+constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 128, 1, 1.0},
+                             {CFG_T, 192, 256, 128, 1, 0.98},
+                             {CFG_H, 128, 256, 128, 1, 0.9},
+                             {CFG_O, 128, 256, 128, 2, 1.1},
+                             {CFG_S, 64, 64, 64, 1, 0.3}};
 
-template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI>
+template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI, int OCC = 1>
 hipError_t run(const GemmArgs& a, hipStream_t st) {
-  using G = Geo<BM, BN, WM, WN, SPLIT>;
+  using G = Geo<BM, BN, WM, WN, SPLIT, OCC>;
   const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, SPLIT, EPI>), dim3((unsigned)tiles), dim3(G::NT), G::kSmem, st,
-                     a);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC>), dim3((unsigned)tiles), dim3(G::NT), G::kSmem,
+                     st, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI>
+template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI, int OCC = 1>
 hipError_t allow_smem() {
-  using G = Geo<BM, BN, WM, WN, SPLIT>;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, SPLIT, EPI>),
+  using G = Geo<BM, BN, WM, WN, SPLIT, OCC>;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
 }
 
@@ -429,6 +433,7 @@ hipError_t allow_smem_all() {
   hipError_t e = allow_smem<256, 256, 2, 2, SPLIT, EPI>();
   if (e == hipSuccess) e = allow_smem<192, 256, 2, 2, SPLIT, EPI>();
   if (e == hipSuccess) e = allow_smem<128, 256, 2, 2, SPLIT, EPI>();
+  if (e == hipSuccess) e = allow_smem<128, 256, 2, 2, SPLIT, EPI, 2>();
   if (e == hipSuccess) e = allow_smem<64, 64, 2, 1, SPLIT, EPI>();
   return e;
 }
@@ -439,11 +444,12 @@ hipError_t run_cfg(int cfg, const GemmArgs& a, hipStream_t st) {
     case CFG_L: return run<256, 256, 2, 2, SPLIT, EPI>(a, st);
     case CFG_T: return run<192, 256, 2, 2, SPLIT, EPI>(a, st);
     case CFG_H: return run<128, 256, 2, 2, SPLIT, EPI>(a, st);
+    case CFG_O: return run<128, 256, 2, 2, SPLIT, EPI, 2>(a, st);
     default: return run<64, 64, 2, 1, SPLIT, EPI>(a, st);
   }
 }
 
-// Estimated time ~ rounds of 256 workgroups x tile area / relative efficiency.
+// Estimated time ~ rounds of (256 * occupancy) workgroups x per-CU area of a round / efficiency.
 int pick_cfg(int epi, const GemmArgs& a) {
   int best = -1;
   double best_t = 1e300;
@@ -451,7 +457,11 @@ int pick_cfg(int epi, const GemmArgs& a) {
     if (a.N % c.bn) continue;
     if (epi == EPI_QKV && (a.hidden % c.wave_n)) continue;   // a wave's columns stay in one of q / k / v
     const double tiles = (double)((a.M + c.bm - 1) / c.bm) * (a.N / c.bn);
-    const double t = std::ceil(tiles / 256.0) * c.bm * c.bn / c.eff;
+    const double rounds = std::ceil(tiles / (256.0 * c.occ));
+    // co-resident workgroups only hide each other's epilogues once they are staggered,
+    // i.e. from the second round on; a single round runs like one workgroup per CU
+    const double eff = (c.occ > 1 && rounds < 2) ? 0.9 : c.eff;
+    const double t = rounds * c.occ * c.bm * c.bn / eff;
     if (t < best_t) {
       best_t = t;
       best = c.cfg;

@@ -54,6 +54,39 @@ def cpu_baseline(wl, n_items=3):
                       f"float64 NumPy, {dt:.1f} s"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen2vl-8img-mixed-32L.md")
+
+
+def kernel_sources_digest():
+    """sha256 over the HIP kernel sources: counter figures taken with other kernels are stale."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "multimodal_vlm_vision_amd", "csrc", "*.hip"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary (copy-calibrated), or None when absent or taken with different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(blob)
+    except (OSError, IndexError, ValueError):
+        return None, None
+    if data.get("kernel_sources_sha256_16") != kernel_sources_digest():
+        return None, "stale: kernels changed since the counters were taken"
+    row = data.get("per_launch", {}).get(kernel)
+    if not row:
+        return None, None
+    return row["fetch_bytes"] + row["write_bytes"], os.path.relpath(TRAFFIC_FILE, ROOT)
+
+
 def normpatch_stream(n_images=48, side=1344, reps=5):
     """normpatch alone on a >= 1 GB streaming batch (48 images of 1344 x 1344): the
     per-forward traffic of the bench batch (~52 MB) fits in the 256 MB last-level cache,
@@ -103,6 +136,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workload", type=int, default=WORKLOAD)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 512 MiB device-to-device copy (3 times): the known-size kernel "
+                         "that scales the HBM byte counters of a rocprofv3 --pmc run")
+    ap.add_argument("--no-stream", action="store_true", help="skip the normpatch streaming measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the vision tower is not sharded "
@@ -212,11 +249,20 @@ def main():
         "kernels": kern,
     }
     graph.close()
-    log("normpatch streaming measurement ...")
-    line["normpatch_stream"] = normpatch_stream()
-    ns = line["normpatch_stream"]
-    log(f"normpatch stream: {ns['patches']} patches, {ns['bytes_per_launch'] / 1e9:.2f} GB/launch, "
-        f"{ns['avg_us']:.1f} us, {ns['gbs']:.0f} GB/s ({100 * ns['hbm_frac']:.1f}% of HBM peak)")
+    roof["traffic"], roof["traffic_source"] = measured_traffic(dom)
+    if not args.no_stream:
+        log("normpatch streaming measurement ...")
+        line["normpatch_stream"] = normpatch_stream()
+        ns = line["normpatch_stream"]
+        log(f"normpatch stream: {ns['patches']} patches, {ns['bytes_per_launch'] / 1e9:.2f} GB/launch, "
+            f"{ns['avg_us']:.1f} us, {ns['gbs']:.0f} GB/s ({100 * ns['hbm_frac']:.1f}% of HBM peak)")
+    if args.calibrate_copy:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x 512 MiB device-to-device")
     if not args.no_cpu:
         log("CPU oracle baseline ...")
         line["cpu_baseline"] = cpu_baseline(wl)

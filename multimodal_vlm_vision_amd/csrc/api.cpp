@@ -66,6 +66,17 @@ vit_status copy_out(const Stop& st, const void* src, size_t bytes, hipStream_t s
   return VIT_OK;
 }
 
+// Debug copy of a blocked bf16 GEMM operand as row-major [rows][out_cols] (see launch_unblock).
+vit_status copy_blocked(const Stop& st, const uint16_t* src, int64_t rows, int cols, int group, int out_cols,
+                        hipStream_t s) {
+  const size_t bytes = (size_t)rows * out_cols * 2;
+  if (st.dst_bytes < bytes) {
+    set_error("debug stage needs %zu bytes, dst has %zu", bytes, st.dst_bytes);
+    return VIT_E_WORKSPACE;
+  }
+  return launch_unblock(src, rows, cols, group, out_cols, static_cast<uint16_t*>(st.dst), s);
+}
+
 vit_status check_common(const vit_ctx* ctx, const vit_plan* plan, const void* ws, size_t ws_bytes) {
   if (!ctx || !plan) {
     set_error("ctx and plan must not be NULL");
@@ -171,12 +182,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
            launch_normpatch(pixels, units, pl->n_units, W.lut, ctx->norm_affine ? &ctx->affine : nullptr, X, st));
   else
     LAUNCH("normrows_u8", 0, Nd * kFeat * 3, false, launch_normrows_u8(patches, N, W.lut, X, st));
-  if (stop.hit(-1, 0)) {
-    if (stop.dst_bytes < (size_t)N * kFeat * 2) return copy_out(stop, X, (size_t)N * kFeat * 2, st);
-    HIP_TRY(hipMemcpy2DAsync(stop.dst, kFeat * 2, X, kFeatPad * 2, kFeat * 2, N,
-                             hipMemcpyDeviceToDevice, st));
-    return VIT_OK;
-  }
+  if (stop.hit(-1, 0)) return copy_blocked(stop, X, N, kFeatPad, 1, kFeat, st);
 
   // 2. patch embedding (conv with kernel == stride as one GEMM), fp32 into the residual
   GemmArgs g;
@@ -185,12 +191,12 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   LAUNCH("gemm_patch_embed", 2.0 * Nd * dd * kFeat, 0, true, launch_gemm(EPI_F32, g, st));
   if (stop.hit(-1, 1)) return copy_out(stop, R, (size_t)N * d * 4, st);
 
-  const double norm_bytes = Nd * dd * 6;   // fp32 row in, bf16 row out
+  const double norm_bytes = Nd * dd * (4 + 2 * S);   // fp32 row in, bf16 row (hi and lo) out
   for (int l = 0; l < c.layers; ++l) {
     const LayerW& L = W.layers[l];
     LAUNCH("rownorm", 0, norm_bytes, false,
-           launch_rownorm(c.norm_kind, R, N, d, L.n1g, L.n1b, c.norm_eps, H, split, st));
-    if (stop.hit(l, 1)) return copy_out(stop, H, (size_t)N * S * d * 2, st);
+           launch_rownorm(c.norm_kind, R, N, d, L.n1g, L.n1b, c.norm_eps, H, split, 1, st));
+    if (stop.hit(l, 1)) return copy_blocked(stop, H, N, S * d, 1, S * d, st);
 
     GemmArgs q;
     q.A = H; q.lda = S * d; q.B = L.qkv_w; q.ldb = d; q.a_group = split ? d : 0;
@@ -219,7 +225,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
       a2.n_short = lists.n_short;
       LAUNCH("attention_short", 4.0 * dd * lists.sq_short, 0, true, launch_attention(a2, st));
     }
-    if (stop.hit(l, 5)) return copy_out(stop, O, (size_t)N * d * 2, st);
+    if (stop.hit(l, 5)) return copy_blocked(stop, O, N, d, 1, d, st);
 
     GemmArgs pj;
     pj.A = O; pj.lda = d; pj.B = L.proj_w; pj.ldb = d;
@@ -228,8 +234,8 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     if (stop.hit(l, 6)) return copy_out(stop, R, (size_t)N * d * 4, st);
 
     LAUNCH("rownorm", 0, norm_bytes, false,
-           launch_rownorm(c.norm_kind, R, N, d, L.n2g, L.n2b, c.norm_eps, H, split, st));
-    if (stop.hit(l, 7)) return copy_out(stop, H, (size_t)N * S * d * 2, st);
+           launch_rownorm(c.norm_kind, R, N, d, L.n2g, L.n2b, c.norm_eps, H, split, 1, st));
+    if (stop.hit(l, 7)) return copy_blocked(stop, H, N, S * d, 1, S * d, st);
 
     GemmArgs f1;
     f1.A = H; f1.lda = S * d; f1.B = L.fc1_w; f1.ldb = d; f1.a_group = split ? d : 0;
@@ -243,7 +249,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
       LAUNCH("gemm_gateup_swiglu", 4.0 * Nd * c.mlp_dim * dd, 0, true,
              launch_gemm(EPI_SWIGLU, f1, st));
     }
-    if (stop.hit(l, 8)) return copy_out(stop, F, (size_t)N * S * mp * 2, st);
+    if (stop.hit(l, 8)) return copy_blocked(stop, F, N, S * mp, 1, S * mp, st);
 
     GemmArgs f2;
     f2.A = F; f2.lda = S * mp; f2.B = L.fc2_w; f2.ldb = mp; f2.a_group = split ? mp : 0;
@@ -252,11 +258,12 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     if (stop.hit(l, 9)) return copy_out(stop, R, (size_t)N * d * 4, st);
   }
 
-  // merger: per-patch norm, 4 rows -> one 4d vector (free: rows are adjacent), MLP
+  // merger: per-patch norm written straight into the merger's view (a unit's 4 patch rows
+  // side by side as one row of 4 * S * d columns), then the MLP
   const int L = c.layers;
   LAUNCH("rownorm", 0, norm_bytes, false,
-         launch_rownorm(c.norm_kind, R, N, d, W.mq_g, W.mq_b, c.norm_eps, H, split, st));
-  if (stop.hit(L, 1)) return copy_out(stop, H, (size_t)N * S * d * 2, st);
+         launch_rownorm(c.norm_kind, R, N, d, W.mq_g, W.mq_b, c.norm_eps, H, split, 4, st));
+  if (stop.hit(L, 1)) return copy_blocked(stop, H, N, S * d, 4, S * d, st);
   const int64_t U = pl->n_units;
   const double Ud = (double)U;
   GemmArgs m1;
@@ -264,7 +271,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   m1.M = (int)U; m1.N = 4 * d; m1.K = 4 * d; m1.bias = W.m1_b; m1.out = F; m1.ldo = S * 4 * d;
   m1.split_off = split ? 4 * d : 0;
   LAUNCH("gemm_merger_fc1_gelu", 2.0 * Ud * 16 * dd * dd, 0, true, launch_gemm(EPI_GELU, m1, st));
-  if (stop.hit(L, 2)) return copy_out(stop, F, (size_t)U * S * 4 * d * 2, st);
+  if (stop.hit(L, 2)) return copy_blocked(stop, F, U, S * 4 * d, 1, S * 4 * d, st);
   GemmArgs m2;
   m2.A = F; m2.lda = S * 4 * d; m2.B = W.m2_w; m2.ldb = 4 * d; m2.a_group = split ? 4 * d : 0;
   m2.M = (int)U; m2.N = c.out_dim; m2.K = 4 * d; m2.bias = W.m2_b; m2.out = out; m2.ldo = c.out_dim;

@@ -287,7 +287,9 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
     const float lsum = LHALF == 0 ? from_lower_half(lsum_own) : from_upper_half(lsum_own);
     if (q < n) {
       const float inv = 1.0f / lsum;
-      uint16_t* orow = a.o + (int64_t)(seg0 + q) * ld + head * HD + 4 * h;
+      // output row in the blocked GEMM layout (the out-projection's A operand); 4 values per store
+      const int64_t orow = seg0 + q;
+      const int ocol = head * HD + 4 * h;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -295,8 +297,9 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
           const int d = 32 * dt + 8 * g;   // + 4h + e
           if (d + 8 > HD) continue;
           const f32x16& o = O[t][dt];
-          *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16(o[4 * g] * inv, o[4 * g + 1] * inv),
-                                                           pack_bf16(o[4 * g + 2] * inv, o[4 * g + 3] * inv));
+          *reinterpret_cast<uint2*>(a.o + kt_index(orow, ocol + d, ld)) =
+              make_uint2(pack_bf16(o[4 * g] * inv, o[4 * g + 1] * inv),
+                         pack_bf16(o[4 * g + 2] * inv, o[4 * g + 3] * inv));
         }
     }
   }

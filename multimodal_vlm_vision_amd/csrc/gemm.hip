@@ -1,8 +1,8 @@
 // bf16 MFMA GEMM for gfx950 with fused epilogues.
 //
-// C[M][N] = A[M][K] * B[N][K]^T: both operands are K-contiguous (activations
-// row-major, weights stored [out, in]), fp32 accumulation in
-// v_mfma_f32_32x32x16_bf16.  Used for every dense product of the tower:
+// C[M][N] = A[M][K] * B[N][K]^T: both operands in the blocked layout of
+// kt_index (16 rows x 32 K per 1 KB block; activations [tokens][features],
+// weights [out][in]), fp32 accumulation in v_mfma_f32_32x32x16_bf16.  Used for every dense product of the tower:
 // patch embedding (the stride = kernel 3D conv as one GEMM, "vLLM multimodal
 // inference | ViT performance optimisation", section 3.2), qkv, out-proj,
 // MLP and the merger MLP (sections 2.2 and 3.1).  The small elementwise steps
@@ -19,14 +19,18 @@
 //
 // Main loop (per workgroup tile BM x BN, 2x2 waves of (BM/2) x (BN/2)):
 //  * K advances 32 columns per stage.  Tiles move global -> LDS with gfx950's
-//    buffer loads into LDS (no VGPR staging): every lane keeps one fixed
-//    32-bit row offset per load and the K advance rides in the scalar
-//    offset.  LDS rows are 64 bytes; the four 16-byte chunks of row r sit
-//    at chunk ^ (((r >> 1) ^ (r >> 3)) & 3), so the 32x32x16 fragment reads
-//    (32 rows, one chunk) touch distinct banks in every 8- and 16-lane group.
-//  * A ring of 3-4 stages: the loads for stage kt+S-1 are issued while stage
-//    kt is multiplied; one barrier per stage, preceded by an exact vmcnt
-//    wait for the next stage only, so later stages stay in flight.
+//    buffer loads into LDS (no VGPR staging): one 64-lane 16-byte load moves
+//    one 1 KB operand block (whole cache lines: rows of 64-byte K slices would
+//    touch twice as many lines and halve the CU's load rate), every lane keeps
+//    one fixed 32-bit block offset per load and the K advance rides in the
+//    scalar offset.  LDS rows are 64 bytes; the blocked layout already puts
+//    the four 16-byte chunks of row r at chunk ^ (((r >> 1) ^ (r >> 3)) & 3),
+//    so the 32x32x16 fragment reads (32 rows, one chunk) touch distinct banks
+//    in every 8- and 16-lane group.
+//  * A ring of 2-4 stages: a stage's slot is refilled as soon as every wave
+//    has read it (the barrier in the middle of the next stage), so each load
+//    has S-1 whole stages to land; one barrier per stage, preceded by an
+//    exact vmcnt wait for the next stage only.
 //  * MFMA operand fragments are double-buffered in registers: the reads for
 //    the next 16-wide K step are interleaved with the current step's MFMAs.
 //  * Workgroups are remapped so each XCD (dispatch is round-robin over 8
@@ -57,7 +61,6 @@ constexpr int kGroupM = 8;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit dword format, no swizzle
 constexpr int kLdsBytes = 160 * 1024;
 
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
 
 // s_waitcnt vmcnt(n) with lgkm and exp counters left alone (gfx9 encoding)
 template <int N>
@@ -99,15 +102,17 @@ __device__ __forceinline__ float4 f4add(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-// bf16 activation store: hi = bf16(y) at column n; with split_off, lo = bf16(y - hi) at n + split_off
+// bf16 activation store into the blocked layout (ldo columns): hi = bf16(y) at column n; with
+// split_off, lo = bf16(y - hi) at n + split_off.  n % 4 == 0, so the 4 values share one chunk.
 __device__ __forceinline__ void store_act(const GemmArgs& p, int m, int n, float4 y) {
-  uint16_t* o = static_cast<uint16_t*>(p.out) + (int64_t)m * p.ldo + n;
+  uint16_t* o = static_cast<uint16_t*>(p.out);
   const uint2 hi = pack4(y);
-  *reinterpret_cast<uint2*>(o) = hi;
+  *reinterpret_cast<uint2*>(o + kt_index(m, n, p.ldo)) = hi;
   if (p.split_off) {
     const float4 h = make_float4(__builtin_bit_cast(float, hi.x << 16), __builtin_bit_cast(float, hi.x & 0xffff0000u),
                                  __builtin_bit_cast(float, hi.y << 16), __builtin_bit_cast(float, hi.y & 0xffff0000u));
-    *reinterpret_cast<uint2*>(o + p.split_off) = pack4(make_float4(y.x - h.x, y.y - h.y, y.z - h.z, y.w - h.w));
+    *reinterpret_cast<uint2*>(o + kt_index(m, n + p.split_off, p.ldo)) =
+        pack4(make_float4(y.x - h.x, y.y - h.y, y.z - h.z, y.w - h.w));
   }
 }
 
@@ -135,7 +140,7 @@ struct Geo {
   static_assert(AR % (RPL * NW) == 0 && BN % (RPL * NW) == 0, "load split");
   static_assert(kFit >= 2, "two stages must fit in LDS");
   static_assert(kSmem <= kBudget, "LDS budget");
-  static_assert((STAGES - 2) * LPW < 64, "vmcnt range");
+  static_assert((STAGES - 1) * LPW < 64, "vmcnt range");
 };
 
 // Applies the epilogue to one staged 32-row slice (rows m_base.., columns n_base.., width W = TN*32).
@@ -244,9 +249,10 @@ gemm_kernel(GemmArgs p) {
   const int li = logical % in_group;
   const int m0 = (first_m + li % gsz) * BM, n0 = (li / gsz) * BN;
 
-  // ---- load plan: wave wv fills A rows [(wv*LA + j)*RPL, +RPL) and B rows likewise; lane ->
-  // row lane / CPR, physical chunk lane % CPR, which holds logical chunk swz(row, lane % CPR).
-  // Rows past M / N read the last valid row; those results are never stored.
+  // ---- load plan: wave wv's j-th load fills stage rows [(wv*LA + j)*16, +16) of A (B likewise)
+  // with one operand block; lane l lands at byte 16*l of those rows, where the block keeps it.
+  // Row groups past M / N read the last group; those results are never stored.
+  static_assert(RPL == 16, "one load = one 16-row block");
   const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.A), (short)0, (int)p.a_bytes,
                                                     kRsrcWord3);
   const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.B), (short)0, (int)p.b_bytes,
@@ -255,27 +261,26 @@ gemm_kernel(GemmArgs p) {
   // variants with this clang; only the first LA / LB entries are used)
   static_assert(LA <= 16 && LB <= 16, "load plan");
   uint32_t offa[16], offb[16];
+  const int last_ga = (p.M + 15) / 16 - 1, last_gb = p.N / 16 - 1;
+  const int64_t kba = p.lda / BK, kbb = p.ldb / BK;   // blocks per row group
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
-    const int r = (wv * LA + j) * RPL + lane / CPR;
-    const int rr = r % BM;
-    const int m = min(m0 + rr, p.M - 1);
-    const int c = swz(r, lane % CPR);
-    offa[j] = (uint32_t)(((int64_t)m * p.lda + c * 8 + (r >= BM ? p.a_group : 0)) * 2);
+    const int r = (wv * LA + j) * RPL;   // hi rows [0, BM), then lo rows [BM, 2BM)
+    const int g = min((m0 + r % BM) / 16, last_ga);
+    offa[j] = (uint32_t)((g * kba + (r >= BM ? p.a_group / BK : 0)) * 1024 + lane * 16);
   }
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
-    const int r = (wv * LB + j) * RPL + lane / CPR;
-    const int n = min(n0 + r, p.N - 1);
-    const int c = swz(AR + r, lane % CPR);
-    offb[j] = (uint32_t)(((int64_t)n * p.ldb + c * 8) * 2);
+    const int g = min((n0 + (wv * LB + j) * RPL) / 16, last_gb);
+    offb[j] = (uint32_t)(g * kbb * 1024 + lane * 16);
   }
   const int nk = p.K / BK;
   auto issue = [&](int kt, int buf) {
     kt = min(kt, nk - 1);   // past the end: reload the last stage into a free slot (never read)
     const int k0 = kt * BK;
-    const uint32_t ka = (uint32_t)(SPLIT ? (k0 / p.a_group) * 2 * p.a_group + k0 % p.a_group : k0) * 2;
-    const uint32_t kb = (uint32_t)k0 * 2;
+    // K block k0 / 32 sits 1 KB after block 0 of its row group (A: hi block; lo is a_group later)
+    const uint32_t ka = (uint32_t)((SPLIT ? (k0 / p.a_group) * 2 * p.a_group + k0 % p.a_group : k0) / BK) * 1024;
+    const uint32_t kb = (uint32_t)(k0 / BK) * 1024;
     uint16_t* st = smem + buf * G::kStage;
 #pragma unroll
     for (int j = 0; j < LA; ++j)
@@ -304,16 +309,16 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wm * TM * 32 + i * 32 + (lane & 31);
-      xa[i] = *reinterpret_cast<const bf16x8*>(st + r * BK + swz(r, c) * 8);
+      xa[i] = *reinterpret_cast<const bf16x8*>(st + r * BK + kt_chunk(r, c) * 8);
       if constexpr (SPLIT) {
         const int rl = BM + r;
-        xl[i] = *reinterpret_cast<const bf16x8*>(st + rl * BK + swz(rl, c) * 8);
+        xl[i] = *reinterpret_cast<const bf16x8*>(st + rl * BK + kt_chunk(rl, c) * 8);
       }
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = AR + wn * TN * 32 + j * 32 + (lane & 31);
-      xb[j] = *reinterpret_cast<const bf16x8*>(st + r * BK + swz(r, c) * 8);
+      xb[j] = *reinterpret_cast<const bf16x8*>(st + r * BK + kt_chunk(r, c) * 8);
     }
   };
   auto mfma_step = [&](const bf16x8 (&xa)[TM], const bf16x8 (&xl)[TM], const bf16x8 (&xb)[TN]) {
@@ -333,45 +338,46 @@ gemm_kernel(GemmArgs p) {
   constexpr int NMF = TM * TN * (SPLIT ? 2 : 1);   // MFMAs per 16-wide K step
   constexpr int NDS = TM * (SPLIT ? 2 : 1) + TN;    // fragment reads per K step
 
-  // ---- prologue: stages 0 .. S-2 in flight, stage 0 landed everywhere
+  // ---- prologue: every stage in flight, stage 0 landed everywhere
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(s, s);
-  wait_vm<(S - 2) * G::LPW>();
+  for (int s = 0; s < S; ++s) issue(s, s);
+  wait_vm<(S - 1) * G::LPW>();
   __builtin_amdgcn_s_barrier();
   lfrag(0, 0, fa[0], fl[0], fb[0]);
 
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt % S;
-    // step 0: MFMAs on K columns [0,16) of stage kt; read [16,32); refill the slot of stage kt-1.
-    // The fragment reads are issued before the loads into LDS: the compiler cannot prove that
-    // the two touch different stages, so reads placed after the loads could not move past
-    // them and the loads would issue as one burst instead of one per MFMA.
+    // step 0: MFMAs on K columns [0,16) of stage kt while reading columns [16,32)
     lfrag(buf, 1, fa[1], fl[1], fb[1]);
-    issue(kt + S - 1, (kt + S - 1) % S);
     mfma_step(fa[0], fl[0], fb[0]);
 #pragma unroll
     for (int i = 0; i < NDS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
     }
-#pragma unroll
-    for (int i = 0; i < G::LPW; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (buffer load -> LDS)
-    }
     __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // step 1: stage kt+1 must have landed (own loads), and every wave must be done with
-    // stage kt's reads before its slot is refilled next iteration
+    // step 1: stage kt+1 must have landed (own loads, then the barrier for everyone else's).
+    // Past the barrier every wave holds stage kt's last fragments in registers, so its slot is
+    // refilled right away with stage kt+S: each load has S-1 whole iterations to land.  The
+    // fragment reads are issued before the loads into LDS: the compiler cannot prove that the
+    // two touch different stages, so reads placed after the loads could not move past them
+    // and the loads would issue as one burst instead of one per MFMA.
     wait_vm<(S - 2) * G::LPW>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     lfrag((kt + 1) % S, 0, fa[0], fl[0], fb[0]);
+    issue(kt + S, buf);
     mfma_step(fa[1], fl[1], fb[1]);
 #pragma unroll
     for (int i = 0; i < NDS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < G::LPW; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (buffer load -> LDS)
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -510,16 +516,18 @@ vit_status launch_gemm(int epi, const GemmArgs& in, void* stream) {
   if (in.M <= 0) return VIT_OK;
   GemmArgs a = in;
   const bool split = a.a_group > 0;
-  if (a.N % 64 || a.K % BK || a.K <= 0 || a.lda % 8 || a.ldb % 8 || a.ldo % 4 ||
+  const int64_t a_cols = split ? 2 * (int64_t)a.K : a.K;
+  const bool bf16_out = epi == EPI_GELU || epi == EPI_SWIGLU;
+  if (a.N % 64 || a.K % BK || a.K <= 0 || a.lda % BK || a.ldb % BK || a.lda < a_cols || a.ldb < a.K ||
+      a.ldo % 4 || (bf16_out && (a.ldo % BK || a.split_off % BK)) ||
       (split && (a.a_group % BK || a.K % a.a_group))) {
-    set_error("gemm: unsupported shape M=%d N=%d K=%d group=%d (N a multiple of 64, K and the hi/lo group "
-              "multiples of 32)", a.M, a.N, a.K, a.a_group);
+    set_error("gemm: unsupported shape M=%d N=%d K=%d group=%d (N a multiple of 64; K, the hi/lo group and "
+              "the blocked operand widths multiples of 32)", a.M, a.N, a.K, a.a_group);
     return VIT_E_ARG;
   }
-  // byte extents of the operands, addressed with 32-bit buffer offsets
-  const int64_t a_cols = split ? 2 * (int64_t)a.K : a.K;
-  const int64_t a_bytes = ((int64_t)(a.M - 1) * a.lda + a_cols) * 2;
-  const int64_t b_bytes = ((int64_t)(a.N - 1) * a.ldb + a.K) * 2;
+  // byte extents of the blocked operands (rows padded to 16), addressed with 32-bit buffer offsets
+  const int64_t a_bytes = round_up(a.M, 16) * a.lda * 2;
+  const int64_t b_bytes = (int64_t)a.N * a.ldb * 2;
   if (a_bytes >= (int64_t)1 << 31 || b_bytes >= (int64_t)1 << 31) {
     set_error("gemm: operand larger than 2 GiB (M=%d N=%d K=%d)", a.M, a.N, a.K);
     return VIT_E_ARG;

@@ -5,7 +5,8 @@
 // norm epsilon defaulting to 1e-6; "vLLM multimodal inference | ViT
 // performance optimisation", section 3.5 names RMSNorm among the fused ops).
 // One wave per row; the row stays in registers, so the statistics are exact
-// two-pass sums in float32; output is rounded to nearest-even bfloat16.
+// two-pass sums in float32; output is rounded to nearest-even bfloat16 and
+// stored in the blocked layout the GEMMs load (kt_index).
 #include <hip/hip_runtime.h>
 
 #include "vit_internal.h"
@@ -36,11 +37,12 @@ __device__ __forceinline__ float bf16_lo(float x) {
 }
 
 // VPL = float4 chunks per lane (d <= 256 * VPL).  SPLIT: each output row is
-// [hi | lo] with hi = bf16(y) and lo = bf16(y - hi), row stride 2d.
+// [hi | lo] with hi = bf16(y) and lo = bf16(y - hi).  Input row `row` lands in blocked row
+// row / group at column offset (row % group) * S * d of a group * S * d wide matrix.
 template <int KIND, int VPL, bool SPLIT>
 __global__ void __launch_bounds__(kThreads)
 rownorm_kernel(const float* __restrict__ r, int64_t rows, int d, const float* __restrict__ g,
-               const float* __restrict__ b, float eps, uint16_t* __restrict__ out) {
+               const float* __restrict__ b, float eps, int group, uint16_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -66,8 +68,9 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, int d, const float* __
     }
   }
   const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
-  uint2* dst = reinterpret_cast<uint2*>(out + row * d * (SPLIT ? 2 : 1));
-  uint2* dst_lo = reinterpret_cast<uint2*>(out + row * d * 2 + d);
+  const int w = d * (SPLIT ? 2 : 1);
+  const int64_t orow = row / group;
+  const int ocol = (int)(row % group) * w, ocols = group * w;
   const float4* g4 = reinterpret_cast<const float4*>(g);
   const float4* b4 = reinterpret_cast<const float4*>(b);
 #pragma unroll
@@ -84,26 +87,28 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, int d, const float* __
         const float4 bb = b4[c];
         y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
       }
-      dst[c] = make_uint2(pack_bf16(y.x, y.y), pack_bf16(y.z, y.w));
+      *reinterpret_cast<uint2*>(out + kt_index(orow, ocol + 4 * c, ocols)) =
+          make_uint2(pack_bf16(y.x, y.y), pack_bf16(y.z, y.w));
       if (SPLIT)
-        dst_lo[c] = make_uint2(pack_bf16(bf16_lo(y.x), bf16_lo(y.y)), pack_bf16(bf16_lo(y.z), bf16_lo(y.w)));
+        *reinterpret_cast<uint2*>(out + kt_index(orow, ocol + d + 4 * c, ocols)) =
+            make_uint2(pack_bf16(bf16_lo(y.x), bf16_lo(y.y)), pack_bf16(bf16_lo(y.z), bf16_lo(y.w)));
     }
   }
 }
 
 template <int KIND, bool SPLIT>
 vit_status launch_kind(const float* r, int64_t rows, int d, const float* g, const float* b,
-                       float eps, uint16_t* out, hipStream_t st) {
+                       float eps, int group, uint16_t* out, hipStream_t st) {
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   const int vpl = (d / 4 + 63) / 64;
   if (vpl <= 1)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 1, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 1, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, group, out);
   else if (vpl <= 2)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 2, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 2, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, group, out);
   else if (vpl <= 5)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 5, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 5, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, group, out);
   else if (vpl <= 8)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 8, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, out);
+    hipLaunchKernelGGL((rownorm_kernel<KIND, 8, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, group, out);
   else {
     set_error("rownorm: hidden %d too wide (max 2048)", d);
     return VIT_E_ARG;
@@ -111,19 +116,56 @@ vit_status launch_kind(const float* r, int64_t rows, int d, const float* g, cons
   return VIT_OK;
 }
 
+// Debug copy: blocked bf16 -> row-major, 4 values (one 8-byte piece of a chunk) per thread.
+__global__ void __launch_bounds__(kThreads)
+unblock_kernel(const uint16_t* __restrict__ src, int64_t rows, int cols, int group, int out_cols,
+               uint16_t* __restrict__ dst) {
+  const int q4 = out_cols / 4;
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= rows * q4) return;
+  const int64_t m = j / q4;
+  const int c = (int)(j % q4) * 4;
+  const int64_t s = kt_index(m / group, (m % group) * cols + c, (int64_t)group * cols);
+  *reinterpret_cast<uint2*>(dst + m * out_cols + c) = *reinterpret_cast<const uint2*>(src + s);
+}
+
 }  // namespace
 
-vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
-                          const float* b, float eps, uint16_t* out, bool split, void* stream) {
+vit_status launch_unblock(const uint16_t* src, int64_t rows, int cols, int group, int out_cols,
+                          uint16_t* dst, void* stream) {
   if (rows <= 0) return VIT_OK;
+  if (cols % 32 || out_cols % 4 || out_cols > cols || group < 1) {
+    set_error("unblock: bad shape cols=%d out_cols=%d group=%d", cols, out_cols, group);
+    return VIT_E_ARG;
+  }
+  const int64_t blocks = (rows * (out_cols / 4) + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(unblock_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     src, rows, cols, group, out_cols, dst);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("unblock launch: %s", hipGetErrorString(e));
+    return VIT_E_HIP;
+  }
+  return VIT_OK;
+}
+
+vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
+                          const float* b, float eps, uint16_t* out, bool split, int group,
+                          void* stream) {
+  if (rows <= 0) return VIT_OK;
+  if (d % 32 || group < 1 || rows % group) {
+    set_error("rownorm: hidden %d must be a multiple of 32 and rows %lld a multiple of the group %d", d,
+              (long long)rows, group);
+    return VIT_E_ARG;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   vit_status s;
   if (kind == VIT_NORM_LAYER)
-    s = split ? launch_kind<VIT_NORM_LAYER, true>(r, rows, d, g, b, eps, out, st)
-              : launch_kind<VIT_NORM_LAYER, false>(r, rows, d, g, b, eps, out, st);
+    s = split ? launch_kind<VIT_NORM_LAYER, true>(r, rows, d, g, b, eps, group, out, st)
+              : launch_kind<VIT_NORM_LAYER, false>(r, rows, d, g, b, eps, group, out, st);
   else
-    s = split ? launch_kind<VIT_NORM_RMS, true>(r, rows, d, g, b, eps, out, st)
-              : launch_kind<VIT_NORM_RMS, false>(r, rows, d, g, b, eps, out, st);
+    s = split ? launch_kind<VIT_NORM_RMS, true>(r, rows, d, g, b, eps, group, out, st)
+              : launch_kind<VIT_NORM_RMS, false>(r, rows, d, g, b, eps, group, out, st);
   if (s != VIT_OK) return s;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -18,10 +18,11 @@
 //    adjacent lanes read adjacent bytes of one image row, all issued before
 //    the first LDS store; an image's single frame is read once and serves
 //    both temporal slots;
-//  * output: the block's 4 * kUnitsPerBlock rows of 1184 bf16 (columns
-//    1176..1183 zero, so the patch-embed GEMM needs no K tail) are one
-//    contiguous run, written as 16-byte nontemporal stores by consecutive
-//    lanes.
+//  * output: the block's 4 * kUnitsPerBlock = 32 rows of 1184 bf16 (columns
+//    1176..1183 zero, so the patch-embed GEMM needs no K tail) are two whole
+//    16-row groups of the blocked GEMM layout (kt_index), i.e. one contiguous
+//    run, written as 16-byte nontemporal stores by consecutive lanes in
+//    memory order.
 // A per-block table maps each output feature to its staged byte (offset,
 // channel, temporal slot), so a 16-byte output chunk costs one table read and
 // 8 pairs of LDS lookups instead of per-element index division.
@@ -42,6 +43,8 @@ constexpr int kUnitBytes = kTemporal * kSlotBytes;            // 4704
 constexpr int kUnitDwords = kUnitBytes / 4;                   // 1176
 constexpr int kChunksPerRow = kFeatPad / 8;                   // 148
 constexpr int kChunksPerUnit = 4 * kChunksPerRow;             // 592
+constexpr int kColBlocks = kFeatPad / 32;                     // 37 blocks of 32 features
+static_assert(4 * kUnitsPerBlock % 16 == 0, "a block's rows are whole 16-row groups");
 constexpr uint16_t kPadFeature = 0x8000;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 constexpr int kRowPieces = kRowBytes / 12;                    // 7 pieces of 12 bytes per unit row
@@ -119,11 +122,17 @@ normpatch_kernel(const uint8_t* __restrict__ pixels, const UnitDesc* __restrict_
     }
   __syncthreads();
 
+  // q walks the block's output run in memory order: 16-row group, 32-feature block, row,
+  // chunk position; the position holds feature chunk kt_chunk(row, position).
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
-  uint16_t* xb = x + u0 * 4 * kFeatPad;
-  for (int q = tid; q < nu * kChunksPerUnit; q += kThreads) {
-    const int u = q / kChunksPerUnit, rem = q - u * kChunksPerUnit;
-    const int rr = rem / kChunksPerRow, k8 = rem - rr * kChunksPerRow;   // row in unit (dh, dw), chunk
+  uint16_t* xb = x + u0 * 4 * kFeatPad;   // = first element of the block's first row group
+  for (int q = tid; q < kUnitsPerBlock * kChunksPerUnit; q += kThreads) {
+    const int grp = q / (kColBlocks * 64), rem0 = q - grp * (kColBlocks * 64);
+    const int kb = rem0 >> 6, r16 = (rem0 >> 2) & 15, pos = rem0 & 3;
+    const int br = grp * 16 + r16;   // row within the block
+    const int u = br >> 2, rr = br & 3;   // unit, row in unit (dh, dw)
+    if (u >= nu) continue;
+    const int k8 = kb * 4 + kt_chunk(u0 * 4 + br, pos);   // feature chunk
     const int shift = (rr >> 1) * (kPatch * kRowBytes) + (rr & 1) * (kPatch * 3);
     const bool image = sud[u].fstride == 0;
     const uint8_t* ub = sb + u * kUnitBytes + shift;
@@ -172,7 +181,7 @@ normpatch_kernel(const uint8_t* __restrict__ pixels, const UnitDesc* __restrict_
   }
 }
 
-// uint8 flatten_patches rows [N][1176] -> bf16 [N][1184]; 8 features per thread
+// uint8 flatten_patches rows [N][1176] -> blocked bf16 [N][1184]; 8 features per thread
 // (1176 = 147 * 8 and 392 = 49 * 8, so a chunk never straddles a channel).
 __global__ void __launch_bounds__(kThreads)
 normrows_kernel(const uint8_t* __restrict__ patches, int64_t n_rows,
@@ -194,7 +203,7 @@ normrows_kernel(const uint8_t* __restrict__ patches, int64_t n_rows,
     pk.z = b(raw.y, 0) | (b(raw.y, 1) << 16);
     pk.w = b(raw.y, 2) | (b(raw.y, 3) << 16);
   }
-  *reinterpret_cast<uint4*>(x + row * kFeatPad + 8 * k8) = pk;
+  *reinterpret_cast<uint4*>(x + kt_index(row, 8 * k8, kFeatPad)) = pk;
 }
 
 }  // namespace

@@ -196,15 +196,18 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
     off = round_up((int64_t)(off + bytes), 256);
     return o;
   };
-  p->off_x = take((size_t)N * kFeatPad * 2);
-  p->off_r = take((size_t)N * d * 4);
+  // GEMM operands (X, H, O, F) are blocked: rows padded to whole 16-row groups, for the
+  // patch rows (N) and for the merger's view of them (N / 4 rows of 4 patch rows each)
+  const int64_t Np = round_up(N, 16), Up = round_up(N / 4, 16);
   const int64_t S = p->split;
-  p->off_h = take((size_t)N * S * d * 2);
+  p->off_x = take((size_t)Np * kFeatPad * 2);
+  p->off_r = take((size_t)N * d * 4);
+  p->off_h = take((size_t)std::max(Np * S * d, Up * 4 * S * d) * 2);
   p->off_q = take((size_t)N * d * 2);
   p->off_k = take((size_t)N * d * 2);
   p->off_vt = take((size_t)N * d * 2);
-  p->off_o = take((size_t)N * d * 2);
-  p->off_f = take((size_t)N * S * std::max<int64_t>(p->mlp_pad, d) * 2);
+  p->off_o = take((size_t)Np * d * 2);
+  p->off_f = take((size_t)std::max(Np * S * p->mlp_pad, Up * 4 * S * d) * 2);
   p->off_pix = take(px);
   p->off_out = take((size_t)p->n_units * c.out_dim * 4);
   p->ws_bytes = off;

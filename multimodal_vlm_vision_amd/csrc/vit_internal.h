@@ -27,6 +27,21 @@ constexpr int kUnitPx = kMerge * kPatch;                  // 28-pixel side of a 
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// ---------------------------------------------------------------- GEMM operand layout
+
+// Every bf16 matrix that feeds a GEMM (weights, normalised patches, norm outputs,
+// attention output, MLP activations) is stored in 1 KB blocks of 16 rows x 32 columns:
+// blocks ordered by row group, then by column block; inside a block row r takes 64 bytes,
+// its four 16-byte chunks permuted by kt_chunk.  A 64-lane 16-byte load then moves one
+// whole block (eight full 128-byte lines instead of sixteen half lines), and the block
+// lands in LDS already in the bank-conflict-free order the MFMA fragment reads need.
+// Rows are padded to a multiple of 16, columns must be a multiple of 32.
+constexpr int kt_chunk(int64_t r, int q) { return q ^ (int)(((r >> 1) ^ (r >> 3)) & 3); }
+constexpr int64_t kt_index(int64_t r, int64_t c, int64_t cols) {
+  return ((((r >> 4) * (cols >> 5) + (c >> 5)) << 9) | ((r & 15) << 5) |
+          ((int64_t)kt_chunk(r, (int)((c >> 3) & 3)) << 3) | (c & 7));
+}
+
 // bfloat16 round-to-nearest-even of a float, as raw bits (host side).
 uint16_t f32_to_bf16_bits(float f);
 
@@ -166,15 +181,15 @@ enum GemmEpi : int {
 };
 
 struct GemmArgs {
-  const uint16_t* A = nullptr; int64_t lda = 0;   // [M][K] bf16 (split: [M][2K], see a_group)
-  const uint16_t* B = nullptr; int64_t ldb = 0;   // [N][K] bf16
+  const uint16_t* A = nullptr; int64_t lda = 0;   // blocked (kt_index) [M][lda] bf16, lda >= K (2K split)
+  const uint16_t* B = nullptr; int64_t ldb = 0;   // blocked [N][ldb] bf16, ldb >= K
   int M = 0, N = 0, K = 0;                        // K = logical reduction length
   // Split activations: when a_group > 0, each A row holds hi/lo pairs in groups of a_group
   // columns, [hi(g) | lo(g)] repeated, and the product is sum_k (hi + lo)[k] * B[n][k].
   int a_group = 0;
   uint32_t a_bytes = 0, b_bytes = 0;              // operand extents (set by launch_gemm)
   const float* bias = nullptr;
-  void* out = nullptr; int64_t ldo = 0;
+  void* out = nullptr; int64_t ldo = 0;           // fp32 row-major, or blocked bf16 (GELU / SwiGLU)
   // QKV epilogue
   uint16_t* q = nullptr; uint16_t* k = nullptr; uint16_t* vt = nullptr;
   int64_t n_tok = 0;
@@ -196,9 +211,17 @@ vit_status launch_normpatch(const uint8_t* pixels, const UnitDesc* units, int64_
                             const uint16_t* lut, const NormAffine* affine, uint16_t* x, void* stream);
 vit_status launch_normrows_u8(const uint8_t* patches, int64_t n_rows, const uint16_t* lut,
                               uint16_t* x, void* stream);
-// Row norm of fp32 rows [rows][d] into bf16; split: output rows [hi(d) | lo(d)] (stride 2d).
+// Row norm of fp32 rows [rows][d] into bf16 in the blocked GEMM layout; split: each row is
+// [hi(d) | lo(d)].  group > 1 stores `group` consecutive rows as one row of group * S * d
+// columns (the merger's view of 2x2 patch blocks).
 vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
-                          const float* b, float eps, uint16_t* out, bool split, void* stream);
+                          const float* b, float eps, uint16_t* out, bool split, int group,
+                          void* stream);
+// Blocked bf16 matrix -> row-major [rows][out_cols] (debug copies): row m of the result is
+// row m / group, columns (m % group) * cols + [0, out_cols) of a blocked matrix with
+// group * cols columns.
+vit_status launch_unblock(const uint16_t* src, int64_t rows, int cols, int group, int out_cols,
+                          uint16_t* dst, void* stream);
 
 struct AttnArgs {
   const uint16_t* q = nullptr; const uint16_t* k = nullptr; const uint16_t* vt = nullptr;

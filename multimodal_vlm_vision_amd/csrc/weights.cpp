@@ -101,13 +101,15 @@ struct Packer {
     blob.resize(off + bytes);
     return off;
   }
-  // rows x cols bf16 matrix; element (r, c) = src(r, c) via a callback (0 outside)
+  // rows x cols bf16 GEMM operand in the blocked layout (kt_index); element (r, c) = src(r, c)
+  // via a callback.  Every packed matrix has rows a multiple of 64 and cols of 32 (checked by
+  // the configuration and the padding of the K dimensions).
   template <class F>
   size_t mat(int64_t rows, int64_t cols, F src) {
     size_t off = reserve((size_t)rows * cols * 2);
     uint16_t* d = reinterpret_cast<uint16_t*>(blob.data() + off);
     for (int64_t r = 0; r < rows; ++r)
-      for (int64_t c = 0; c < cols; ++c) d[r * cols + c] = f32_to_bf16_bits(src(r, c));
+      for (int64_t c = 0; c < cols; ++c) d[kt_index(r, c, cols)] = f32_to_bf16_bits(src(r, c));
     return off;
   }
   template <class F>

@@ -102,17 +102,21 @@ __device__ __forceinline__ float4 f4add(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-// bf16 activation store into the blocked layout (ldo columns): hi = bf16(y) at column n; with
-// split_off, lo = bf16(y - hi) at n + split_off.  n % 4 == 0, so the 4 values share one chunk.
-__device__ __forceinline__ void store_act(const GemmArgs& p, int m, int n, float4 y) {
+// bf16 activation store into the blocked layout (ldo columns): hi = bf16(y) of the 8 columns
+// n..n+7 (one 16-byte chunk, n % 8 == 0); with split_off, lo = bf16(y - hi) at n + split_off.
+__device__ __forceinline__ void store_act8(const GemmArgs& p, int m, int n, const float (&y)[8]) {
   uint16_t* o = static_cast<uint16_t*>(p.out);
-  const uint2 hi = pack4(y);
-  *reinterpret_cast<uint2*>(o + kt_index(m, n, p.ldo)) = hi;
+  uint32_t hi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi[i] = pack2(y[2 * i], y[2 * i + 1]);
+  *reinterpret_cast<uint4*>(o + kt_index(m, n, p.ldo)) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
   if (p.split_off) {
-    const float4 h = make_float4(__builtin_bit_cast(float, hi.x << 16), __builtin_bit_cast(float, hi.x & 0xffff0000u),
-                                 __builtin_bit_cast(float, hi.y << 16), __builtin_bit_cast(float, hi.y & 0xffff0000u));
-    *reinterpret_cast<uint2*>(o + kt_index(m, n + p.split_off, p.ldo)) =
-        pack4(make_float4(y.x - h.x, y.y - h.y, y.z - h.z, y.w - h.w));
+    uint32_t lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lo[i] = pack2(y[2 * i] - __builtin_bit_cast(float, hi[i] << 16),
+                    y[2 * i + 1] - __builtin_bit_cast(float, hi[i] & 0xffff0000u));
+    *reinterpret_cast<uint4*>(o + kt_index(m, n + p.split_off, p.ldo)) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
 }
 
@@ -149,7 +153,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
                                                int lane) {
   constexpr int SST = W + 8;
   constexpr int C4 = W / 4;   // float4 chunks per row
-  if (EPI == EPI_F32 || EPI == EPI_RES || EPI == EPI_GELU || EPI == EPI_OUT) {
+  if (EPI == EPI_F32 || EPI == EPI_RES || EPI == EPI_OUT) {
 #pragma unroll
     for (int q = 0; q < 32 * C4 / 64; ++q) {
       const int id = lane + 64 * q, r = id / C4, c4 = id % C4;
@@ -163,15 +167,52 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
         if (EPI == EPI_RES) {
           float4* o = reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)m * p.ldo + n);
           *o = f4add(*o, f4add(v, b));
-        } else if (EPI == EPI_OUT) {
+        } else {
           *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)p.row_map[m] * p.ldo + n) = f4add(v, b);
-        } else {   // GELU -> bf16 (hi, and lo when split)
-          const float4 x = f4add(v, b);
-          store_act(p, m, n, make_float4(gelu(x.x), gelu(x.y), gelu(x.z), gelu(x.w)));
         }
       }
     }
-  } else if (EPI == EPI_SWIGLU || (EPI == EPI_QKV && n_base < 2 * p.hidden)) {
+  } else if (EPI == EPI_GELU || EPI == EPI_SWIGLU) {
+    // bf16 activations into the blocked layout: a lane produces one 16-byte chunk (8 columns)
+    // of hi (and one of lo), so the 64 lanes of a store write one whole 1 KB block.  The lane's
+    // chunk position in the block is q; it holds logical chunk kt_chunk(row, q).
+    constexpr int OW = EPI == EPI_SWIGLU ? W / 2 : W;   // output columns of the slice
+    constexpr int OB = OW / 32;                          // output column blocks
+    const int r16 = lane >> 2, q = lane & 3;
+#pragma unroll
+    for (int blk = 0; blk < 2 * OB; ++blk) {
+      const int rg = blk / OB, ob = blk % OB;
+      const int r = 16 * rg + r16, m = m_base + r;
+      if (m >= p.M) continue;
+      const int c = kt_chunk(m, q);
+      float y[8];
+      int oc;
+      if (EPI == EPI_GELU) {
+        const int cl = 32 * ob + 8 * c;
+        oc = n_base + cl;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float4 x = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 4 * h),
+                                 *reinterpret_cast<const float4*>(p.bias + oc + 4 * h));
+          y[4 * h] = gelu(x.x); y[4 * h + 1] = gelu(x.y); y[4 * h + 2] = gelu(x.z); y[4 * h + 3] = gelu(x.w);
+        }
+      } else {
+        // gate columns cl.., up columns cl + 32.. of the slice's 64-column block ob
+        const int cl = 64 * ob + 8 * c;
+        oc = n_base / 2 + 32 * ob + 8 * c;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float4 g = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 4 * h),
+                                 *reinterpret_cast<const float4*>(p.bias + n_base + cl + 4 * h));
+          const float4 u = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 32 + 4 * h),
+                                 *reinterpret_cast<const float4*>(p.bias + n_base + cl + 32 + 4 * h));
+          y[4 * h] = silu(g.x) * u.x; y[4 * h + 1] = silu(g.y) * u.y;
+          y[4 * h + 2] = silu(g.z) * u.z; y[4 * h + 3] = silu(g.w) * u.w;
+        }
+      }
+      store_act8(p, m, oc, y);
+    }
+  } else if (EPI == EPI_QKV && n_base < 2 * p.hidden) {
     // pairs: columns c (c % 64 < 32) and c + 32 of each 64-column block
     constexpr int G4 = W / 8;   // first-member float4 chunks per row
 #pragma unroll
@@ -184,11 +225,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
                              *reinterpret_cast<const float4*>(p.bias + n));
       const float4 b = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 32),
                              *reinterpret_cast<const float4*>(p.bias + n + 32));
-      if (EPI == EPI_SWIGLU) {
-        const int oc = (n - (n & 63)) / 2 + (n & 31);
-        const float4 y = make_float4(silu(a.x) * b.x, silu(a.y) * b.y, silu(a.z) * b.z, silu(a.w) * b.w);
-        store_act(p, m, oc, y);
-      } else {
+      {
         // RoPE on 4 consecutive rotary pairs of one head (head_dim/2 is a multiple of 4)
         const int d = p.hidden, hd = p.head_dim, rr = hd / 2, nf = p.nfreq;
         const int part = n / d, jj = n - part * d;
@@ -412,7 +449,7 @@ struct CfgInfo {
   double eff;   // relative efficiency (larger wave tiles read less LDS per MFMA)
 };
 // (efficiencies fitted to measured times of the tower's products on MI355X)
-constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 128, 1, 1.0},
+constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 128, 1, 1.0},   // (order used by pick_cfg)
                              {CFG_T, 192, 256, 128, 1, 0.98},
                              {CFG_H, 128, 256, 128, 1, 0.9},
                              {CFG_O, 128, 256, 128, 2, 1.1},
@@ -456,13 +493,29 @@ hipError_t run_cfg(int cfg, const GemmArgs& a, hipStream_t st) {
 }
 
 // Estimated time ~ rounds of (256 * occupancy) workgroups x per-CU area of a round / efficiency.
+static_assert(kCfgs[1].cfg == CFG_T && kCfgs[3].cfg == CFG_O, "pick_cfg indexes the table");
+
 int pick_cfg(int epi, const GemmArgs& a) {
+  auto fits = [&](const CfgInfo& c) {
+    return a.N % c.bn == 0 && !(epi == EPI_QKV && a.hidden % c.wave_n);   // QKV: a wave's columns stay in one of q / k / v
+  };
+  auto tiles_of = [&](const CfgInfo& c) { return (double)((a.M + c.bm - 1) / c.bm) * (a.N / c.bn); };
+  // Measured on the tower's products with blocked operands: two workgroups per CU win as
+  // soon as every CU gets a tile (each hides the other's epilogue and barriers), except for
+  // long reductions where the 192x256 tile already fills >= 85% of its last round.
+  const CfgInfo& o = kCfgs[3];
+  const CfgInfo& t = kCfgs[1];
+  if (fits(o) && tiles_of(o) >= 256.0) {
+    const int k_eff = a.K * (a.a_group > 0 ? 2 : 1);
+    const double t_fill = tiles_of(t) / (256.0 * std::ceil(tiles_of(t) / 256.0));
+    if (k_eff >= 8192 && fits(t) && t_fill >= 0.85) return t.cfg;
+    return o.cfg;
+  }
   int best = -1;
   double best_t = 1e300;
   for (const CfgInfo& c : kCfgs) {
-    if (a.N % c.bn) continue;
-    if (epi == EPI_QKV && (a.hidden % c.wave_n)) continue;   // a wave's columns stay in one of q / k / v
-    const double tiles = (double)((a.M + c.bm - 1) / c.bm) * (a.N / c.bn);
+    if (!fits(c)) continue;
+    const double tiles = tiles_of(c);
     const double rounds = std::ceil(tiles / (256.0 * c.occ));
     // co-resident workgroups only hide each other's epilogues once they are staggered,
     // i.e. from the second round on; a single round runs like one workgroup per CU

@@ -175,6 +175,8 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   uint16_t* O = reinterpret_cast<uint16_t*>(ws + pl->off_o);
   uint16_t* F = reinterpret_cast<uint16_t*>(ws + pl->off_f);
 
+  if (pl->vt_ld > N) VIT_TRY(launch_vt_pad_zero(VT, d, N, pl->vt_ld, st));
+
   // 1. rescale + normalise + patchify: every needed pixel byte read once, 1176 bf16 written per row
   const double np_bytes = (double)pl->pixel_read_bytes + Nd * kFeat * 2;
   if (pixels)
@@ -201,18 +203,23 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     GemmArgs q;
     q.A = H; q.lda = S * d; q.B = L.qkv_w; q.ldb = d; q.a_group = split ? d : 0;
     q.M = (int)N; q.N = 3 * d; q.K = d; q.bias = L.qkv_b;
-    q.q = Q; q.k = K; q.vt = VT; q.n_tok = N;
+    q.q = Q; q.k = K; q.vt = VT; q.n_tok = N; q.vt_ld = pl->vt_ld;
     q.row_pos = rowpos; q.cos_tab = cos_t; q.sin_tab = sin_t;
     q.nfreq = pl->nfreq; q.head_dim = hd; q.hidden = d;
     LAUNCH("gemm_qkv_rope", 2.0 * Nd * 3 * dd * dd, 0, true, launch_gemm(EPI_QKV, q, st));
     if (stop.hit(l, 2)) return copy_out(stop, Q, (size_t)N * d * 2, st);
     if (stop.hit(l, 3)) return copy_out(stop, K, (size_t)N * d * 2, st);
-    if (stop.hit(l, 4)) return copy_out(stop, VT, (size_t)N * d * 2, st);
+    if (stop.hit(l, 4)) {
+      if (stop.dst_bytes < (size_t)N * d * 2) return copy_out(stop, VT, (size_t)N * d * 2, st);
+      HIP_TRY(hipMemcpy2DAsync(stop.dst, N * 2, VT, pl->vt_ld * 2, N * 2, d, hipMemcpyDeviceToDevice, st));
+      return VIT_OK;
+    }
 
     const bool windowed = c.window_px > 0 && !ctx->is_full_layer(l);
     const AttnLists& lists = windowed ? pl->win : pl->full;
     AttnArgs at;
-    at.q = Q; at.k = K; at.vt = VT; at.o = O; at.n_tok = N; at.heads = c.heads; at.head_dim = hd;
+    at.q = Q; at.k = K; at.vt = VT; at.o = O; at.n_tok = N; at.vt_ld = pl->vt_ld;
+    at.heads = c.heads; at.head_dim = hd;
     at.work_long = reinterpret_cast<const AttnWork*>(ws + lists.off_long);
     at.work_short = reinterpret_cast<const AttnWork*>(ws + lists.off_short);
     if (lists.n_long > 0) {

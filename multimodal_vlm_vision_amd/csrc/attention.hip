@@ -29,8 +29,10 @@
 //
 // K tiles (32 keys x head_dim, row stride head_dim + 8 so 16-byte fragment
 // reads of 16 consecutive rows hit distinct banks) and V^T tiles (head_dim
-// rows x 32 keys, row stride 36) move global -> LDS with gfx950's buffer loads
-// into LDS, into a double-buffered ring.  Work units are laid out so each XCD
+// rows x the 40 keys from the 8-aligned token at or below the block's first
+// key, so every load is a whole 16-byte chunk of a 16-byte aligned V^T row)
+// move global -> LDS with gfx950's 16-byte buffer loads into LDS, into a
+// double-buffered ring.  Work units are laid out so each XCD
 // (workgroups are dispatched round-robin over 8 XCDs) runs contiguous
 // (head, segment) ranges and shares their K/V in its L2.  Long segments use
 // 4-wave workgroups (256 queries share each K/V tile); short segments
@@ -88,10 +90,14 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
   constexpr int KS = HD + 8;                 // K tile row stride (elements)
   constexpr int KCH = KS / 8;                // 16-byte chunks per K row (the last is padding)
   constexpr int KLOADS = (KB * KCH + 63) / 64;      // 1 KB direct loads per K tile
-  constexpr int VS = KB + 4;                 // V^T tile row stride (elements)
-  constexpr int VDW = VS / 2;                // dwords per V^T row
+  // V^T tile: each row holds the 40 keys from the 8-aligned token at or below the block's first
+  // key (16-byte loads need 16-byte aligned rows; segments start at multiples of 4 tokens), so
+  // the block's keys sit at DELTA = seg_start % 8 within the row.
+  constexpr int VP = KB + 8;                 // keys per V^T tile row (80 bytes, 5 chunks)
+  constexpr int VCH = VP / 8;                // 16-byte chunks per V^T row
+  constexpr int VDW = VP / 2;                // dwords per V^T row
   constexpr int VROWS = DT * 32;             // rows HD.. are constant (ones, then zeros)
-  constexpr int VLOADS = (HD * VDW + 63) / 64;      // 256 B direct loads per V^T tile
+  constexpr int VLOADS = (HD * VCH + 63) / 64;      // 1 KB direct loads per V^T tile
   constexpr int LROW = HD - 32 * (DT - 1);   // row of the sums inside the last O^T tile
   constexpr int LIDX = 4 * (LROW / 8) + (LROW % 4), LHALF = (LROW % 8) / 4;
   static_assert(HD % 16 == 0 && KCH % 2 == 1, "head_dim must be a multiple of 16");
@@ -117,7 +123,8 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
   const int qbase = wk.q0 + wv * 64;
   const uint16_t* Qh = a.q + (int64_t)head * a.n_tok * HD;
   const uint16_t* Kh = a.k + (int64_t)head * a.n_tok * HD;
-  const uint16_t* Vh = a.vt + (int64_t)head * HD * a.n_tok;
+  const uint16_t* Vh = a.vt + (int64_t)head * HD * a.vt_ld;
+  const int delta = seg0 & 7;
 
   // constant V^T rows: HD = ones (softmax denominator), the rest zeros; never overwritten
   for (int i = tid; i < (VROWS - HD) * VDW; i += NW * 64) {
@@ -161,7 +168,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
   const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kh), (short)0,
                                                     (int)(a.n_tok * HD * 2), kRsrcWord3);
   const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vh), (short)0,
-                                                    (int)(a.n_tok * HD * 2), kRsrcWord3);
+                                                    (int)(a.vt_ld * HD * 2), kRsrcWord3);
   // (fixed-size arrays: a dependent bound here fails the host-side instantiation with this
   // clang; only the first KLW / VLW entries are used)
   static_assert(KLW <= 8 && VLW <= 24, "load plan");
@@ -173,8 +180,8 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
   }
 #pragma unroll
   for (int j = 0; j < VLW; ++j) {
-    const int id = (wv + j * NW) * 64 + lane, dd = id / VDW, c = id % VDW;
-    voff[j] = dd < HD ? (uint32_t)(dd * a.n_tok + (c < KB / 2 ? 2 * c : 0)) * 2 : 0u;
+    const int id = (wv + j * NW) * 64 + lane, dd = id / VCH, c = id % VCH;
+    voff[j] = dd < HD ? (uint32_t)(dd * a.vt_ld + 8 * c) * 2 : 0u;
   }
   auto dload = [&](int kb, uint16_t* dK, uint32_t* dV) {
     const uint32_t key0 = (uint32_t)(seg0 + kb * KB);
@@ -189,9 +196,9 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
     for (int j = 0; j < VLW; ++j) {
       const int i = wv + j * NW;
       if (i >= VLOADS) break;
-      if ((i * 64 + lane) / VDW < HD)   // lanes past the real rows must not touch the constant rows
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dV + i * 64), 4,
-                                                 voff[j], key0 * 2, 0, 0);
+      if (i * 64 + lane < HD * VCH)   // lanes past the real rows must not touch the constant rows
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dV + i * 64 * 4), 16,
+                                                 voff[j], (key0 - delta) * 2, 0, 0);
     }
   };
 
@@ -256,7 +263,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
       //      16c + 4h + 0..3, 16c + 8 + 4h + 0..3 (the order of the lane's probabilities)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vr = Vt + (32 * dt + l32) * VS + 4 * h;
+        const uint16_t* vr = Vt + (32 * dt + l32) * VP + delta + 4 * h;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + 16 * c);
@@ -316,11 +323,36 @@ hipError_t run_hd(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+__global__ void vt_pad_zero_kernel(uint16_t* vt, int rows, int64_t n_tok, int64_t vt_ld) {
+  const int pad = (int)(vt_ld - n_tok);
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)rows * pad) return;
+  vt[(i / pad) * vt_ld + n_tok + i % pad] = 0;
+}
+
 }  // namespace
+
+vit_status launch_vt_pad_zero(uint16_t* vt, int rows, int64_t n_tok, int64_t vt_ld, void* stream) {
+  if (vt_ld <= n_tok || rows <= 0) return VIT_OK;
+  const int64_t n = (int64_t)rows * (vt_ld - n_tok);
+  hipLaunchKernelGGL(vt_pad_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), vt, rows, n_tok, vt_ld);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("V^T pad clear: %s", hipGetErrorString(e));
+    return VIT_E_HIP;
+  }
+  return VIT_OK;
+}
 
 vit_status launch_attention(const AttnArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (a.n_tok * a.head_dim * 2 >= ((int64_t)1 << 31)) {
+  if (a.vt_ld < a.n_tok || a.vt_ld % 8) {
+    set_error("attention: V^T pitch %lld must be a multiple of 8 and cover %lld tokens", (long long)a.vt_ld,
+              (long long)a.n_tok);
+    return VIT_E_ARG;
+  }
+  if (a.vt_ld * a.head_dim * 2 >= ((int64_t)1 << 31)) {
     set_error("attention: %lld tokens exceed the 2 GiB per-head operand limit", (long long)a.n_tok);
     return VIT_E_ARG;
   }

@@ -257,7 +257,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
       const float4 v = make_float4(sc[(4 * rg + 0) * SST + c] + b, sc[(4 * rg + 1) * SST + c] + b,
                                    sc[(4 * rg + 2) * SST + c] + b, sc[(4 * rg + 3) * SST + c] + b);
       const int nn = n - 2 * d, head = nn / hd, dd = nn % hd;
-      *reinterpret_cast<uint2*>(p.vt + ((int64_t)head * hd + dd) * p.n_tok + m) = pack4(v);
+      *reinterpret_cast<uint2*>(p.vt + ((int64_t)head * hd + dd) * p.vt_ld + m) = pack4(v);
     }
   }
 }

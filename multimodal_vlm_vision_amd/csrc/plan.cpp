@@ -205,7 +205,8 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   p->off_h = take((size_t)std::max(Np * S * d, Up * 4 * S * d) * 2);
   p->off_q = take((size_t)N * d * 2);
   p->off_k = take((size_t)N * d * 2);
-  p->off_vt = take((size_t)N * d * 2);
+  p->vt_ld = round_up(N, 8);   // 16-byte aligned V^T rows for the attention's tile loads
+  p->off_vt = take((size_t)p->vt_ld * d * 2);
   p->off_o = take((size_t)Np * d * 2);
   p->off_f = take((size_t)std::max(Np * S * p->mlp_pad, Up * 4 * S * d) * 2);
   p->off_pix = take(px);

@@ -148,6 +148,7 @@ struct vit_plan {
   // workspace layout (byte offsets; all 256-byte aligned)
   size_t off_x = 0, off_r = 0, off_h = 0, off_q = 0, off_k = 0, off_vt = 0, off_o = 0, off_f = 0;
   size_t off_pix = 0, off_out = 0, ws_bytes = 0;
+  int64_t vt_ld = 0;              // V^T row pitch (tokens), N rounded up to 8
 };
 
 struct vit_graph {
@@ -193,6 +194,7 @@ struct GemmArgs {
   // QKV epilogue
   uint16_t* q = nullptr; uint16_t* k = nullptr; uint16_t* vt = nullptr;
   int64_t n_tok = 0;
+  int64_t vt_ld = 0;   // V^T row pitch in tokens (a multiple of 8)
   const int32_t* row_pos = nullptr;
   const float* cos_tab = nullptr; const float* sin_tab = nullptr;
   int nfreq = 0, head_dim = 0, hidden = 0;
@@ -227,10 +229,15 @@ struct AttnArgs {
   const uint16_t* q = nullptr; const uint16_t* k = nullptr; const uint16_t* vt = nullptr;
   uint16_t* o = nullptr;
   int64_t n_tok = 0;
+  int64_t vt_ld = 0;   // V^T row pitch in tokens: a multiple of 8, pad columns finite (zero)
   int heads = 0, head_dim = 0;
   const AttnWork* work_long = nullptr; int n_long = 0;
   const AttnWork* work_short = nullptr; int n_short = 0;
 };
 vit_status launch_attention(const AttnArgs& a, void* stream);
+// Zeroes the pad columns [n_tok, vt_ld) of the rows V^T rows (attention reads whole 16-byte
+// chunks, so keys past a segment may come from the pad; they get probability 0, and must not
+// be NaN).
+vit_status launch_vt_pad_zero(uint16_t* vt, int rows, int64_t n_tok, int64_t vt_ld, void* stream);
 
 }  // namespace vitmi

@@ -213,51 +213,69 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
       store_act8(p, m, oc, y);
     }
   } else if (EPI == EPI_QKV && n_base < 2 * p.hidden) {
-    // pairs: columns c (c % 64 < 32) and c + 32 of each 64-column block
-    constexpr int G4 = W / 8;   // first-member float4 chunks per row
+    // pairs: columns c (c % 64 < 32) and c + 32 of each 64-column block.  A lane rotates 8
+    // consecutive rotary pairs of one head (head_dim/2 is a multiple of 8 and the frequency
+    // count per axis, head_dim/4, a multiple of 4, so each group of 4 has one axis) and writes
+    // each member half as one 16-byte store.
+    constexpr int G8 = W / 16;   // first-member groups of 8 per row
+    const int d = p.hidden, hd = p.head_dim, rr = hd / 2, nf = p.nfreq;
 #pragma unroll
-    for (int q = 0; q < 32 * G4 / 64; ++q) {
-      const int id = lane + 64 * q, r = id / G4, g = id % G4;
-      const int cl = (g / 8) * 64 + (g % 8) * 4;          // local column of the first member
+    for (int q = 0; q < 32 * G8 / 64; ++q) {
+      const int id = lane + 64 * q, r = id / G8, g = id % G8;
+      const int cl = (g / 4) * 64 + (g % 4) * 8;          // local column of the first member
       const int m = m_base + r, n = n_base + cl;
       if (m >= p.M) continue;
-      const float4 a = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl),
-                             *reinterpret_cast<const float4*>(p.bias + n));
-      const float4 b = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 32),
-                             *reinterpret_cast<const float4*>(p.bias + n + 32));
-      {
-        // RoPE on 4 consecutive rotary pairs of one head (head_dim/2 is a multiple of 4)
-        const int d = p.hidden, hd = p.head_dim, rr = hd / 2, nf = p.nfreq;
-        const int part = n / d, jj = n - part * d;
-        const int pair = 32 * (jj / 64) + (jj % 64);
-        const int head = pair / rr, kk = pair % rr;
-        const int pos = p.row_pos[m];
-        const int ax = kk < nf ? (pos >> 16) : (pos & 0xffff);
-        const int fi = kk < nf ? kk : kk - nf;
+      const int part = n / d, jj = n - part * d;
+      const int pair = 32 * (jj / 64) + (jj % 64);
+      const int head = pair / rr, kk = pair % rr;
+      const int pos = p.row_pos[m];
+      uint32_t w1[4], w2[4];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const float4 a = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 4 * hf),
+                               *reinterpret_cast<const float4*>(p.bias + n + 4 * hf));
+        const float4 b = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 32 + 4 * hf),
+                               *reinterpret_cast<const float4*>(p.bias + n + 32 + 4 * hf));
+        const int k4 = kk + 4 * hf;
+        const int ax = k4 < nf ? (pos >> 16) : (pos & 0xffff);
+        const int fi = k4 < nf ? k4 : k4 - nf;
         const float4 cs = *reinterpret_cast<const float4*>(p.cos_tab + ax * nf + fi);
         const float4 sn = *reinterpret_cast<const float4*>(p.sin_tab + ax * nf + fi);
-        const float4 y1 = make_float4(a.x * cs.x - b.x * sn.x, a.y * cs.y - b.y * sn.y,
-                                      a.z * cs.z - b.z * sn.z, a.w * cs.w - b.w * sn.w);
-        const float4 y2 = make_float4(b.x * cs.x + a.x * sn.x, b.y * cs.y + a.y * sn.y,
-                                      b.z * cs.z + a.z * sn.z, b.w * cs.w + a.w * sn.w);
-        uint16_t* o = (part == 0 ? p.q : p.k) + ((int64_t)head * p.n_tok + m) * hd;
-        *reinterpret_cast<uint2*>(o + kk) = pack4(y1);
-        *reinterpret_cast<uint2*>(o + kk + rr) = pack4(y2);
+        const uint2 u1 = pack4(make_float4(a.x * cs.x - b.x * sn.x, a.y * cs.y - b.y * sn.y,
+                                           a.z * cs.z - b.z * sn.z, a.w * cs.w - b.w * sn.w));
+        const uint2 u2 = pack4(make_float4(b.x * cs.x + a.x * sn.x, b.y * cs.y + a.y * sn.y,
+                                           b.z * cs.z + a.z * sn.z, b.w * cs.w + a.w * sn.w));
+        w1[2 * hf] = u1.x; w1[2 * hf + 1] = u1.y;
+        w2[2 * hf] = u2.x; w2[2 * hf + 1] = u2.y;
       }
+      uint16_t* o = (part == 0 ? p.q : p.k) + ((int64_t)head * p.n_tok + m) * hd;
+      *reinterpret_cast<uint4*>(o + kk) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+      *reinterpret_cast<uint4*>(o + kk + rr) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
     }
   } else if (EPI == EPI_QKV) {
-    // V part: transposed store [head][dim][token]; each item is 4 consecutive rows of one column
+    // V part: transposed store [head][dim][token]; an item is 8 consecutive rows of one column,
+    // one 16-byte store (the V^T pitch is a multiple of 8).  A last group with only 4 valid
+    // rows (row counts are multiples of 4) stores those 4: the pad columns must stay zero.
     const int d = p.hidden, hd = p.head_dim;
 #pragma unroll
-    for (int q = 0; q < 8 * W / 64; ++q) {
-      const int id = lane + 64 * q, rg = id % 8, c = id / 8;
-      const int m = m_base + 4 * rg, n = n_base + c;
+    for (int q = 0; q < 4 * W / 64; ++q) {
+      const int id = lane + 64 * q, rg = id % 4, c = id / 4;
+      const int m = m_base + 8 * rg, n = n_base + c;
       if (m >= p.M) continue;
       const float b = p.bias[n];
-      const float4 v = make_float4(sc[(4 * rg + 0) * SST + c] + b, sc[(4 * rg + 1) * SST + c] + b,
-                                   sc[(4 * rg + 2) * SST + c] + b, sc[(4 * rg + 3) * SST + c] + b);
+      const float4 v0 = make_float4(sc[(8 * rg + 0) * SST + c] + b, sc[(8 * rg + 1) * SST + c] + b,
+                                    sc[(8 * rg + 2) * SST + c] + b, sc[(8 * rg + 3) * SST + c] + b);
+      const float4 v1 = make_float4(sc[(8 * rg + 4) * SST + c] + b, sc[(8 * rg + 5) * SST + c] + b,
+                                    sc[(8 * rg + 6) * SST + c] + b, sc[(8 * rg + 7) * SST + c] + b);
       const int nn = n - 2 * d, head = nn / hd, dd = nn % hd;
-      *reinterpret_cast<uint2*>(p.vt + ((int64_t)head * hd + dd) * p.vt_ld + m) = pack4(v);
+      uint16_t* o = p.vt + ((int64_t)head * hd + dd) * p.vt_ld + m;
+      const uint2 u0 = pack4(v0);
+      if (m + 8 <= p.M) {
+        const uint2 u1 = pack4(v1);
+        *reinterpret_cast<uint4*>(o) = make_uint4(u0.x, u0.y, u1.x, u1.y);
+      } else {
+        *reinterpret_cast<uint2*>(o) = u0;
+      }
     }
   }
 }

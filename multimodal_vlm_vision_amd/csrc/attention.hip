@@ -25,7 +25,9 @@
 // Online softmax in fp32 with exp2 and the 1/sqrt(d) scale folded into one
 // FMA; P is rounded to bf16 for the MFMA.  The running max is only raised (and
 // O rescaled) when a block's max exceeds it by more than 2^8, which keeps the
-// rescale off the common path without changing the math.
+// rescale off the common path without changing the math.  The two MFMA groups of
+// a block run at raised wave priority (s_setprio): a co-resident wave in its
+// softmax then fills the matrix pipe's gaps instead of delaying it.
 //
 // K tiles (32 keys x head_dim, row stride head_dim + 8 so 16-byte fragment
 // reads of 16 consecutive rows hit distinct banks) and V^T tiles (head_dim
@@ -215,12 +217,14 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) S[t][e] = 0.f;
       const uint16_t* kr = Kt + l32 * KS + 8 * h;
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * c);
 #pragma unroll
         for (int t = 0; t < QT; ++t) S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][c], S[t], 0, 0, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // ---- mask keys past the segment end (last step only); lane's keys are 8g + 4h + e
       const int key_base = kb * KB;
       if (key_base + KB > n) {
@@ -261,6 +265,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
       }
       // ---- O^T += V^T P^T over the 32 keys; V^T fragment of chunk c lists keys
       //      16c + 4h + 0..3, 16c + 8 + 4h + 0..3 (the order of the lane's probabilities)
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const uint16_t* vr = Vt + (32 * dt + l32) * VP + delta + 4 * h;
@@ -273,6 +278,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
           for (int t = 0; t < QT; ++t) O[t][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][c], O[t][dt], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
   };

@@ -211,7 +211,9 @@ vit_status vit_encode_profiled(const vit_ctx* ctx, const vit_plan* plan, const u
  *   layer = -1: step 0 normalised patches bf16 [N][1176];
  *               step 1 patch embedding f32 [N][hidden]
  *   0 <= layer < layers:
- *               1 norm1 bf16 [N][S*hidden]; 2 q bf16 [heads][N][head_dim];
+ *               1 norm1 bf16 [N][S*hidden];
+ *               2 q after RoPE, times log2(e)/sqrt(head_dim) (the scale the attention
+ *                 kernel expects, applied before rounding), bf16 [heads][N][head_dim];
  *               3 k bf16 [heads][N][head_dim]; 4 v bf16 [heads][head_dim][N];
  *               5 attention bf16 [N][hidden]; 6 residual after out-proj f32 [N][hidden];
  *               7 norm2 bf16 [N][S*hidden]; 8 MLP activation bf16 [N][S*mlp_pad];

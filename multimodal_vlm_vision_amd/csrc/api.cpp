@@ -206,6 +206,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     q.q = Q; q.k = K; q.vt = VT; q.n_tok = N; q.vt_ld = pl->vt_ld;
     q.row_pos = rowpos; q.cos_tab = cos_t; q.sin_tab = sin_t;
     q.nfreq = pl->nfreq; q.head_dim = hd; q.hidden = d;
+    q.q_scale = (float)(1.4426950408889634 / std::sqrt((double)hd));   // log2(e) / sqrt(head_dim)
     LAUNCH("gemm_qkv_rope", 2.0 * Nd * 3 * dd * dd, 0, true, launch_gemm(EPI_QKV, q, st));
     if (stop.hit(l, 2)) return copy_out(stop, Q, (size_t)N * d * 2, st);
     if (stop.hit(l, 3)) return copy_out(stop, K, (size_t)N * d * 2, st);

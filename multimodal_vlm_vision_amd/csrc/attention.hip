@@ -22,10 +22,13 @@
 //  * The softmax denominator comes from the padding of the last O^T row tile:
 //    row head_dim of the V^T tile holds ones (and the rows after it zeros), so
 //    O^T row head_dim accumulates sum_k P.
-// Online softmax in fp32 with exp2 and the 1/sqrt(d) scale folded into one
-// FMA; P is rounded to bf16 for the MFMA.  The running max is only raised (and
-// O rescaled) when a block's max exceeds it by more than 2^8, which keeps the
-// rescale off the common path without changing the math.  The two MFMA groups of
+// Online softmax in fp32 with exp2: q arrives scaled by log2(e)/sqrt(d) (the
+// qkv epilogue applies it before q is rounded to bf16), and every score MFMA
+// chain starts from an accumulator tile holding -m (the query's running
+// offset), so the MFMAs return the exp2 argument s - m itself and the common
+// path spends no VALU op on it; P is rounded to bf16 for the MFMA.  The offset
+// is only raised (and O rescaled) when a block's max exceeds it by more than
+// 2^8, which keeps the rescale off the common path without changing the math.  The two MFMA groups of
 // a block run at raised wave priority (s_setprio): a co-resident wave in its
 // softmax then fills the matrix pipe's gaps instead of delaying it.
 //
@@ -151,15 +154,17 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
 
   f32x16 O[QT][DT];
   float m[QT];
+  f32x16 nm[QT];   // -m[t] in every entry: the score MFMAs start from it, so they yield s - m
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     m[t] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) nm[t][e] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) O[t][dt][e] = 0.f;
   }
-  const float sc = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(head_dim)
   const int nkb = (n + KB - 1) / KB;
 
   // Direct global -> LDS tile loads through buffer resources over this head's K and V^T:
@@ -212,17 +217,14 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
       const uint16_t* Vt = reinterpret_cast<const uint16_t*>(cV);
       // ---- S^T = K Q^T for both query tiles: rows = 32 keys, columns = 32 queries
       f32x16 S[QT];
-#pragma unroll
-      for (int t = 0; t < QT; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) S[t][e] = 0.f;
       const uint16_t* kr = Kt + l32 * KS + 8 * h;
       __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * c);
 #pragma unroll
-        for (int t = 0; t < QT; ++t) S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][c], S[t], 0, 0, 0);
+        for (int t = 0; t < QT; ++t)
+          S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][c], c == 0 ? nm[t] : S[t], 0, 0, 0);
       }
       __builtin_amdgcn_s_setprio(0);
       // ---- mask keys past the segment end (last step only); lane's keys are 8g + 4h + e
@@ -238,28 +240,32 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
       bf16x8 pb[QT][2];
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
+        // S holds s - m (s = q.k in log2 units: q carries log2(e) / sqrt(head_dim))
         float mx = S[t][0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[t][e]);
         mx = max_xor32(mx);
-        const float bm = mx * sc;
-        if (kb == 0) {
-          m[t] = bm;
-        } else {
-          const bool need = bm > m[t] + 8.0f;
-          if (__builtin_amdgcn_ballot_w64(need)) {
-            const float mn = need ? bm : m[t];
-            const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
-            m[t] = mn;
+        const bool need = kb == 0 || mx > 8.0f;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          // raise the offset by the block max where needed (always on the first block)
+          const float mn = need ? m[t] + mx : m[t];
+          const float dm = mn - m[t];
+          if (kb > 0) {
+            const float alpha = __builtin_amdgcn_exp2f(-dm);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
           }
+          m[t] = mn;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            nm[t][e] = -mn;
+            S[t][e] -= dm;
+          }
         }
-        const float mo = m[t];
         uint32_t pw[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          pw[i] = pack_bf16(__builtin_amdgcn_exp2f(S[t][2 * i] * sc - mo), __builtin_amdgcn_exp2f(S[t][2 * i + 1] * sc - mo));
+          pw[i] = pack_bf16(__builtin_amdgcn_exp2f(S[t][2 * i]), __builtin_amdgcn_exp2f(S[t][2 * i + 1]));
         pb[t][0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
         pb[t][1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
       }

@@ -213,6 +213,8 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
       store_act8(p, m, oc, y);
     }
   } else if (EPI == EPI_QKV && n_base < 2 * p.hidden) {
+    // q is stored times q_scale (the attention kernel's log2(e) / sqrt(head_dim)), applied
+    // before the bf16 rounding.
     // pairs: columns c (c % 64 < 32) and c + 32 of each 64-column block.  A lane rotates 8
     // consecutive rotary pairs of one head (head_dim/2 is a multiple of 8 and the frequency
     // count per axis, head_dim/4, a multiple of 4, so each group of 4 has one axis) and writes
@@ -229,6 +231,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
       const int pair = 32 * (jj / 64) + (jj % 64);
       const int head = pair / rr, kk = pair % rr;
       const int pos = p.row_pos[m];
+      const float qs = part == 0 ? p.q_scale : 1.0f;
       uint32_t w1[4], w2[4];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -241,10 +244,10 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
         const int fi = k4 < nf ? k4 : k4 - nf;
         const float4 cs = *reinterpret_cast<const float4*>(p.cos_tab + ax * nf + fi);
         const float4 sn = *reinterpret_cast<const float4*>(p.sin_tab + ax * nf + fi);
-        const uint2 u1 = pack4(make_float4(a.x * cs.x - b.x * sn.x, a.y * cs.y - b.y * sn.y,
-                                           a.z * cs.z - b.z * sn.z, a.w * cs.w - b.w * sn.w));
-        const uint2 u2 = pack4(make_float4(b.x * cs.x + a.x * sn.x, b.y * cs.y + a.y * sn.y,
-                                           b.z * cs.z + a.z * sn.z, b.w * cs.w + a.w * sn.w));
+        const uint2 u1 = pack4(make_float4((a.x * cs.x - b.x * sn.x) * qs, (a.y * cs.y - b.y * sn.y) * qs,
+                                           (a.z * cs.z - b.z * sn.z) * qs, (a.w * cs.w - b.w * sn.w) * qs));
+        const uint2 u2 = pack4(make_float4((b.x * cs.x + a.x * sn.x) * qs, (b.y * cs.y + a.y * sn.y) * qs,
+                                           (b.z * cs.z + a.z * sn.z) * qs, (b.w * cs.w + a.w * sn.w) * qs));
         w1[2 * hf] = u1.x; w1[2 * hf + 1] = u1.y;
         w2[2 * hf] = u2.x; w2[2 * hf + 1] = u2.y;
       }

@@ -198,6 +198,7 @@ struct GemmArgs {
   const int32_t* row_pos = nullptr;
   const float* cos_tab = nullptr; const float* sin_tab = nullptr;
   int nfreq = 0, head_dim = 0, hidden = 0;
+  float q_scale = 1.0f;   // q is stored multiplied by this (log2(e) / sqrt(head_dim))
   // output scatter
   const int32_t* row_map = nullptr;
   // GELU / SwiGLU: when nonzero, also store lo = bf16(y - bf16(y)) at column + split_off

@@ -112,7 +112,9 @@ def check_block(run, layer):
     ref = O.norm(r_in, run.wl.weights, p + ".n1", c.norm_kind, c.norm_eps)
     assert_close_bf16(h1, ref, rel=2.0 ** -8, abs_=1e-5, what=f"L{layer} norm1")
 
-    qg, kg, vg = run.stage(layer, 2), run.stage(layer, 3), run.stage(layer, 4)
+    # the library stores q times log2(e)/sqrt(head_dim) (the attention kernel's exp2 scale)
+    qg = run.stage(layer, 2) / (np.log2(np.e) / np.sqrt(hd))
+    kg, vg = run.stage(layer, 3), run.stage(layer, 4)
     qkv = h1 @ W64(run, p + ".qkv.w").T + W64(run, p + ".qkv.b")
     q = O.apply_rope(qkv[:, :d].reshape(-1, H, hd), ang)
     k = O.apply_rope(qkv[:, d:2 * d].reshape(-1, H, hd), ang)

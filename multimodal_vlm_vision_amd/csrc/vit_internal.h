@@ -189,6 +189,7 @@ struct GemmArgs {
   // columns, [hi(g) | lo(g)] repeated, and the product is sum_k (hi + lo)[k] * B[n][k].
   int a_group = 0;
   uint32_t a_bytes = 0, b_bytes = 0;              // operand extents (set by launch_gemm)
+  int group_m = 8;                                // row tiles per XCD tile group (set by launch_gemm)
   const float* bias = nullptr;
   void* out = nullptr; int64_t ldo = 0;           // fp32 row-major, or blocked bf16 (GELU / SwiGLU)
   // QKV epilogue

@@ -33,7 +33,9 @@
  *  - All validation happens before the first enqueue.
  *  - The caller owns every device buffer (pixels, workspace, output).  The
  *    library owns its weight arena (inside vit_ctx) and the plan's host data.
- *    Only vit_finalize_weights and vit_graph_capture allocate device memory.
+ *    Only vit_finalize_weights and vit_graph_capture[_bucket] allocate device
+ *    memory (graph objects); vit_graph_capture_bucket also allocates pinned
+ *    host memory for its staging buffer.
  *  - Device pointers are plain HIP device addresses; streams are hipStream_t
  *    passed as void* (NULL = the default stream).
  *  - Pixels are uint8 only: there is no float input and no "already
@@ -182,6 +184,33 @@ vit_status vit_graph_capture(const vit_ctx* ctx, const vit_plan* plan, void* ws,
 vit_status vit_graph_io(const vit_graph* g, uint8_t** pixels_in, float** out);
 vit_status vit_graph_launch(vit_graph* g, void* stream);
 void vit_graph_destroy(vit_graph* g);
+
+/* Shape-bucketed graph ("GPUModelRunner.execute_model" notes, capture
+ * section: graphs are captured largest shape first and smaller ones reuse
+ * the memory; vLLM PR #55370 report, comment highlights: a u8 input buffer
+ * inside the graph, and no normalisation work on padding rows).
+ * vit_graph_capture_bucket captures the forward for a capacity plan
+ * (`plan`: the largest batch the graph must serve) in a form whose kernels
+ * read the batch sizes (patches, merge units, attention work-list lengths)
+ * from device memory, so padded capacity is skipped by normalisation,
+ * attention and the products rather than computed.  Launched plainly
+ * (vit_graph_launch) it encodes `plan`.  Also allocates one pinned host
+ * staging buffer of the plan's metadata size.  Same requirements as
+ * vit_graph_capture. */
+vit_status vit_graph_capture_bucket(const vit_ctx* ctx, const vit_plan* plan, void* ws,
+                                    size_t ws_bytes, void* stream, vit_graph** out);
+/* Replays a bucketed graph for another plan of the same context: the plan's
+ * metadata is written into the graph's metadata region (one asynchronous
+ * host-to-device copy on `stream`, from the staging buffer, which is reused
+ * once the previous copy has completed) and the graph is launched.  The
+ * caller writes the plan's pixels (its pixel_bytes) at vit_graph_io's input
+ * first; its output is rows [0, N/4) of vit_graph_io's output.  The plan
+ * must fit the capacity: patches, pixel bytes, largest grid side and each
+ * attention work-list length at most the captured plan's (VIT_E_SHAPE names
+ * the first that does not), and the same tower configuration (VIT_E_ARG).
+ * VIT_E_STATE for a graph not captured with vit_graph_capture_bucket.  An
+ * empty plan enqueues nothing. */
+vit_status vit_graph_launch_plan(vit_graph* g, const vit_plan* plan, void* stream);
 
 void vit_destroy(vit_ctx* ctx);
 

@@ -72,6 +72,8 @@ _SIGS = {
     "vit_graph_capture": (ctypes.c_int32, [_P, _P, _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
     "vit_graph_io": (ctypes.c_int32, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
     "vit_graph_launch": (ctypes.c_int32, [_P, _P]),
+    "vit_graph_capture_bucket": (ctypes.c_int32, [_P, _P, _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
+    "vit_graph_launch_plan": (ctypes.c_int32, [_P, _P, _P]),
     "vit_graph_destroy": (None, [_P]),
     "vit_destroy": (None, [_P]),
     "vit_encode_profiled": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P,
@@ -194,18 +196,25 @@ class Plan:
 
 
 class Graph:
-    def __init__(self, tower, plan: Plan, ws, stream=None):
+    """vit_graph_capture, or vit_graph_capture_bucket when bucket=True (plan = the capacity)."""
+
+    def __init__(self, tower, plan: Plan, ws, stream=None, bucket: bool = False):
         self.lib = tower.lib
         self.handle = _P()
         self._keep = (tower, plan, ws)
-        _check(self.lib, self.lib.vit_graph_capture(tower.handle, plan.handle, _ptr(ws), ws.numel(),
-                                                    _stream_handle(stream), ctypes.byref(self.handle)))
+        capture = self.lib.vit_graph_capture_bucket if bucket else self.lib.vit_graph_capture
+        _check(self.lib, capture(tower.handle, plan.handle, _ptr(ws), ws.numel(),
+                                 _stream_handle(stream), ctypes.byref(self.handle)))
         pin, pout = _P(), _P()
         _check(self.lib, self.lib.vit_graph_io(self.handle, ctypes.byref(pin), ctypes.byref(pout)))
         self.pixels_ptr, self.out_ptr = pin.value, pout.value
 
     def launch(self, stream=None):
         _check(self.lib, self.lib.vit_graph_launch(self.handle, _stream_handle(stream)))
+
+    def launch_plan(self, plan: Plan, stream=None):
+        """Bucketed graph: replay for another plan that fits the captured capacity."""
+        _check(self.lib, self.lib.vit_graph_launch_plan(self.handle, plan.handle, _stream_handle(stream)))
 
     def close(self):
         if self.handle:
@@ -273,6 +282,10 @@ class VisionTower:
 
     def capture(self, plan: Plan, ws, stream=None) -> Graph:
         return Graph(self, plan, ws, stream)
+
+    def capture_bucket(self, plan: Plan, ws, stream=None) -> Graph:
+        """Bucketed graph for the capacity `plan`; replay other plans with Graph.launch_plan."""
+        return Graph(self, plan, ws, stream, bucket=True)
 
     def close(self):
         if self.handle:

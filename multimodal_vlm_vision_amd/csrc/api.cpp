@@ -149,7 +149,7 @@ struct Prof {
 // Enqueues the forward.  Exactly one of pixels / patches is non-null.
 vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels,
                    const uint8_t* patches, char* ws, float* out, hipStream_t st, bool upload,
-                   const Stop& stop, Prof* prof = nullptr) {
+                   const Stop& stop, Prof* prof = nullptr, bool bucket = false) {
   const vit_config& c = ctx->cfg;
   const DeviceWeights& W = ctx->w;
   const int64_t N = pl->n_rows;
@@ -175,13 +175,20 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   uint16_t* O = reinterpret_cast<uint16_t*>(ws + pl->off_o);
   uint16_t* F = reinterpret_cast<uint16_t*>(ws + pl->off_f);
 
-  if (pl->vt_ld > N) VIT_TRY(launch_vt_pad_zero(VT, d, N, pl->vt_ld, st));
+  // bucketed graph: batch sizes come from the RunDims the replay uploads (the plan here is
+  // the capacity); every count-dependent kernel gets a pointer into it
+  const RunDims* dims = bucket ? reinterpret_cast<const RunDims*>(ws + pl->off_dims) : nullptr;
+  const int32_t* rows_dev = dims ? &dims->n_rows : nullptr;
+  const int32_t* units_dev = dims ? &dims->n_units : nullptr;
+
+  VIT_TRY(launch_vt_pad_zero(VT, d, N, pl->vt_ld, st, rows_dev));
 
   // 1. rescale + normalise + patchify: every needed pixel byte read once, 1176 bf16 written per row
   const double np_bytes = (double)pl->pixel_read_bytes + Nd * kFeat * 2;
   if (pixels)
     LAUNCH("normpatch", 0, np_bytes, false,
-           launch_normpatch(pixels, units, pl->n_units, W.lut, ctx->norm_affine ? &ctx->affine : nullptr, X, st));
+           launch_normpatch(pixels, units, pl->n_units, W.lut, ctx->norm_affine ? &ctx->affine : nullptr, X, st,
+                            units_dev));
   else
     LAUNCH("normrows_u8", 0, Nd * kFeat * 3, false, launch_normrows_u8(patches, N, W.lut, X, st));
   if (stop.hit(-1, 0)) return copy_blocked(stop, X, N, kFeatPad, 1, kFeat, st);
@@ -189,7 +196,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   // 2. patch embedding (conv with kernel == stride as one GEMM), fp32 into the residual
   GemmArgs g;
   g.A = X; g.lda = kFeatPad; g.B = W.pe_w; g.ldb = kFeatPad;
-  g.M = (int)N; g.N = d; g.K = kFeatPad; g.out = R; g.ldo = d;
+  g.M = (int)N; g.N = d; g.K = kFeatPad; g.out = R; g.ldo = d; g.m_dev = rows_dev;
   LAUNCH("gemm_patch_embed", 2.0 * Nd * dd * kFeat, 0, true, launch_gemm(EPI_F32, g, st));
   if (stop.hit(-1, 1)) return copy_out(stop, R, (size_t)N * d * 4, st);
 
@@ -197,12 +204,12 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   for (int l = 0; l < c.layers; ++l) {
     const LayerW& L = W.layers[l];
     LAUNCH("rownorm", 0, norm_bytes, false,
-           launch_rownorm(c.norm_kind, R, N, d, L.n1g, L.n1b, c.norm_eps, H, split, 1, st));
+           launch_rownorm(c.norm_kind, R, N, d, L.n1g, L.n1b, c.norm_eps, H, split, 1, st, rows_dev));
     if (stop.hit(l, 1)) return copy_blocked(stop, H, N, S * d, 1, S * d, st);
 
     GemmArgs q;
     q.A = H; q.lda = S * d; q.B = L.qkv_w; q.ldb = d; q.a_group = split ? d : 0;
-    q.M = (int)N; q.N = 3 * d; q.K = d; q.bias = L.qkv_b;
+    q.M = (int)N; q.N = 3 * d; q.K = d; q.bias = L.qkv_b; q.m_dev = rows_dev;
     q.q = Q; q.k = K; q.vt = VT; q.n_tok = N; q.vt_ld = pl->vt_ld;
     q.row_pos = rowpos; q.cos_tab = cos_t; q.sin_tab = sin_t;
     q.nfreq = pl->nfreq; q.head_dim = hd; q.hidden = d;
@@ -226,28 +233,30 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     if (lists.n_long > 0) {
       AttnArgs a1 = at;
       a1.n_long = lists.n_long;
+      if (dims) a1.n_long_dev = windowed ? &dims->win_long : &dims->full_long;
       LAUNCH("attention", 4.0 * dd * lists.sq_long, 0, true, launch_attention(a1, st));
     }
     if (lists.n_short > 0) {
       AttnArgs a2 = at;
       a2.n_short = lists.n_short;
+      if (dims) a2.n_short_dev = windowed ? &dims->win_short : &dims->full_short;
       LAUNCH("attention_short", 4.0 * dd * lists.sq_short, 0, true, launch_attention(a2, st));
     }
     if (stop.hit(l, 5)) return copy_blocked(stop, O, N, d, 1, d, st);
 
     GemmArgs pj;
     pj.A = O; pj.lda = d; pj.B = L.proj_w; pj.ldb = d;
-    pj.M = (int)N; pj.N = d; pj.K = d; pj.bias = L.proj_b; pj.out = R; pj.ldo = d;
+    pj.M = (int)N; pj.N = d; pj.K = d; pj.bias = L.proj_b; pj.out = R; pj.ldo = d; pj.m_dev = rows_dev;
     LAUNCH("gemm_proj_residual", 2.0 * Nd * dd * dd, 0, true, launch_gemm(EPI_RES, pj, st));
     if (stop.hit(l, 6)) return copy_out(stop, R, (size_t)N * d * 4, st);
 
     LAUNCH("rownorm", 0, norm_bytes, false,
-           launch_rownorm(c.norm_kind, R, N, d, L.n2g, L.n2b, c.norm_eps, H, split, 1, st));
+           launch_rownorm(c.norm_kind, R, N, d, L.n2g, L.n2b, c.norm_eps, H, split, 1, st, rows_dev));
     if (stop.hit(l, 7)) return copy_blocked(stop, H, N, S * d, 1, S * d, st);
 
     GemmArgs f1;
     f1.A = H; f1.lda = S * d; f1.B = L.fc1_w; f1.ldb = d; f1.a_group = split ? d : 0;
-    f1.M = (int)N; f1.K = d; f1.bias = L.fc1_b; f1.out = F; f1.ldo = S * mp;
+    f1.M = (int)N; f1.K = d; f1.bias = L.fc1_b; f1.out = F; f1.ldo = S * mp; f1.m_dev = rows_dev;
     f1.split_off = split ? mp : 0;
     if (c.mlp_kind == VIT_MLP_GELU) {
       f1.N = mp;
@@ -261,7 +270,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
 
     GemmArgs f2;
     f2.A = F; f2.lda = S * mp; f2.B = L.fc2_w; f2.ldb = mp; f2.a_group = split ? mp : 0;
-    f2.M = (int)N; f2.N = d; f2.K = mp; f2.bias = L.fc2_b; f2.out = R; f2.ldo = d;
+    f2.M = (int)N; f2.N = d; f2.K = mp; f2.bias = L.fc2_b; f2.out = R; f2.ldo = d; f2.m_dev = rows_dev;
     LAUNCH("gemm_fc2_residual", 2.0 * Nd * dd * c.mlp_dim, 0, true, launch_gemm(EPI_RES, f2, st));
     if (stop.hit(l, 9)) return copy_out(stop, R, (size_t)N * d * 4, st);
   }
@@ -270,19 +279,21 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   // side by side as one row of 4 * S * d columns), then the MLP
   const int L = c.layers;
   LAUNCH("rownorm", 0, norm_bytes, false,
-         launch_rownorm(c.norm_kind, R, N, d, W.mq_g, W.mq_b, c.norm_eps, H, split, 4, st));
+         launch_rownorm(c.norm_kind, R, N, d, W.mq_g, W.mq_b, c.norm_eps, H, split, 4, st, rows_dev));
   if (stop.hit(L, 1)) return copy_blocked(stop, H, N, S * d, 4, S * d, st);
   const int64_t U = pl->n_units;
   const double Ud = (double)U;
   GemmArgs m1;
   m1.A = H; m1.lda = S * 4 * d; m1.B = W.m1_w; m1.ldb = 4 * d; m1.a_group = split ? d : 0;
   m1.M = (int)U; m1.N = 4 * d; m1.K = 4 * d; m1.bias = W.m1_b; m1.out = F; m1.ldo = S * 4 * d;
+  m1.m_dev = units_dev;
   m1.split_off = split ? 4 * d : 0;
   LAUNCH("gemm_merger_fc1_gelu", 2.0 * Ud * 16 * dd * dd, 0, true, launch_gemm(EPI_GELU, m1, st));
   if (stop.hit(L, 2)) return copy_blocked(stop, F, U, S * 4 * d, 1, S * 4 * d, st);
   GemmArgs m2;
   m2.A = F; m2.lda = S * 4 * d; m2.B = W.m2_w; m2.ldb = 4 * d; m2.a_group = split ? 4 * d : 0;
   m2.M = (int)U; m2.N = c.out_dim; m2.K = 4 * d; m2.bias = W.m2_b; m2.out = out; m2.ldo = c.out_dim;
+  m2.m_dev = units_dev;
   m2.row_map = unitdst;
   LAUNCH("gemm_merger_fc2", 2.0 * Ud * c.out_dim * 4 * dd, 0, true, launch_gemm(EPI_OUT, m2, st));
   if (stop.hit(L, 3)) return copy_out(stop, out, (size_t)U * c.out_dim * 4, st);
@@ -595,8 +606,10 @@ vit_status vit_debug_stage(const vit_ctx* ctx, const vit_plan* plan, const uint8
   return forward(ctx, plan, pixels_u8, nullptr, w, out, static_cast<hipStream_t>(stream), true, s);
 }
 
-vit_status vit_graph_capture(const vit_ctx* ctx, const vit_plan* plan, void* ws, size_t ws_bytes,
-                             void* stream, vit_graph** out) {
+namespace {
+
+vit_status capture_graph(const vit_ctx* ctx, const vit_plan* plan, void* ws, size_t ws_bytes,
+                         void* stream, bool bucket, vit_graph** out) {
   if (!out) {
     set_error("out must not be NULL");
     return VIT_E_ARG;
@@ -622,7 +635,7 @@ vit_status vit_graph_capture(const vit_ctx* ctx, const vit_plan* plan, void* ws,
     return VIT_E_HIP;
   }
   vit_status s = forward(ctx, plan, reinterpret_cast<const uint8_t*>(w + plan->off_pix), nullptr, w,
-                         reinterpret_cast<float*>(w + plan->off_out), cap, false, Stop{});
+                         reinterpret_cast<float*>(w + plan->off_out), cap, false, Stop{}, nullptr, bucket);
   e = hipStreamEndCapture(cap, &graph);
   (void)hipStreamDestroy(cap);
   if (s != VIT_OK) {
@@ -652,7 +665,91 @@ vit_status vit_graph_capture(const vit_ctx* ctx, const vit_plan* plan, void* ws,
   g->ws = ws;
   g->graph = graph;
   g->exec = exec;
+  g->bucket = bucket;
+  if (bucket) {
+    // pinned staging copy of the metadata region: the capacity plan's tables (cos/sin stay
+    // valid for every smaller plan) with the per-batch parts rewritten at each launch
+    hipEvent_t ev = nullptr;
+    if (hipHostMalloc(reinterpret_cast<void**>(&g->staging), plan->meta.size(), hipHostMallocDefault) !=
+            hipSuccess ||
+        hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+      vit_graph_destroy(g);
+      set_error("staging buffer for the bucketed graph: %s", hipGetErrorString(hipGetLastError()));
+      return VIT_E_HIP;
+    }
+    g->staged = ev;
+    std::memcpy(g->staging, plan->meta.data(), plan->meta.size());
+  }
   *out = g;
+  return VIT_OK;
+}
+
+}  // namespace
+
+vit_status vit_graph_capture(const vit_ctx* ctx, const vit_plan* plan, void* ws, size_t ws_bytes,
+                             void* stream, vit_graph** out) {
+  return capture_graph(ctx, plan, ws, ws_bytes, stream, false, out);
+}
+
+vit_status vit_graph_capture_bucket(const vit_ctx* ctx, const vit_plan* plan, void* ws,
+                                    size_t ws_bytes, void* stream, vit_graph** out) {
+  return capture_graph(ctx, plan, ws, ws_bytes, stream, true, out);
+}
+
+vit_status vit_graph_launch_plan(vit_graph* g, const vit_plan* plan, void* stream) {
+  if (!g || !plan) {
+    set_error("graph and plan must not be NULL");
+    return VIT_E_ARG;
+  }
+  if (!g->bucket) {
+    set_error("graph was not captured with vit_graph_capture_bucket");
+    return VIT_E_STATE;
+  }
+  const vit_plan* cap = g->plan;
+  const vit_config& a = plan->cfg;
+  const vit_config& b = cap->cfg;
+  if (a.hidden != b.hidden || a.heads != b.heads || a.layers != b.layers || a.mlp_dim != b.mlp_dim ||
+      a.window_px != b.window_px || a.out_dim != b.out_dim || plan->head_dim != cap->head_dim ||
+      plan->split != cap->split) {
+    set_error("plan was built for another tower configuration than the captured one");
+    return VIT_E_ARG;
+  }
+  if (plan->n_rows == 0) return VIT_OK;
+  struct Fit {
+    const char* what;
+    int64_t need, have;
+  } fits[] = {{"patches", plan->n_rows, cap->n_rows},
+              {"pixel bytes", (int64_t)plan->pixel_bytes, (int64_t)cap->pixel_bytes},
+              {"largest grid side", plan->max_pos, cap->max_pos},
+              {"long attention units", plan->full.n_long, cap->full.n_long},
+              {"short attention units", plan->full.n_short, cap->full.n_short},
+              {"long window units", plan->win.n_long, cap->win.n_long},
+              {"short window units", plan->win.n_short, cap->win.n_short}};
+  for (const Fit& f : fits)
+    if (f.need > f.have) {
+      set_error("plan exceeds the bucket: %lld %s, capacity %lld", (long long)f.need, f.what,
+                (long long)f.have);
+      return VIT_E_SHAPE;
+    }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the staging buffer is rewritten only once the previous upload from it has completed
+  HIP_TRY(hipEventSynchronize(static_cast<hipEvent_t>(g->staged)));
+  uint8_t* dst = g->staging;
+  const uint8_t* src = plan->meta.data();
+  auto put = [&](int64_t to, int64_t from, size_t bytes) {
+    if (bytes) std::memcpy(dst + to, src + from, bytes);
+  };
+  put(cap->off_dims, plan->off_dims, sizeof(RunDims));
+  put(cap->off_units, plan->off_units, (size_t)plan->n_units * sizeof(UnitDesc));
+  put(cap->off_rowpos, plan->off_rowpos, (size_t)plan->n_rows * sizeof(int32_t));
+  put(cap->off_unitdst, plan->off_unitdst, (size_t)plan->n_units * sizeof(int32_t));
+  put(cap->full.off_long, plan->full.off_long, (size_t)plan->full.n_long * sizeof(AttnWork));
+  put(cap->full.off_short, plan->full.off_short, (size_t)plan->full.n_short * sizeof(AttnWork));
+  put(cap->win.off_long, plan->win.off_long, (size_t)plan->win.n_long * sizeof(AttnWork));
+  put(cap->win.off_short, plan->win.off_short, (size_t)plan->win.n_short * sizeof(AttnWork));
+  HIP_TRY(hipMemcpyAsync(g->ws, dst, cap->meta.size(), hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(g->staged), st));
+  HIP_TRY(hipGraphLaunch(static_cast<hipGraphExec_t>(g->exec), st));
   return VIT_OK;
 }
 
@@ -678,6 +775,11 @@ vit_status vit_graph_launch(vit_graph* g, void* stream) {
 
 void vit_graph_destroy(vit_graph* g) {
   if (!g) return;
+  if (g->staged) {
+    (void)hipEventSynchronize(static_cast<hipEvent_t>(g->staged));
+    (void)hipEventDestroy(static_cast<hipEvent_t>(g->staged));
+  }
+  if (g->staging) (void)hipHostFree(g->staging);
   if (g->exec) (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(g->exec));
   if (g->graph) (void)hipGraphDestroy(static_cast<hipGraph_t>(g->graph));
   delete g;

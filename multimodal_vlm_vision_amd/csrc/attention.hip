@@ -87,9 +87,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-template <int HD, int NW>
+// DYN: the work-list length comes from device memory at run time (bucketed graphs); a separate
+// instantiation, so the plain path keeps it a launch constant.
+template <int HD, int NW, bool DYN>
 __global__ void __launch_bounds__(NW * 64, 2)
-attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
+attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int32_t* __restrict__ n_work_dev) {
   constexpr int NCH = HD / 16;               // 16-wide reduction chunks of S^T = K Q^T
   constexpr int DT = (HD + 1 + 31) / 32;     // 32-row tiles of O^T, incl. the row of ones
   constexpr int KS = HD + 8;                 // K tile row stride (elements)
@@ -114,8 +116,10 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
   __shared__ __attribute__((aligned(16))) uint32_t sV0[VROWS * VDW], sV1[VROWS * VDW];
 
   // ---- work unit: XCD-contiguous ranges of (head, unit), units of a segment adjacent
+  if (DYN) n_work = *n_work_dev;
   const int G = n_work * a.heads;
   const int pid = blockIdx.x;
+  if (pid >= G) return;
   const int xcd = pid & 7, local = pid >> 3;
   const int per = G >> 3, rem = G & 7;
   const int logical = xcd * per + min(xcd, rem) + local;
@@ -326,29 +330,40 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work) {
 
 template <int HD>
 hipError_t run_hd(const AttnArgs& a, hipStream_t st) {
-  if (a.n_long > 0)
-    hipLaunchKernelGGL((attn_kernel<HD, 4>), dim3(a.n_long * a.heads), dim3(256), 0, st, a, a.work_long,
-                       a.n_long);
-  if (a.n_short > 0)
-    hipLaunchKernelGGL((attn_kernel<HD, 1>), dim3(a.n_short * a.heads), dim3(64), 0, st, a, a.work_short,
-                       a.n_short);
+  if (a.n_long > 0 && a.n_long_dev)
+    hipLaunchKernelGGL((attn_kernel<HD, 4, true>), dim3(a.n_long * a.heads), dim3(256), 0, st, a, a.work_long,
+                       a.n_long, a.n_long_dev);
+  else if (a.n_long > 0)
+    hipLaunchKernelGGL((attn_kernel<HD, 4, false>), dim3(a.n_long * a.heads), dim3(256), 0, st, a, a.work_long,
+                       a.n_long, nullptr);
+  if (a.n_short > 0 && a.n_short_dev)
+    hipLaunchKernelGGL((attn_kernel<HD, 1, true>), dim3(a.n_short * a.heads), dim3(64), 0, st, a, a.work_short,
+                       a.n_short, a.n_short_dev);
+  else if (a.n_short > 0)
+    hipLaunchKernelGGL((attn_kernel<HD, 1, false>), dim3(a.n_short * a.heads), dim3(64), 0, st, a, a.work_short,
+                       a.n_short, nullptr);
   return hipGetLastError();
 }
 
-__global__ void vt_pad_zero_kernel(uint16_t* vt, int rows, int64_t n_tok, int64_t vt_ld) {
-  const int pad = (int)(vt_ld - n_tok);
+// Zeroes V^T columns [n, n + 64) (clipped to the pitch) of every row: the attention's tile
+// loads read at most 40 keys past the last token.  n is the token count, read at run time
+// when n_tok_dev is set (bucketed graph).
+__global__ void vt_pad_zero_kernel(uint16_t* vt, int rows, int64_t n_tok, const int32_t* n_tok_dev, int64_t vt_ld) {
+  const int64_t n = n_tok_dev ? (int64_t)*n_tok_dev : n_tok;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)rows * pad) return;
-  vt[(i / pad) * vt_ld + n_tok + i % pad] = 0;
+  if (i >= (int64_t)rows * 64) return;
+  const int64_t col = n + (i & 63);
+  if (col < vt_ld) vt[(i >> 6) * vt_ld + col] = 0;
 }
 
 }  // namespace
 
-vit_status launch_vt_pad_zero(uint16_t* vt, int rows, int64_t n_tok, int64_t vt_ld, void* stream) {
-  if (vt_ld <= n_tok || rows <= 0) return VIT_OK;
-  const int64_t n = (int64_t)rows * (vt_ld - n_tok);
+vit_status launch_vt_pad_zero(uint16_t* vt, int rows, int64_t n_tok, int64_t vt_ld, void* stream,
+                              const int32_t* n_tok_dev) {
+  if ((vt_ld <= n_tok && !n_tok_dev) || rows <= 0) return VIT_OK;
+  const int64_t n = (int64_t)rows * 64;
   hipLaunchKernelGGL(vt_pad_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), vt, rows, n_tok, vt_ld);
+                     static_cast<hipStream_t>(stream), vt, rows, n_tok, n_tok_dev, vt_ld);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("V^T pad clear: %s", hipGetErrorString(e));

@@ -150,7 +150,7 @@ struct Geo {
 
 // Applies the epilogue to one staged 32-row slice (rows m_base.., columns n_base.., width W = TN*32).
 template <int EPI, int W>
-__device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* sc, int m_base, int n_base,
+__device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const float* sc, int m_base, int n_base,
                                                int lane) {
   constexpr int SST = W + 8;
   constexpr int C4 = W / 4;   // float4 chunks per row
@@ -159,7 +159,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
     for (int q = 0; q < 32 * C4 / 64; ++q) {
       const int id = lane + 64 * q, r = id / C4, c4 = id % C4;
       const int m = m_base + r, n = n_base + 4 * c4;
-      if (m >= p.M) continue;
+      if (m >= M) continue;
       const float4 v = *reinterpret_cast<const float4*>(sc + r * SST + 4 * c4);
       if (EPI == EPI_F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)m * p.ldo + n) = v;
@@ -184,7 +184,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
     for (int blk = 0; blk < 2 * OB; ++blk) {
       const int rg = blk / OB, ob = blk % OB;
       const int r = 16 * rg + r16, m = m_base + r;
-      if (m >= p.M) continue;
+      if (m >= M) continue;
       const int c = kt_chunk(m, q);
       float y[8];
       int oc;
@@ -227,7 +227,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
       const int id = lane + 64 * q, r = id / G8, g = id % G8;
       const int cl = (g / 4) * 64 + (g % 4) * 8;          // local column of the first member
       const int m = m_base + r, n = n_base + cl;
-      if (m >= p.M) continue;
+      if (m >= M) continue;
       const int part = n / d, jj = n - part * d;
       const int pair = 32 * (jj / 64) + (jj % 64);
       const int head = pair / rr, kk = pair % rr;
@@ -265,7 +265,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
     for (int q = 0; q < 4 * W / 64; ++q) {
       const int id = lane + 64 * q, rg = id % 4, c = id / 4;
       const int m = m_base + 8 * rg, n = n_base + c;
-      if (m >= p.M) continue;
+      if (m >= M) continue;
       const float b = p.bias[n];
       const float4 v0 = make_float4(sc[(8 * rg + 0) * SST + c] + b, sc[(8 * rg + 1) * SST + c] + b,
                                     sc[(8 * rg + 2) * SST + c] + b, sc[(8 * rg + 3) * SST + c] + b);
@@ -274,7 +274,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
       const int nn = n - 2 * d, head = nn / hd, dd = nn % hd;
       uint16_t* o = p.vt + ((int64_t)head * hd + dd) * p.vt_ld + m;
       const uint2 u0 = pack4(v0);
-      if (m + 8 <= p.M) {
+      if (m + 8 <= M) {
         const uint2 u1 = pack4(v1);
         *reinterpret_cast<uint4*>(o) = make_uint4(u0.x, u0.y, u1.x, u1.y);
       } else {
@@ -284,7 +284,9 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, const float* s
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI, int OCC>
+// DYN: M comes from device memory at run time (bucketed graphs); a separate instantiation, so
+// the plain path keeps M as a launch constant.
+template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI, int OCC, bool DYN>
 __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_kernel(GemmArgs p) {
   using G = Geo<BM, BN, WM, WN, SPLIT, OCC>;
@@ -296,9 +298,13 @@ gemm_kernel(GemmArgs p) {
   const int wm = wv % WM, wn = wv / WM;
 
   // ---- tile index: XCD-contiguous ranges, then grouped row-major order
-  const int gm = (p.M + BM - 1) / BM, gn = (p.N + BN - 1) / BN;
+  // M at run time when a bucketed graph passes it in device memory (the grid covers the
+  // capacity; workgroups past this batch's tiles leave at once)
+  const int M = DYN ? *p.m_dev : p.M;
+  const int gm = (M + BM - 1) / BM, gn = (p.N + BN - 1) / BN;
   const int Gt = gm * gn;
   const int pid = blockIdx.x;
+  if (pid >= Gt) return;
   const int xcd = pid & 7, local = pid >> 3;
   const int per = Gt >> 3, rem = Gt & 7;
   const int logical = xcd * per + min(xcd, rem) + local;
@@ -320,7 +326,7 @@ gemm_kernel(GemmArgs p) {
   // variants with this clang; only the first LA / LB entries are used)
   static_assert(LA <= 16 && LB <= 16, "load plan");
   uint32_t offa[16], offb[16];
-  const int last_ga = (p.M + 15) / 16 - 1, last_gb = p.N / 16 - 1;
+  const int last_ga = (M + 15) / 16 - 1, last_gb = p.N / 16 - 1;
   const int64_t kba = p.lda / BK, kbb = p.ldb / BK;   // blocks per row group
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
@@ -457,7 +463,7 @@ gemm_kernel(GemmArgs p) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sc[(8 * (e / 4) + lr + (e % 4)) * G::SST + j * 32 + lc] = acc[i][j][e];
-    epilogue_slice<EPI, TN * 32>(p, sc, m0 + wm * TM * 32 + i * 32, n0 + wn * TN * 32, lane);
+    epilogue_slice<EPI, TN * 32>(p, M, sc, m0 + wm * TM * 32 + i * 32, n0 + wn * TN * 32, lane);
   }
 }
 
@@ -481,16 +487,24 @@ template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI, int OCC = 1>
 hipError_t run(const GemmArgs& a, hipStream_t st) {
   using G = Geo<BM, BN, WM, WN, SPLIT, OCC>;
   const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC>), dim3((unsigned)tiles), dim3(G::NT), G::kSmem,
-                     st, a);
+  if (a.m_dev)
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC, true>), dim3((unsigned)tiles), dim3(G::NT),
+                       G::kSmem, st, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC, false>), dim3((unsigned)tiles), dim3(G::NT),
+                       G::kSmem, st, a);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI, int OCC = 1>
 hipError_t allow_smem() {
   using G = Geo<BM, BN, WM, WN, SPLIT, OCC>;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC, false>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
+  return e;
 }
 
 template <bool SPLIT, int EPI>

@@ -39,13 +39,14 @@ __device__ __forceinline__ float bf16_lo(float x) {
 // VPL = float4 chunks per lane (d <= 256 * VPL).  SPLIT: each output row is
 // [hi | lo] with hi = bf16(y) and lo = bf16(y - hi).  Input row `row` lands in blocked row
 // row / group at column offset (row % group) * S * d of a group * S * d wide matrix.
-template <int KIND, int VPL, bool SPLIT>
+template <int KIND, int VPL, bool SPLIT, bool DYN>
 __global__ void __launch_bounds__(kThreads)
-rownorm_kernel(const float* __restrict__ r, int64_t rows, int d, const float* __restrict__ g,
-               const float* __restrict__ b, float eps, int group, uint16_t* __restrict__ out) {
+rownorm_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __restrict__ rows_dev, int d,
+               const float* __restrict__ g, const float* __restrict__ b, float eps, int group,
+               uint16_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  if (row >= (DYN ? (int64_t)*rows_dev : rows)) return;   // DYN: run-time count (bucketed graph)
   const float4* src = reinterpret_cast<const float4*>(r + row * d);
   const int n4 = d >> 2;
   float4 v[VPL];
@@ -97,22 +98,30 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, int d, const float* __
 }
 
 template <int KIND, bool SPLIT>
-vit_status launch_kind(const float* r, int64_t rows, int d, const float* g, const float* b,
-                       float eps, int group, uint16_t* out, hipStream_t st) {
+vit_status launch_kind(const float* r, int64_t rows, const int32_t* rows_dev, int d, const float* g,
+                       const float* b, float eps, int group, uint16_t* out, hipStream_t st) {
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   const int vpl = (d / 4 + 63) / 64;
-  if (vpl <= 1)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 1, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, group, out);
-  else if (vpl <= 2)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 2, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, group, out);
-  else if (vpl <= 5)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 5, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, group, out);
-  else if (vpl <= 8)
-    hipLaunchKernelGGL((rownorm_kernel<KIND, 8, SPLIT>), grid, dim3(kThreads), 0, st, r, rows, d, g, b, eps, group, out);
-  else {
+#define VIT_ROWNORM(V)                                                                                  \
+  if (rows_dev)                                                                                         \
+    hipLaunchKernelGGL((rownorm_kernel<KIND, V, SPLIT, true>), grid, dim3(kThreads), 0, st, r, rows,    \
+                       rows_dev, d, g, b, eps, group, out);                                             \
+  else                                                                                                  \
+    hipLaunchKernelGGL((rownorm_kernel<KIND, V, SPLIT, false>), grid, dim3(kThreads), 0, st, r, rows,   \
+                       rows_dev, d, g, b, eps, group, out);
+  if (vpl <= 1) {
+    VIT_ROWNORM(1)
+  } else if (vpl <= 2) {
+    VIT_ROWNORM(2)
+  } else if (vpl <= 5) {
+    VIT_ROWNORM(5)
+  } else if (vpl <= 8) {
+    VIT_ROWNORM(8)
+  } else {
     set_error("rownorm: hidden %d too wide (max 2048)", d);
     return VIT_E_ARG;
   }
+#undef VIT_ROWNORM
   return VIT_OK;
 }
 
@@ -151,7 +160,7 @@ vit_status launch_unblock(const uint16_t* src, int64_t rows, int cols, int group
 
 vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
                           const float* b, float eps, uint16_t* out, bool split, int group,
-                          void* stream) {
+                          void* stream, const int32_t* rows_dev) {
   if (rows <= 0) return VIT_OK;
   if (d % 32 || group < 1 || rows % group) {
     set_error("rownorm: hidden %d must be a multiple of 32 and rows %lld a multiple of the group %d", d,
@@ -161,11 +170,11 @@ vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const f
   hipStream_t st = static_cast<hipStream_t>(stream);
   vit_status s;
   if (kind == VIT_NORM_LAYER)
-    s = split ? launch_kind<VIT_NORM_LAYER, true>(r, rows, d, g, b, eps, group, out, st)
-              : launch_kind<VIT_NORM_LAYER, false>(r, rows, d, g, b, eps, group, out, st);
+    s = split ? launch_kind<VIT_NORM_LAYER, true>(r, rows, rows_dev, d, g, b, eps, group, out, st)
+              : launch_kind<VIT_NORM_LAYER, false>(r, rows, rows_dev, d, g, b, eps, group, out, st);
   else
-    s = split ? launch_kind<VIT_NORM_RMS, true>(r, rows, d, g, b, eps, group, out, st)
-              : launch_kind<VIT_NORM_RMS, false>(r, rows, d, g, b, eps, group, out, st);
+    s = split ? launch_kind<VIT_NORM_RMS, true>(r, rows, rows_dev, d, g, b, eps, group, out, st)
+              : launch_kind<VIT_NORM_RMS, false>(r, rows, rows_dev, d, g, b, eps, group, out, st);
   if (s != VIT_OK) return s;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

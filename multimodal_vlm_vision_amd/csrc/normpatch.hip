@@ -80,14 +80,17 @@ __device__ __forceinline__ uint16_t feature_entry(int f) {
 template <bool AFFINE>
 __global__ void __launch_bounds__(kThreads)
 normpatch_kernel(const uint8_t* __restrict__ pixels, const UnitDesc* __restrict__ units,
-                 int64_t n_units, const uint16_t* __restrict__ lut_g, NormAffine na, uint16_t* __restrict__ x) {
+                 int64_t n_units, const int32_t* __restrict__ n_units_dev, const uint16_t* __restrict__ lut_g,
+                 NormAffine na, uint16_t* __restrict__ x) {
   __shared__ uint32_t stage[kUnitsPerBlock * kUnitDwords];
   __shared__ __attribute__((aligned(16))) uint16_t tab[kFeatPad];
   __shared__ uint16_t lut[3 * 256];
   __shared__ UnitDesc sud[kUnitsPerBlock];
   const int tid = threadIdx.x;
   const int64_t u0 = (int64_t)blockIdx.x * kUnitsPerBlock;
-  const int nu = (int)min<int64_t>(kUnitsPerBlock, n_units - u0);
+  const int64_t n_all = n_units_dev ? (int64_t)*n_units_dev : n_units;   // run-time count (bucketed graph)
+  if (u0 >= n_all) return;
+  const int nu = (int)min<int64_t>(kUnitsPerBlock, n_all - u0);
   if (!AFFINE)
     for (int i = tid; i < 3 * 256; i += kThreads) lut[i] = lut_g[i];
   for (int f = tid; f < kFeatPad; f += kThreads) tab[f] = feature_entry(f);
@@ -209,15 +212,17 @@ normrows_kernel(const uint8_t* __restrict__ patches, int64_t n_rows,
 }  // namespace
 
 vit_status launch_normpatch(const uint8_t* pixels, const UnitDesc* units, int64_t n_units,
-                            const uint16_t* lut, const NormAffine* affine, uint16_t* x, void* stream) {
+                            const uint16_t* lut, const NormAffine* affine, uint16_t* x, void* stream,
+                            const int32_t* n_units_dev) {
   if (n_units <= 0) return VIT_OK;
   const int64_t blocks = (n_units + kUnitsPerBlock - 1) / kUnitsPerBlock;
   if (affine)
     hipLaunchKernelGGL(normpatch_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), pixels, units, n_units, lut, *affine, x);
+                       static_cast<hipStream_t>(stream), pixels, units, n_units, n_units_dev, lut, *affine, x);
   else
     hipLaunchKernelGGL(normpatch_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), pixels, units, n_units, lut, NormAffine{}, x);
+                       static_cast<hipStream_t>(stream), pixels, units, n_units, n_units_dev, lut, NormAffine{},
+                       x);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("normpatch launch: %s", hipGetErrorString(e));

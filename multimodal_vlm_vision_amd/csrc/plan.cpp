@@ -179,6 +179,7 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
 
   std::vector<uint8_t>& blob = p->meta;
   blob.clear();
+  p->off_dims = put(blob, std::vector<RunDims>(1, RunDims{}));   // filled in below
   p->off_units = put(blob, units);
   p->off_rowpos = put(blob, rowpos);
   p->off_unitdst = put(blob, unitdst);
@@ -187,6 +188,14 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   build_lists(item_segs, blob, p->full, p->max_seg_full);
   if (wu > 0) build_lists(win_segs, blob, p->win, p->max_seg_win);
   blob.resize(round_up((int64_t)blob.size(), 256));
+  RunDims dims{};
+  dims.n_rows = (int32_t)n_rows;
+  dims.n_units = (int32_t)p->n_units;
+  dims.full_long = p->full.n_long;
+  dims.full_short = p->full.n_short;
+  dims.win_long = p->win.n_long;
+  dims.win_short = p->win.n_short;
+  std::memcpy(blob.data() + p->off_dims, &dims, sizeof dims);
 
   // ---- workspace layout
   const int64_t N = n_rows, d = c.hidden;

@@ -75,6 +75,18 @@ struct AttnLists {
   double sq_short = 0.0;
 };
 
+// Batch sizes for a bucketed graph: the kernels of a graph captured for a capacity plan read
+// these from device memory (the first 32 bytes of the plan's metadata region) instead of
+// their launch-time counts, so any batch that fits the capacity replays the same graph.
+struct RunDims {
+  int32_t n_rows;       // patches N
+  int32_t n_units;      // merge units N / 4
+  int32_t full_long, full_short;   // attention work-list lengths, item segments
+  int32_t win_long, win_short;     // and windows
+  int32_t pad[2];
+};
+static_assert(sizeof(RunDims) == 32, "RunDims layout");
+
 // Per-channel affine form of the normalisation, y = fma(x, a_c, b_c) in float32 then
 // bf16 round-to-nearest-even.  Used only when the host has verified that it reproduces
 // the exactly rounded table for all 768 (channel, byte) pairs.
@@ -142,6 +154,7 @@ struct vit_plan {
 
   // metadata blob uploaded to ws at offset 0
   std::vector<uint8_t> meta;
+  int64_t off_dims = 0;           // RunDims (always at 0)
   int64_t off_units = 0, off_rowpos = 0, off_unitdst = 0, off_cos = 0, off_sin = 0;
   vitmi::AttnLists full, win;
 
@@ -153,10 +166,13 @@ struct vit_plan {
 
 struct vit_graph {
   const vit_ctx* ctx = nullptr;
-  const vit_plan* plan = nullptr;
+  const vit_plan* plan = nullptr;   // the captured (capacity) plan
   void* ws = nullptr;
   void* graph = nullptr;   // hipGraph_t
   void* exec = nullptr;    // hipGraphExec_t
+  bool bucket = false;     // kernels read the batch sizes from the RunDims in ws
+  uint8_t* staging = nullptr;   // pinned copy of the metadata region (bucket replays)
+  void* staged = nullptr;       // hipEvent_t: the last upload from `staging` has completed
 };
 
 namespace vitmi {
@@ -185,6 +201,7 @@ struct GemmArgs {
   const uint16_t* A = nullptr; int64_t lda = 0;   // blocked (kt_index) [M][lda] bf16, lda >= K (2K split)
   const uint16_t* B = nullptr; int64_t ldb = 0;   // blocked [N][ldb] bf16, ldb >= K
   int M = 0, N = 0, K = 0;                        // K = logical reduction length
+  const int32_t* m_dev = nullptr;                 // if set: M read at run time (M above is the capacity)
   // Split activations: when a_group > 0, each A row holds hi/lo pairs in groups of a_group
   // columns, [hi(g) | lo(g)] repeated, and the product is sum_k (hi + lo)[k] * B[n][k].
   int a_group = 0;
@@ -211,16 +228,19 @@ vit_status launch_gemm(int epi, const GemmArgs& a, void* stream);
 vit_status prepare_gemm_kernels();
 
 // affine == nullptr: table lookups (always exact)
+// n_units_dev (optional): unit count read at run time; n_units is then the capacity.
 vit_status launch_normpatch(const uint8_t* pixels, const UnitDesc* units, int64_t n_units,
-                            const uint16_t* lut, const NormAffine* affine, uint16_t* x, void* stream);
+                            const uint16_t* lut, const NormAffine* affine, uint16_t* x, void* stream,
+                            const int32_t* n_units_dev = nullptr);
 vit_status launch_normrows_u8(const uint8_t* patches, int64_t n_rows, const uint16_t* lut,
                               uint16_t* x, void* stream);
 // Row norm of fp32 rows [rows][d] into bf16 in the blocked GEMM layout; split: each row is
 // [hi(d) | lo(d)].  group > 1 stores `group` consecutive rows as one row of group * S * d
 // columns (the merger's view of 2x2 patch blocks).
+// rows_dev (optional): row count read at run time; rows is then the capacity.
 vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
                           const float* b, float eps, uint16_t* out, bool split, int group,
-                          void* stream);
+                          void* stream, const int32_t* rows_dev = nullptr);
 // Blocked bf16 matrix -> row-major [rows][out_cols] (debug copies): row m of the result is
 // row m / group, columns (m % group) * cols + [0, out_cols) of a blocked matrix with
 // group * cols columns.
@@ -235,11 +255,14 @@ struct AttnArgs {
   int heads = 0, head_dim = 0;
   const AttnWork* work_long = nullptr; int n_long = 0;
   const AttnWork* work_short = nullptr; int n_short = 0;
+  // if set: list lengths read at run time (n_long / n_short above are the capacities)
+  const int32_t* n_long_dev = nullptr; const int32_t* n_short_dev = nullptr;
 };
 vit_status launch_attention(const AttnArgs& a, void* stream);
-// Zeroes the pad columns [n_tok, vt_ld) of the rows V^T rows (attention reads whole 16-byte
-// chunks, so keys past a segment may come from the pad; they get probability 0, and must not
-// be NaN).
-vit_status launch_vt_pad_zero(uint16_t* vt, int rows, int64_t n_tok, int64_t vt_ld, void* stream);
+// Zeroes V^T columns [n_tok, n_tok + 64), clipped to the pitch, of every row (the attention
+// reads whole 16-byte chunks up to 40 keys past a segment; those keys get probability 0 and
+// must not be NaN).  n_tok_dev (optional): token count read at run time.
+vit_status launch_vt_pad_zero(uint16_t* vt, int rows, int64_t n_tok, int64_t vt_ld, void* stream,
+                              const int32_t* n_tok_dev = nullptr);
 
 }  // namespace vitmi

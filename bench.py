@@ -10,8 +10,10 @@ graph; K steps are timed between device synchronisations.
 
 Also reported: a per-kernel breakdown from hipEvents around every launch
 (one profiled eager forward per timed step), the dominant kernel's roofline
-fraction, aggregate MFMA utilisation, and the CPU oracle's throughput on a
-bounded sample of the same batch (the three smallest images, full depth).
+fraction, aggregate MFMA utilisation, the CPU oracle's throughput on a
+bounded sample of the same batch (the three smallest images, full depth), and
+a shape-bucketed graph captured for the batch replaying it and its first half
+of items, against that half's own exact-shape graph.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu]
 """
@@ -129,6 +131,49 @@ def normpatch_stream(n_images=48, side=1344, reps=5):
     return res
 
 
+def bucket_replay(tower, plan, wl, steps, warmup, stream):
+    """One bucketed graph captured for the batch (the capacity) replays the batch and a smaller
+    batch (its first half of items) through vit_graph_launch_plan, against that smaller batch's
+    own exact-shape graph: the cost of serving mixes from one capture."""
+    import torch
+    from workloads import pack_pixels
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / steps * 1e3
+
+    sub_items = wl.items[:max(1, len(wl.items) // 2)]
+    g = [it.grid_thw for it in sub_items]
+    f = [it.n_frames for it in sub_items]
+    sub = tower.plan(g, f)
+    px_full = torch.from_numpy(pack_pixels(wl.items)).cuda()
+    px_sub = torch.from_numpy(pack_pixels(sub_items)).cuda()
+    bws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device="cuda")
+    bg = tower.capture_bucket(plan, bws)
+    off = bg.pixels_ptr - bws.data_ptr()
+    bws[off:off + px_full.numel()].copy_(px_full)
+    full_ms = timed(lambda: bg.launch_plan(plan, stream))
+    bws[off:off + px_sub.numel()].copy_(px_sub)
+    sub_ms = timed(lambda: bg.launch_plan(sub, stream))
+    bg.close()
+    del bws
+    sws = torch.empty(sub.ws_bytes, dtype=torch.uint8, device="cuda")
+    sg = tower.capture(sub, sws)
+    soff = sg.pixels_ptr - sws.data_ptr()
+    sws[soff:soff + px_sub.numel()].copy_(px_sub)
+    exact_ms = timed(lambda: sg.launch(stream))
+    sg.close()
+    return {"capacity_patches": plan.n_patches, "full_ms": full_ms, "subset_items": len(sub_items),
+            "subset_patches": sub.n_patches, "subset_ms": sub_ms, "subset_exact_graph_ms": exact_ms,
+            "subset_overhead_pct": 100.0 * (sub_ms / exact_ms - 1.0)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +185,7 @@ def main():
                     help="also run a 512 MiB device-to-device copy (3 times): the known-size kernel "
                          "that scales the HBM byte counters of a rocprofv3 --pmc run")
     ap.add_argument("--no-stream", action="store_true", help="skip the normpatch streaming measurement")
+    ap.add_argument("--no-bucket", action="store_true", help="skip the shape-bucketed graph measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the vision tower is not sharded "
@@ -250,6 +296,12 @@ def main():
     }
     graph.close()
     roof["traffic"], roof["traffic_source"] = measured_traffic(dom)
+    if not args.no_bucket:
+        line["bucket"] = bucket_replay(tower, plan, wl, args.steps, args.warmup, stream)
+        b = line["bucket"]
+        log(f"bucketed graph (capacity {b['capacity_patches']} patches): full batch {b['full_ms']:.3f} ms; "
+            f"{b['subset_patches']}-patch batch {b['subset_ms']:.3f} ms vs {b['subset_exact_graph_ms']:.3f} ms "
+            f"in its own graph")
     if not args.no_stream:
         log("normpatch streaming measurement ...")
         line["normpatch_stream"] = normpatch_stream()

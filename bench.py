@@ -13,7 +13,8 @@ Also reported: a per-kernel breakdown from hipEvents around every launch
 fraction, aggregate MFMA utilisation, the CPU oracle's throughput on a
 bounded sample of the same batch (the three smallest images, full depth), and
 a shape-bucketed graph captured for the batch replaying it and its first half
-of items, against that half's own exact-shape graph.
+of items, against that half's own exact-shape graph, and the batch through
+the vision-embedding cache (cold, warm, and the content-key pass alone).
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu]
 """
@@ -131,6 +132,37 @@ def normpatch_stream(n_images=48, side=1344, reps=5):
     return res
 
 
+def cache_replay(tower, plan, pixels, ws, out, wl, steps, stream):
+    """The batch through the vision-embedding cache: cold (every item encoded and inserted) and
+    warm (every item served from the arena), plus the content-key pass alone.  Wall time per
+    call; each call synchronises once on its keys."""
+    import torch
+    from multimodal_vlm_vision_amd import EmbeddingCache
+
+    arena = torch.empty(plan.out_rows * plan.out_cols * 4 + (1 << 20), dtype=torch.uint8, device="cuda")
+
+    def wall(fn, n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / n * 1e3
+
+    cold = []
+    for _ in range(2):
+        cache = EmbeddingCache(tower, arena)
+        cold.append(wall(lambda: tower.encode_cached(cache, plan, pixels, ws, out, stream), 1))
+        cache.close()
+    cache = EmbeddingCache(tower, arena)
+    tower.encode_cached(cache, plan, pixels, ws, out, stream)
+    warm_ms = wall(lambda: tower.encode_cached(cache, plan, pixels, ws, out, stream), steps)
+    cache.close()
+    keys_ms = wall(lambda: tower.pixel_keys(plan, pixels, ws, stream), steps)
+    return {"items": len(wl.items), "cold_ms": min(cold), "warm_ms": warm_ms, "keys_ms": keys_ms,
+            "pixel_bytes": plan.pixel_bytes, "key_gbs": plan.pixel_bytes / (keys_ms * 1e-3) / 1e9}
+
+
 def bucket_replay(tower, plan, wl, steps, warmup, stream):
     """One bucketed graph captured for the batch (the capacity) replays the batch and a smaller
     batch (its first half of items) through vit_graph_launch_plan, against that smaller batch's
@@ -186,6 +218,7 @@ def main():
                          "that scales the HBM byte counters of a rocprofv3 --pmc run")
     ap.add_argument("--no-stream", action="store_true", help="skip the normpatch streaming measurement")
     ap.add_argument("--no-bucket", action="store_true", help="skip the shape-bucketed graph measurement")
+    ap.add_argument("--no-cache", action="store_true", help="skip the embedding-cache measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the vision tower is not sharded "
@@ -296,6 +329,12 @@ def main():
     }
     graph.close()
     roof["traffic"], roof["traffic_source"] = measured_traffic(dom)
+    if not args.no_cache:
+        line["embedding_cache"] = cache_replay(tower, plan, pixels, ws, out, wl, args.steps, stream)
+        c = line["embedding_cache"]
+        log(f"embedding cache: cold {c['cold_ms']:.3f} ms, warm (all {c['items']} items cached) "
+            f"{c['warm_ms']:.3f} ms; content keys alone {c['keys_ms']:.3f} ms "
+            f"({c['key_gbs']:.0f} GB/s of pixels)")
     if not args.no_bucket:
         line["bucket"] = bucket_replay(tower, plan, wl, args.steps, args.warmup, stream)
         b = line["bucket"]

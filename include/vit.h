@@ -35,7 +35,8 @@
  *    library owns its weight arena (inside vit_ctx) and the plan's host data.
  *    Only vit_finalize_weights and vit_graph_capture[_bucket] allocate device
  *    memory (graph objects); vit_graph_capture_bucket also allocates pinned
- *    host memory for its staging buffer.
+ *    host memory for its staging buffer.  The embedding cache's arena is the
+ *    caller's.
  *  - Device pointers are plain HIP device addresses; streams are hipStream_t
  *    passed as void* (NULL = the default stream).
  *  - Pixels are uint8 only: there is no float input and no "already
@@ -108,6 +109,7 @@ typedef struct vit_config {
 typedef struct vit_ctx vit_ctx;
 typedef struct vit_plan vit_plan;
 typedef struct vit_graph vit_graph;
+typedef struct vit_cache vit_cache;
 
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char* vit_last_error(void);
@@ -211,6 +213,41 @@ vit_status vit_graph_capture_bucket(const vit_ctx* ctx, const vit_plan* plan, vo
  * VIT_E_STATE for a graph not captured with vit_graph_capture_bucket.  An
  * empty plan enqueues nothing. */
 vit_status vit_graph_launch_plan(vit_graph* g, const vit_plan* plan, void* stream);
+
+/* Vision-embedding cache ("vLLM multimodal inference | ViT performance
+ * optimisation", section 2.3: a vision-embedding cache shared across
+ * requests).  Merged embeddings of items are kept in `arena` (device,
+ * caller-owned, 256-byte aligned, arena_bytes may be 0) and reused when an
+ * item with the same pixel content key and the same grid (t, h, w, n_frames)
+ * is encoded again through vit_encode_cached.  The arena is a ring with
+ * first-in first-out eviction; an item larger than the arena is never cached.
+ * The cache is bound to ctx (the weights).  No GPU call; not thread-safe. */
+vit_status vit_cache_create(const vit_ctx* ctx, void* arena, size_t arena_bytes, vit_cache** out);
+/* Number of cached items and arena bytes they hold. */
+vit_status vit_cache_stats(const vit_cache* cache, int64_t* entries, size_t* bytes_used);
+void vit_cache_destroy(vit_cache* cache);
+/* vit_encode through the cache: computes every item's pixel content key on
+ * the device, copies the keys to the host and synchronises `stream` (the
+ * hit/miss split is a host decision), copies cached items' rows from the
+ * arena into `out`, encodes the remaining items as one batch (their pixels
+ * gathered into the workspace), writes their rows into `out` (item order,
+ * as vit_encode) and caches them.  Everything after the key read is
+ * asynchronous on `stream`; the arena must not be touched by other work
+ * until it completes.  *n_hits (optional) receives the number of items
+ * served from the cache.  pixels_u8 must be 16-byte aligned.  Errors as
+ * vit_encode. */
+vit_status vit_encode_cached(const vit_ctx* ctx, vit_cache* cache, const vit_plan* plan,
+                             const uint8_t* pixels_u8, void* ws, size_t ws_bytes, float* out,
+                             void* stream, int32_t* n_hits);
+/* The content keys alone: keys[2 i], keys[2 i + 1] (host array of 2 * n_items)
+ * receive item i's 128-bit key.  With the item's pixel bytes read as L / 8
+ * little-endian 64-bit words w_k, lane j (G_0 = 0x9e3779b97f4a7c15,
+ * G_1 = 0xd1b54a32d192ed03) is mix(S_j ^ (L * G_j)) with
+ * S_j = sum_k mix(w_k + (k + 1) G_j) mod 2^64 and mix the SplitMix64
+ * finaliser (Steele, Lea and Flood, OOPSLA 2014).  A content key, not a
+ * cryptographic hash.  Synchronises `stream`. */
+vit_status vit_pixel_keys(const vit_ctx* ctx, const vit_plan* plan, const uint8_t* pixels_u8,
+                          void* ws, size_t ws_bytes, uint64_t* keys, void* stream);
 
 void vit_destroy(vit_ctx* ctx);
 

@@ -7,6 +7,7 @@ missing: there is no CPU or PyTorch fallback.
 
 from .binding import (  # noqa: F401
     LIB_PATH,
+    EmbeddingCache,
     Graph,
     Plan,
     VisionTower,

@@ -74,6 +74,12 @@ _SIGS = {
     "vit_graph_launch": (ctypes.c_int32, [_P, _P]),
     "vit_graph_capture_bucket": (ctypes.c_int32, [_P, _P, _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
     "vit_graph_launch_plan": (ctypes.c_int32, [_P, _P, _P]),
+    "vit_cache_create": (ctypes.c_int32, [_P, _P, ctypes.c_size_t, ctypes.POINTER(_P)]),
+    "vit_cache_stats": (ctypes.c_int32, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)]),
+    "vit_cache_destroy": (None, [_P]),
+    "vit_encode_cached": (ctypes.c_int32, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P,
+                                           ctypes.POINTER(ctypes.c_int32)]),
+    "vit_pixel_keys": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint64), _P]),
     "vit_graph_destroy": (None, [_P]),
     "vit_destroy": (None, [_P]),
     "vit_encode_profiled": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P,
@@ -163,6 +169,7 @@ class Plan:
         g = np.ascontiguousarray(np.asarray(grid_thw, dtype=np.int32).reshape(-1, 3))
         f = np.ascontiguousarray(np.asarray(n_frames, dtype=np.int32).reshape(-1))
         self.handle = _P()
+        self.n_items = len(f)
         _check(self.lib, self.lib.vit_plan_create(
             tower.handle, g.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
             f.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(f), ctypes.byref(self.handle)))
@@ -228,6 +235,33 @@ class Graph:
             pass
 
 
+class EmbeddingCache:
+    """vit_cache over a caller-owned device arena (a uint8 torch tensor)."""
+
+    def __init__(self, tower, arena):
+        self.lib = tower.lib
+        self.handle = _P()
+        self._keep = (tower, arena)
+        n = arena.numel() if arena is not None else 0
+        _check(self.lib, self.lib.vit_cache_create(tower.handle, _ptr(arena), n, ctypes.byref(self.handle)))
+
+    def stats(self):
+        e, b = ctypes.c_int64(), ctypes.c_size_t()
+        _check(self.lib, self.lib.vit_cache_stats(self.handle, ctypes.byref(e), ctypes.byref(b)))
+        return e.value, b.value
+
+    def close(self):
+        if self.handle:
+            self.lib.vit_cache_destroy(self.handle)
+            self.handle = _P()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 class VisionTower:
     """Owns one vit_ctx: configuration, weights (host copies until finalize, then a device arena)."""
 
@@ -282,6 +316,23 @@ class VisionTower:
 
     def capture(self, plan: Plan, ws, stream=None) -> Graph:
         return Graph(self, plan, ws, stream)
+
+    def encode_cached(self, cache: "EmbeddingCache", plan: Plan, pixels, ws, out, stream=None) -> int:
+        """vit_encode through the embedding cache; returns the number of items served from it."""
+        hits = ctypes.c_int32()
+        _check(self.lib, self.lib.vit_encode_cached(self.handle, cache.handle, plan.handle, _ptr(pixels), _ptr(ws),
+                                                    ws.numel() if ws is not None else 0, _ptr(out),
+                                                    _stream_handle(stream), ctypes.byref(hits)))
+        return hits.value
+
+    def pixel_keys(self, plan: Plan, pixels, ws, stream=None) -> np.ndarray:
+        """[n_items][2] uint64 content keys of the items' pixels."""
+        keys = np.zeros((plan.n_items, 2), dtype=np.uint64)
+        _check(self.lib, self.lib.vit_pixel_keys(self.handle, plan.handle, _ptr(pixels), _ptr(ws),
+                                                 ws.numel() if ws is not None else 0,
+                                                 keys.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                                 _stream_handle(stream)))
+        return keys
 
     def capture_bucket(self, plan: Plan, ws, stream=None) -> Graph:
         """Bucketed graph for the capacity `plan`; replay other plans with Graph.launch_plan."""

@@ -401,6 +401,11 @@ bool verify_affine(const vit_config& c, const uint16_t (&lut)[3][256], NormAffin
 }
 
 }  // namespace
+
+vit_status check_plan_ws(const vit_ctx* ctx, const vit_plan* plan, const void* ws, size_t ws_bytes) {
+  return check_common(ctx, plan, ws, ws_bytes);
+}
+
 }  // namespace vitmi
 
 using namespace vitmi;

@@ -259,6 +259,12 @@ struct AttnArgs {
   const int32_t* n_long_dev = nullptr; const int32_t* n_short_dev = nullptr;
 };
 vit_status launch_attention(const AttnArgs& a, void* stream);
+// Per-item partial sums of the pixel content key (pixel_hash.hip): items_dev[i] = {byte offset,
+// 64-bit word count}, sums_dev[2 i + j] = lane-j sum (zeroed here first).
+vit_status launch_pixel_hash(const uint8_t* pixels, const int64_t* items_dev, int n_items, int64_t max_words,
+                             uint64_t* sums_dev, void* stream);
+// The checks every encode entry point makes on (ctx, plan, workspace).
+vit_status check_plan_ws(const vit_ctx* ctx, const vit_plan* plan, const void* ws, size_t ws_bytes);
 // Zeroes V^T columns [n_tok, n_tok + 64), clipped to the pitch, of every row (the attention
 // reads whole 16-byte chunks up to 40 keys past a segment; those keys get probability 0 and
 // must not be NaN).  n_tok_dev (optional): token count read at run time.

@@ -452,3 +452,34 @@ def test_tiny_workload_forward_shape():
     assert out.shape == (4, 128) and np.all(np.isfinite(out))
     cfg5 = tower_config(5)
     assert cfg5.window_px // cfg5.patch == 8
+
+
+# ------------------------------------------------------------------ pixel content key (embedding cache)
+
+def test_pixel_key_mix_is_splitmix64():
+    """The finaliser reproduces the published SplitMix64 outputs from seed 0."""
+    from oracle import pixel_key as PK
+    got = [int(v) for v in PK.splitmix64_stream(0, 3)]
+    assert got == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_pixel_key_sensitivity_and_position():
+    """One changed byte, two swapped words or a different length change both lanes; equal
+    content gives equal keys."""
+    from oracle import pixel_key as PK
+    g = np.random.default_rng(11)
+    x = g.integers(0, 256, size=(1, 56, 28, 3), dtype=np.uint8)
+    k = PK.item_key(x)
+    assert PK.item_key(x.copy()) == k
+    y = x.copy()
+    y[0, 10, 3, 1] ^= 1
+    ky = PK.item_key(y)
+    assert ky[0] != k[0] and ky[1] != k[1]
+    w = x.reshape(-1).view("<u8").copy()
+    w[[0, 1]] = w[[1, 0]]
+    kw = PK.item_key(w.view(np.uint8))
+    if w[0] != w[1]:
+        assert kw[0] != k[0] and kw[1] != k[1]
+    z = np.concatenate([x.reshape(-1), np.zeros(16, np.uint8)])
+    kz = PK.item_key(z)
+    assert kz[0] != k[0] and kz[1] != k[1]

@@ -14,7 +14,8 @@ fraction, aggregate MFMA utilisation, the CPU oracle's throughput on a
 bounded sample of the same batch (the three smallest images, full depth), and
 a shape-bucketed graph captured for the batch replaying it and its first half
 of items, against that half's own exact-shape graph, and the batch through
-the vision-embedding cache (cold, warm, and the content-key pass alone).
+the vision-embedding cache (cold, warm, and the content-key pass alone), and
+the device resize of the batch's images made off-grid.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu]
 """
@@ -132,6 +133,47 @@ def normpatch_stream(n_images=48, side=1344, reps=5):
     return res
 
 
+def resize_measure(wl, steps):
+    """Device resize of the batch's images, each made off-grid by a seeded offset of up to 13
+    pixels per side, back to the 28-pixel grid: one launch per image, all on one stream, timed
+    with events; bytes = source read once + output written once (algorithmic)."""
+    import numpy as np
+    import torch
+    from multimodal_vlm_vision_amd import resize_side, resize_u8
+
+    g = np.random.default_rng(1234)
+
+    def run(shapes):
+        jobs = []
+        for F, H, W in shapes:
+            h, w = H + int(g.integers(1, 14)), W - int(g.integers(1, 14))
+            src = torch.from_numpy(g.integers(0, 256, size=(F, h, w, 3), dtype=np.uint8)).cuda()
+            dst = torch.empty(F, resize_side(h), resize_side(w), 3, dtype=torch.uint8, device="cuda")
+            jobs.append((src, h, w, F, dst))
+        moved = sum(s.numel() + d.numel() for s, _, _, _, d in jobs)
+
+        def batch():
+            for src, h, w, F, dst in jobs:
+                resize_u8(src, h, w, F, dst)
+
+        batch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            batch()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbs = moved / (ms * 1e-3) / 1e9
+        return {"images": len(jobs), "bytes": moved, "ms": ms, "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+
+    res = run([it.frames.shape[:3] for it in wl.items])
+    # a streaming batch far larger than the last-level cache: 48 images of about 1344 x 1344
+    res["stream"] = run([(1, 1344, 1344)] * 48)
+    return res
+
+
 def cache_replay(tower, plan, pixels, ws, out, wl, steps, stream):
     """The batch through the vision-embedding cache: cold (every item encoded and inserted) and
     warm (every item served from the arena), plus the content-key pass alone.  Wall time per
@@ -219,6 +261,7 @@ def main():
     ap.add_argument("--no-stream", action="store_true", help="skip the normpatch streaming measurement")
     ap.add_argument("--no-bucket", action="store_true", help="skip the shape-bucketed graph measurement")
     ap.add_argument("--no-cache", action="store_true", help="skip the embedding-cache measurement")
+    ap.add_argument("--no-resize", action="store_true", help="skip the device-resize measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the vision tower is not sharded "
@@ -329,6 +372,12 @@ def main():
     }
     graph.close()
     roof["traffic"], roof["traffic_source"] = measured_traffic(dom)
+    if not args.no_resize:
+        line["resize"] = resize_measure(wl, args.steps)
+        r = line["resize"]
+        for tag, q in (("batch", r), ("stream", r["stream"])):
+            log(f"device resize ({tag}): {q['images']} off-grid images, {q['bytes'] / 1e6:.1f} MB moved, "
+                f"{q['ms']:.3f} ms, {q['gbs']:.0f} GB/s ({100 * q['hbm_frac']:.1f}% of HBM peak)")
     if not args.no_cache:
         line["embedding_cache"] = cache_replay(tower, plan, pixels, ws, out, wl, args.steps, stream)
         c = line["embedding_cache"]

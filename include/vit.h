@@ -249,6 +249,24 @@ vit_status vit_encode_cached(const vit_ctx* ctx, vit_cache* cache, const vit_pla
 vit_status vit_pixel_keys(const vit_ctx* ctx, const vit_plan* plan, const uint8_t* pixels_u8,
                           void* ws, size_t ws_bytes, uint64_t* keys, void* stream);
 
+/* Device resize before the path ("vLLM multimodal inference | ViT
+ * performance optimisation", section 2.2: the preprocessor resizes and pads
+ * images; SGLang PR #35349 report: CPU preprocessing caps serving
+ * throughput).  vit_resize_side(s) = the nearest multiple of 28 to s (half
+ * up), at least 28 (0 for s < 1).  vit_resize_u8 resizes `frames` HWC RGB
+ * uint8 frames of sh x sw pixels (device, back to back) to
+ * vit_resize_side(sh) x vit_resize_side(sw) into dst (device, same layout;
+ * dst_bytes must cover it, VIT_E_WORKSPACE otherwise; src and dst 4-byte
+ * aligned and not overlapping): bilinear with half-pixel centres (source coordinate
+ * (d + 0.5) * S / D - 0.5, clamped), 11-bit fixed-point weights in integer
+ * arithmetic, rounded half up, so results are exact.  Asynchronous on
+ * `stream`; no allocation.  Sides up to 8192 pixels and sources under
+ * 4 GiB (VIT_E_SHAPE otherwise).  The output frames are valid vit_encode input for
+ * grid (t, vit_resize_side(sh) / 14, vit_resize_side(sw) / 14). */
+int32_t vit_resize_side(int32_t pixels);
+vit_status vit_resize_u8(const uint8_t* src, int32_t sh, int32_t sw, int32_t frames, uint8_t* dst,
+                         size_t dst_bytes, void* stream);
+
 void vit_destroy(vit_ctx* ctx);
 
 /* Per-kernel timing of one forward.  One record per kernel class (e.g.

@@ -15,4 +15,6 @@ from .binding import (  # noqa: F401
     header_symbols,
     load_library,
     make_config,
+    resize_side,
+    resize_u8,
 )

@@ -80,6 +80,8 @@ _SIGS = {
     "vit_encode_cached": (ctypes.c_int32, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P,
                                            ctypes.POINTER(ctypes.c_int32)]),
     "vit_pixel_keys": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint64), _P]),
+    "vit_resize_side": (ctypes.c_int32, [ctypes.c_int32]),
+    "vit_resize_u8": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
     "vit_graph_destroy": (None, [_P]),
     "vit_destroy": (None, [_P]),
     "vit_encode_profiled": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P,
@@ -95,7 +97,7 @@ _lib: Optional[ctypes.CDLL] = None
 def header_symbols() -> list:
     """Names of the functions include/vit.h declares."""
     text = open(HEADER).read()
-    decl = r"^\s*(?:const\s+char\s*\*|vit_status|void)\s+(vit_[a-z_0-9]+)\s*\("
+    decl = r"^\s*(?:const\s+char\s*\*|vit_status|void|int32_t)\s+(vit_[a-z_0-9]+)\s*\("
     return sorted(set(re.findall(decl, text, flags=re.M)))
 
 
@@ -233,6 +235,17 @@ class Graph:
             self.close()
         except Exception:
             pass
+
+
+def resize_side(pixels: int, lib: Optional[ctypes.CDLL] = None) -> int:
+    """vit_resize_side: the 28-multiple a side of `pixels` resizes to."""
+    return int((lib or load_library()).vit_resize_side(int(pixels)))
+
+
+def resize_u8(src, sh: int, sw: int, frames: int, dst, stream=None, lib: Optional[ctypes.CDLL] = None):
+    """vit_resize_u8 on device uint8 tensors (frames x sh x sw x 3 -> frames x dh x dw x 3)."""
+    lib = lib or load_library()
+    _check(lib, lib.vit_resize_u8(_ptr(src), sh, sw, frames, _ptr(dst), dst.numel(), _stream_handle(stream)))
 
 
 class EmbeddingCache:

@@ -1,3 +1,6 @@
+// Host side of the serving helpers around the path: the vision-embedding cache and the device
+// resize entry point (resize.hip).
+//
 // Vision-embedding cache: merged embeddings reused across calls, keyed by the content of an
 // item's uint8 pixels and its grid ("vLLM multimodal inference | ViT performance
 // optimisation", section 2.3 lists a vision-embedding cache shared across requests).
@@ -284,6 +287,41 @@ vit_status vit_encode_cached(const vit_ctx* ctx, vit_cache* cache, const vit_pla
     cache->head = vitmi::round_up((int64_t)(off + bytes), 256);
   }
   return VIT_OK;
+}
+
+int32_t vit_resize_side(int32_t pixels) { return pixels < 1 ? 0 : vitmi::resize_side(pixels); }
+
+vit_status vit_resize_u8(const uint8_t* src, int32_t sh, int32_t sw, int32_t frames, uint8_t* dst,
+                         size_t dst_bytes, void* stream) {
+  if (!src || !dst || sh < 1 || sw < 1 || frames < 1) {
+    vitmi::set_error("resize: src/dst must not be NULL and sh, sw, frames >= 1 (got %d, %d, %d)", sh, sw, frames);
+    return VIT_E_ARG;
+  }
+  if (sh > 8192 || sw > 8192) {
+    vitmi::set_error("resize: sides must be <= 8192 pixels");
+    return VIT_E_SHAPE;
+  }
+  const int dh = vitmi::resize_side(sh), dw = vitmi::resize_side(sw);
+  const size_t need = (size_t)frames * dh * dw * 3, have = (size_t)frames * sh * sw * 3;
+  if (dst_bytes < need) {
+    vitmi::set_error("resize: dst needs %zu bytes, got %zu", need, dst_bytes);
+    return VIT_E_WORKSPACE;
+  }
+  if (need / 256 >= ((size_t)1 << 31)) {
+    vitmi::set_error("resize: output too large");
+    return VIT_E_SHAPE;
+  }
+  if (reinterpret_cast<uintptr_t>(src) % 4 || reinterpret_cast<uintptr_t>(dst) % 4) {
+    vitmi::set_error("resize: src and dst must be 4-byte aligned");
+    return VIT_E_ARG;
+  }
+  const uint8_t* s0 = src;
+  const uint8_t* d0 = dst;
+  if (s0 < d0 + need && d0 < s0 + have) {
+    vitmi::set_error("resize: src and dst must not overlap");
+    return VIT_E_ARG;
+  }
+  return vitmi::launch_resize(src, sh, sw, frames, dst, dh, dw, stream);
 }
 
 }  // extern "C"

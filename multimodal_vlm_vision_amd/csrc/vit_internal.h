@@ -263,6 +263,11 @@ vit_status launch_attention(const AttnArgs& a, void* stream);
 // 64-bit word count}, sums_dev[2 i + j] = lane-j sum (zeroed here first).
 vit_status launch_pixel_hash(const uint8_t* pixels, const int64_t* items_dev, int n_items, int64_t max_words,
                              uint64_t* sums_dev, void* stream);
+// Device resize of uint8 HWC frames to the 28-pixel grid (resize.hip); resize_side gives the
+// target of one side.
+int resize_side(int s);
+vit_status launch_resize(const uint8_t* src, int sh, int sw, int frames, uint8_t* dst, int dh, int dw,
+                         void* stream);
 // The checks every encode entry point makes on (ctx, plan, workspace).
 vit_status check_plan_ws(const vit_ctx* ctx, const vit_plan* plan, const void* ws, size_t ws_bytes);
 // Zeroes V^T columns [n_tok, n_tok + 64), clipped to the pitch, of every row (the attention

@@ -483,3 +483,67 @@ def test_pixel_key_sensitivity_and_position():
     z = np.concatenate([x.reshape(-1), np.zeros(16, np.uint8)])
     kz = PK.item_key(z)
     assert kz[0] != k[0] and kz[1] != k[1]
+
+
+# ------------------------------------------------------------------ device resize (before the path)
+
+def test_resize_side_rule():
+    from oracle import resize as RS
+    assert [RS.resize_side(s) for s in (1, 13, 41, 42, 55, 56, 69, 70, 1344, 1000)] == \
+        [28, 28, 28, 56, 56, 56, 56, 84, 1344, 1008]
+
+
+def test_resize_identity_constant_and_closed_form():
+    from oracle import resize as RS
+    g = np.random.default_rng(5)
+    x = g.integers(0, 256, size=(2, 56, 84, 3), dtype=np.uint8)
+    assert np.array_equal(RS.resize(x), x)                      # already on the grid
+    c = np.full((1, 37, 61, 3), 173, np.uint8)
+    assert np.all(RS.resize(c) == 173)                          # constant stays constant
+    # 14 -> 28 (2x): output d samples s = d/2 - 1/4; on the ramp p_k = 16 k that is 16 s =
+    # 8 d - 4 inside, with d = 0 clamped to p_0 and d = 27 to p_13
+    ramp = np.zeros((1, 14, 14, 3), np.uint8)
+    ramp[0] = (16 * np.arange(14, dtype=np.uint8))[None, :, None]
+    out = RS.resize(ramp)[0, 5, :, 0]
+    assert out.tolist() == [0] + [8 * d - 4 for d in range(1, 27)] + [208]
+    # a single bright column spreads over its two nearest output columns on each side
+    spot = np.zeros((1, 14, 14, 3), np.uint8)
+    spot[0, :, 1] = 200
+    assert RS.resize(spot)[0, 0, :6, 0].tolist() == [0, 50, 150, 150, 50, 0]
+
+
+
+def test_resize_matches_per_pixel_exact_rationals():
+    """The vectorised integer oracle against a per-pixel evaluation of the rule in exact
+    rationals on small off-grid images (down: 41 -> 28, 47 -> 56 up, 69 -> 56)."""
+    from oracle import resize as RS
+    g = np.random.default_rng(6)
+
+    def ref(frames):
+        F, H, W, _ = frames.shape
+        dh, dw = RS.resize_side(H), RS.resize_side(W)
+
+        def ax(d, D, S):
+            s = Fraction(2 * d + 1, 2) * Fraction(S, D) - Fraction(1, 2)
+            if s <= 0:
+                return 0, 0, 0
+            i0 = math.floor(s)
+            if i0 >= S - 1:
+                return S - 1, S - 1, 0
+            return i0, i0 + 1, math.floor((s - i0) * 2048 + Fraction(1, 2))
+
+        out = np.zeros((F, dh, dw, 3), np.uint8)
+        for f in range(F):
+            for y in range(dh):
+                y0, y1, wy = ax(y, dh, H)
+                for x in range(dw):
+                    x0, x1, wx = ax(x, dw, W)
+                    for c in range(3):
+                        top = (2048 - wx) * int(frames[f, y0, x0, c]) + wx * int(frames[f, y0, x1, c])
+                        bot = (2048 - wx) * int(frames[f, y1, x0, c]) + wx * int(frames[f, y1, x1, c])
+                        out[f, y, x, c] = ((2048 - wy) * top + wy * bot + (1 << 21)) >> 22
+        return out
+
+    for h, w in ((41, 47), (69, 30), (29, 83)):
+        x = g.integers(0, 256, size=(1, h, w, 3), dtype=np.uint8)
+        assert np.array_equal(RS.resize(x), ref(x)), (h, w)

@@ -211,7 +211,8 @@ vit_status vit_graph_capture_bucket(const vit_ctx* ctx, const vit_plan* plan, vo
  * attention work-list length at most the captured plan's (VIT_E_SHAPE names
  * the first that does not), and the same tower configuration (VIT_E_ARG).
  * VIT_E_STATE for a graph not captured with vit_graph_capture_bucket.  An
- * empty plan enqueues nothing. */
+ * empty plan enqueues nothing.  Replays of one graph share its workspace:
+ * issue them on one stream (or order them), as for vit_graph_launch. */
 vit_status vit_graph_launch_plan(vit_graph* g, const vit_plan* plan, void* stream);
 
 /* Vision-embedding cache ("vLLM multimodal inference | ViT performance

@@ -28,9 +28,10 @@
 // offset), so the MFMAs return the exp2 argument s - m itself and the common
 // path spends no VALU op on it; P is rounded to bf16 for the MFMA.  The offset
 // is only raised (and O rescaled) when a block's max exceeds it by more than
-// 2^8, which keeps the rescale off the common path without changing the math.  The two MFMA groups of
-// a block run at raised wave priority (s_setprio): a co-resident wave in its
-// softmax then fills the matrix pipe's gaps instead of delaying it.
+// 2^8, which keeps the rescale off the common path without changing the math.
+// The two MFMA groups of a block run at raised wave priority (s_setprio): a
+// co-resident wave in its softmax then fills the matrix pipe's gaps instead of
+// delaying it.
 //
 // K tiles (32 keys x head_dim, row stride head_dim + 8 so 16-byte fragment
 // reads of 16 consecutive rows hit distinct banks) and V^T tiles (head_dim
@@ -41,7 +42,9 @@
 // (workgroups are dispatched round-robin over 8 XCDs) runs contiguous
 // (head, segment) ranges and shares their K/V in its L2.  Long segments use
 // 4-wave workgroups (256 queries share each K/V tile); short segments
-// (windows) use 1-wave workgroups of 64 queries.
+// (windows) use 1-wave workgroups of 64 queries.  The DYN instantiations read
+// the work-list length from device memory (bucketed graphs: the grid covers the
+// capacity and surplus workgroups leave at once).
 #include <hip/hip_runtime.h>
 
 #include <cmath>

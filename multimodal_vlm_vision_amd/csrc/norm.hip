@@ -97,9 +97,84 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __restr
   }
 }
 
+// Two rows per wave (rows 2w, 2w + 1 of a 16-row group share each 128-byte line of the blocked
+// layout): lanes 0-31 take the even row, lanes 32-63 the odd one, so every store instruction
+// writes whole lines.  VPL2 = float4 chunks per lane per row (d <= 128 * VPL2).
+template <int KIND, int VPL2, bool SPLIT, bool DYN>
+__global__ void __launch_bounds__(kThreads)
+rownorm2_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __restrict__ rows_dev, int d,
+                const float* __restrict__ g, const float* __restrict__ b, float eps, uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63, hl = lane >> 5, c32 = lane & 31;
+  const int64_t row = ((int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6)) * 2 + hl;
+  const int64_t nrows = DYN ? (int64_t)*rows_dev : rows;
+  const bool live = row < nrows;
+  const float4* src = reinterpret_cast<const float4*>(r + (live ? row : 0) * d);
+  const int n4 = d >> 2;
+  float4 v[VPL2];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL2; ++i) {
+    const int c = c32 + 32 * i;
+    v[i] = (live && c < n4) ? src[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (KIND == VIT_NORM_LAYER) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  }
+  auto half_sum = [](float x) {
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+  };
+  float mean = 0.f;
+  if (KIND == VIT_NORM_LAYER) mean = half_sum(s) / (float)d;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL2; ++i) {
+    const int c = c32 + 32 * i;
+    if (c < n4) {
+      const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+      q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    }
+  }
+  const float rstd = 1.0f / sqrtf(half_sum(q) / (float)d + eps);
+  if (!live) return;
+  const int w = d * (SPLIT ? 2 : 1);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+#pragma unroll
+  for (int i = 0; i < VPL2; ++i) {
+    const int c = c32 + 32 * i;
+    if (c < n4) {
+      const float4 gg = g4[c];
+      float4 y;
+      y.x = (v[i].x - mean) * rstd * gg.x;
+      y.y = (v[i].y - mean) * rstd * gg.y;
+      y.z = (v[i].z - mean) * rstd * gg.z;
+      y.w = (v[i].w - mean) * rstd * gg.w;
+      if (KIND == VIT_NORM_LAYER) {
+        const float4 bb = b4[c];
+        y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
+      }
+      *reinterpret_cast<uint2*>(out + kt_index(row, 4 * c, w)) =
+          make_uint2(pack_bf16(y.x, y.y), pack_bf16(y.z, y.w));
+      if (SPLIT)
+        *reinterpret_cast<uint2*>(out + kt_index(row, d + 4 * c, w)) =
+            make_uint2(pack_bf16(bf16_lo(y.x), bf16_lo(y.y)), pack_bf16(bf16_lo(y.z), bf16_lo(y.w)));
+    }
+  }
+}
+
 template <int KIND, bool SPLIT>
 vit_status launch_kind(const float* r, int64_t rows, const int32_t* rows_dev, int d, const float* g,
                        const float* b, float eps, int group, uint16_t* out, hipStream_t st) {
+  if (group == 1 && d == 1280) {   // the tower's width: two rows per wave
+    const dim3 grid2((unsigned)((rows + 2 * kRowsPerBlock - 1) / (2 * kRowsPerBlock)));
+    if (rows_dev)
+      hipLaunchKernelGGL((rownorm2_kernel<KIND, 10, SPLIT, true>), grid2, dim3(kThreads), 0, st, r, rows, rows_dev,
+                         d, g, b, eps, out);
+    else
+      hipLaunchKernelGGL((rownorm2_kernel<KIND, 10, SPLIT, false>), grid2, dim3(kThreads), 0, st, r, rows, rows_dev,
+                         d, g, b, eps, out);
+    return VIT_OK;
+  }
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   const int vpl = (d / 4 + 63) / 64;
 #define VIT_ROWNORM(V)                                                                                  \

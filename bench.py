@@ -262,6 +262,8 @@ def main():
     ap.add_argument("--no-bucket", action="store_true", help="skip the shape-bucketed graph measurement")
     ap.add_argument("--no-cache", action="store_true", help="skip the embedding-cache measurement")
     ap.add_argument("--no-resize", action="store_true", help="skip the device-resize measurement")
+    ap.add_argument("--activations", default="bf16f8", choices=["bf16f8", "bf16x2"],
+                    help="form of the compensated GEMM activations (bf16 + e4m3 residual, or hi+lo bf16 pairs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the vision tower is not sharded "
@@ -280,7 +282,7 @@ def main():
     log(f"workload {cfg.name}: {len(wl.items)} items, N={wl.n_patches} patches, "
         f"grids={[it.grid_thw for it in wl.items]} ({time.perf_counter() - t0:.1f} s to draw)")
     dev = torch.device("cuda:0")
-    tower = VisionTower(cfg)
+    tower = VisionTower(cfg, activation_precision=args.activations)
     tower.load_weights(wl.weights)
     tower.finalize()
     plan = tower.plan(wl.grid_thw, wl.n_frames)
@@ -363,7 +365,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "items": len(wl.items), "patches": wl.n_patches,
                    "layers": cfg.layers, "hidden": cfg.hidden, "heads": cfg.heads, "mlp": cfg.mlp_dim,
-                   "out_dim": cfg.out_dim, "mode": "hipgraph", "parallelism": "single-gpu"},
+                   "out_dim": cfg.out_dim, "mode": "hipgraph", "parallelism": "single-gpu",
+                   "activations": args.activations},
         "mfma_util_pct": mfma_util,
         "algorithmic_tflop_per_step": flops_step / 1e12,
         "eager_ms_per_step": eager_ms,

@@ -73,6 +73,7 @@ typedef int32_t vit_status;
 
 #define VIT_ACT_BF16     0  /* GEMM activation operands rounded once to bfloat16 */
 #define VIT_ACT_BF16X2   1  /* norm, MLP and merger activations kept as hi+lo bfloat16 pairs */
+#define VIT_ACT_BF16F8   2  /* the same activations kept as bfloat16 + e4m3 residual */
 
 #define VIT_MAX_FULL_LAYERS 64
 
@@ -102,7 +103,13 @@ typedef struct vit_config {
    * over both halves against the same bf16 weights (twice the MFMA work of the
    * qkv, MLP and merger products), which removes their activation rounding;
    * q, k, v, the attention probabilities and the attention output stay
-   * single bf16.  VIT_ACT_BF16 rounds every GEMM activation once. */
+   * single bf16.  VIT_ACT_BF16F8 keeps the same activations as hi = bf16(x)
+   * plus the residual x - hi in OCP e4m3 (scaled by 2^9); the GEMM adds the
+   * residual's product against an e4m3 copy of the weights (per-row power-of-two
+   * scales) through the scaled fp8 MFMA, so the residual costs half the MFMA
+   * time of a second bf16 product and 1 instead of 2 bytes per element (its
+   * error, ~2^-12 of x, stays far below the bf16 rounding it compensates).
+   * VIT_ACT_BF16 rounds every GEMM activation once. */
   int32_t activation_precision;
 } vit_config;
 

@@ -77,6 +77,17 @@ vit_status copy_blocked(const Stop& st, const uint16_t* src, int64_t rows, int c
   return launch_unblock(src, rows, cols, group, out_cols, static_cast<uint16_t*>(st.dst), s);
 }
 
+// compensated activation in the bf16 + e4m3 form -> [hi | residual] bf16 rows (2 * out_cols)
+vit_status copy_blocked_f8(const Stop& st, const uint16_t* src, const uint8_t* src8, int64_t rows, int cols,
+                           int group, int out_cols, hipStream_t s) {
+  const size_t bytes = (size_t)rows * out_cols * 4;
+  if (st.dst_bytes < bytes) {
+    set_error("debug stage needs %zu bytes, dst has %zu", bytes, st.dst_bytes);
+    return VIT_E_WORKSPACE;
+  }
+  return launch_unblock_f8(src, src8, rows, cols, group, out_cols, static_cast<uint16_t*>(st.dst), s);
+}
+
 vit_status check_common(const vit_ctx* ctx, const vit_plan* plan, const void* ws, size_t ws_bytes) {
   if (!ctx || !plan) {
     set_error("ctx and plan must not be NULL");
@@ -88,7 +99,7 @@ vit_status check_common(const vit_ctx* ctx, const vit_plan* plan, const void* ws
   }
   if (plan->cfg.hidden != ctx->cfg.hidden || plan->cfg.layers != ctx->cfg.layers ||
       plan->cfg.window_px != ctx->cfg.window_px || plan->head_dim != ctx->head_dim ||
-      plan->split != ctx->split) {
+      plan->split != ctx->split || plan->f8 != ctx->f8) {
     set_error("plan was built for a different tower configuration");
     return VIT_E_ARG;
   }
@@ -156,6 +167,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   const int d = c.hidden, hd = ctx->head_dim, mp = ctx->mlp_pad;
   const int S = ctx->split;            // 2: activations stored as [hi | lo] rows
   const bool split = S == 2;
+  const bool f8 = ctx->f8;             // activations stored as bf16 rows + e4m3 residuals
   const double Nd = (double)N, dd = (double)d;
   if (N == 0) return VIT_OK;
   if (prof) prof->st = st;
@@ -174,6 +186,13 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   uint16_t* VT = reinterpret_cast<uint16_t*>(ws + pl->off_vt);
   uint16_t* O = reinterpret_cast<uint16_t*>(ws + pl->off_o);
   uint16_t* F = reinterpret_cast<uint16_t*>(ws + pl->off_f);
+  uint8_t* H8 = f8 ? reinterpret_cast<uint8_t*>(ws + pl->off_h8) : nullptr;
+  uint8_t* F8 = f8 ? reinterpret_cast<uint8_t*>(ws + pl->off_f8) : nullptr;
+  // debug copies of the compensated activations: [hi | lo] rows in either form
+  auto copy_act = [&](const uint16_t* src, const uint8_t* src8, int64_t rows, int cols, int group) {
+    return f8 ? copy_blocked_f8(stop, src, src8, rows, cols, group, cols, st)
+              : copy_blocked(stop, src, rows, S * cols, group, S * cols, st);
+  };
 
   // bucketed graph: batch sizes come from the RunDims the replay uploads (the plan here is
   // the capacity); every count-dependent kernel gets a pointer into it
@@ -200,12 +219,12 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   LAUNCH("gemm_patch_embed", 2.0 * Nd * dd * kFeat, 0, true, launch_gemm(EPI_F32, g, st));
   if (stop.hit(-1, 1)) return copy_out(stop, R, (size_t)N * d * 4, st);
 
-  const double norm_bytes = Nd * dd * (4 + 2 * S);   // fp32 row in, bf16 row (hi and lo) out
+  const double norm_bytes = Nd * dd * (4 + 2 * S + (f8 ? 1 : 0));   // fp32 row in, bf16 row (hi and lo) out
   for (int l = 0; l < c.layers; ++l) {
     const LayerW& L = W.layers[l];
     LAUNCH("rownorm", 0, norm_bytes, false,
-           launch_rownorm(c.norm_kind, R, N, d, L.n1g, L.n1b, c.norm_eps, H, split, 1, st, rows_dev));
-    if (stop.hit(l, 1)) return copy_blocked(stop, H, N, S * d, 1, S * d, st);
+           launch_rownorm(c.norm_kind, R, N, d, L.n1g, L.n1b, c.norm_eps, H, split, 1, st, rows_dev, H8));
+    if (stop.hit(l, 1)) return copy_act(H, H8, N, d, 1);
 
     GemmArgs q;
     q.A = H; q.lda = S * d; q.B = L.qkv_w; q.ldb = d; q.a_group = split ? d : 0;
@@ -214,6 +233,9 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     q.row_pos = rowpos; q.cos_tab = cos_t; q.sin_tab = sin_t;
     q.nfreq = pl->nfreq; q.head_dim = hd; q.hidden = d;
     q.q_scale = (float)(1.4426950408889634 / std::sqrt((double)hd));   // log2(e) / sqrt(head_dim)
+    if (f8) {
+      q.A8 = H8; q.lda8 = d; q.B8 = L.qkv_w8; q.ldb8 = d; q.b8_scale = L.qkv_s8;
+    }
     LAUNCH("gemm_qkv_rope", 2.0 * Nd * 3 * dd * dd, 0, true, launch_gemm(EPI_QKV, q, st));
     if (stop.hit(l, 2)) return copy_out(stop, Q, (size_t)N * d * 2, st);
     if (stop.hit(l, 3)) return copy_out(stop, K, (size_t)N * d * 2, st);
@@ -251,13 +273,17 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     if (stop.hit(l, 6)) return copy_out(stop, R, (size_t)N * d * 4, st);
 
     LAUNCH("rownorm", 0, norm_bytes, false,
-           launch_rownorm(c.norm_kind, R, N, d, L.n2g, L.n2b, c.norm_eps, H, split, 1, st, rows_dev));
-    if (stop.hit(l, 7)) return copy_blocked(stop, H, N, S * d, 1, S * d, st);
+           launch_rownorm(c.norm_kind, R, N, d, L.n2g, L.n2b, c.norm_eps, H, split, 1, st, rows_dev, H8));
+    if (stop.hit(l, 7)) return copy_act(H, H8, N, d, 1);
 
     GemmArgs f1;
     f1.A = H; f1.lda = S * d; f1.B = L.fc1_w; f1.ldb = d; f1.a_group = split ? d : 0;
     f1.M = (int)N; f1.K = d; f1.bias = L.fc1_b; f1.out = F; f1.ldo = S * mp; f1.m_dev = rows_dev;
     f1.split_off = split ? mp : 0;
+    if (f8) {
+      f1.A8 = H8; f1.lda8 = d; f1.B8 = L.fc1_w8; f1.ldb8 = d; f1.b8_scale = L.fc1_s8;
+      f1.out8 = F8; f1.ldo8 = mp;
+    }
     if (c.mlp_kind == VIT_MLP_GELU) {
       f1.N = mp;
       LAUNCH("gemm_fc1_gelu", 2.0 * Nd * c.mlp_dim * dd, 0, true, launch_gemm(EPI_GELU, f1, st));
@@ -266,11 +292,14 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
       LAUNCH("gemm_gateup_swiglu", 4.0 * Nd * c.mlp_dim * dd, 0, true,
              launch_gemm(EPI_SWIGLU, f1, st));
     }
-    if (stop.hit(l, 8)) return copy_blocked(stop, F, N, S * mp, 1, S * mp, st);
+    if (stop.hit(l, 8)) return copy_act(F, F8, N, mp, 1);
 
     GemmArgs f2;
     f2.A = F; f2.lda = S * mp; f2.B = L.fc2_w; f2.ldb = mp; f2.a_group = split ? mp : 0;
     f2.M = (int)N; f2.N = d; f2.K = mp; f2.bias = L.fc2_b; f2.out = R; f2.ldo = d; f2.m_dev = rows_dev;
+    if (f8) {
+      f2.A8 = F8; f2.lda8 = mp; f2.B8 = L.fc2_w8; f2.ldb8 = mp; f2.b8_scale = L.fc2_s8;
+    }
     LAUNCH("gemm_fc2_residual", 2.0 * Nd * dd * c.mlp_dim, 0, true, launch_gemm(EPI_RES, f2, st));
     if (stop.hit(l, 9)) return copy_out(stop, R, (size_t)N * d * 4, st);
   }
@@ -279,8 +308,8 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   // side by side as one row of 4 * S * d columns), then the MLP
   const int L = c.layers;
   LAUNCH("rownorm", 0, norm_bytes, false,
-         launch_rownorm(c.norm_kind, R, N, d, W.mq_g, W.mq_b, c.norm_eps, H, split, 4, st, rows_dev));
-  if (stop.hit(L, 1)) return copy_blocked(stop, H, N, S * d, 4, S * d, st);
+         launch_rownorm(c.norm_kind, R, N, d, W.mq_g, W.mq_b, c.norm_eps, H, split, 4, st, rows_dev, H8));
+  if (stop.hit(L, 1)) return copy_act(H, H8, N, d, 4);
   const int64_t U = pl->n_units;
   const double Ud = (double)U;
   GemmArgs m1;
@@ -288,13 +317,20 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   m1.M = (int)U; m1.N = 4 * d; m1.K = 4 * d; m1.bias = W.m1_b; m1.out = F; m1.ldo = S * 4 * d;
   m1.m_dev = units_dev;
   m1.split_off = split ? 4 * d : 0;
+  if (f8) {
+    m1.A8 = H8; m1.lda8 = 4 * d; m1.B8 = W.m1_w8; m1.ldb8 = 4 * d; m1.b8_scale = W.m1_s8;
+    m1.out8 = F8; m1.ldo8 = 4 * d;
+  }
   LAUNCH("gemm_merger_fc1_gelu", 2.0 * Ud * 16 * dd * dd, 0, true, launch_gemm(EPI_GELU, m1, st));
-  if (stop.hit(L, 2)) return copy_blocked(stop, F, U, S * 4 * d, 1, S * 4 * d, st);
+  if (stop.hit(L, 2)) return copy_act(F, F8, U, 4 * d, 1);
   GemmArgs m2;
   m2.A = F; m2.lda = S * 4 * d; m2.B = W.m2_w; m2.ldb = 4 * d; m2.a_group = split ? 4 * d : 0;
   m2.M = (int)U; m2.N = c.out_dim; m2.K = 4 * d; m2.bias = W.m2_b; m2.out = out; m2.ldo = c.out_dim;
   m2.m_dev = units_dev;
   m2.row_map = unitdst;
+  if (f8) {
+    m2.A8 = F8; m2.lda8 = 4 * d; m2.B8 = W.m2_w8; m2.ldb8 = 4 * d; m2.b8_scale = W.m2_s8;
+  }
   LAUNCH("gemm_merger_fc2", 2.0 * Ud * c.out_dim * 4 * dd, 0, true, launch_gemm(EPI_OUT, m2, st));
   if (stop.hit(L, 3)) return copy_out(stop, out, (size_t)U * c.out_dim * 4, st);
   return VIT_OK;
@@ -345,8 +381,9 @@ vit_status validate_config(const vit_config* c, int* head_dim) {
     set_error("window_px must be 0 or a positive multiple of 28");
     return VIT_E_ARG;
   }
-  if (c->activation_precision != VIT_ACT_BF16 && c->activation_precision != VIT_ACT_BF16X2) {
-    set_error("activation_precision must be VIT_ACT_BF16 or VIT_ACT_BF16X2");
+  if (c->activation_precision != VIT_ACT_BF16 && c->activation_precision != VIT_ACT_BF16X2 &&
+      c->activation_precision != VIT_ACT_BF16F8) {
+    set_error("activation_precision must be VIT_ACT_BF16, VIT_ACT_BF16X2 or VIT_ACT_BF16F8");
     return VIT_E_ARG;
   }
   if (c->n_full_attn_layers < 0 || c->n_full_attn_layers > VIT_MAX_FULL_LAYERS) {
@@ -437,6 +474,7 @@ vit_status vit_create(const vit_config* cfg, vit_ctx** out) {
   ctx->head_dim = hd;
   ctx->mlp_pad = (int)round_up(cfg->mlp_dim, 64);
   ctx->split = cfg->activation_precision == VIT_ACT_BF16X2 ? 2 : 1;
+  ctx->f8 = cfg->activation_precision == VIT_ACT_BF16F8;
   build_lut(*cfg, ctx->lut);
   ctx->norm_affine = verify_affine(*cfg, ctx->lut, &ctx->affine);
   *out = ctx;
@@ -715,7 +753,7 @@ vit_status vit_graph_launch_plan(vit_graph* g, const vit_plan* plan, void* strea
   const vit_config& b = cap->cfg;
   if (a.hidden != b.hidden || a.heads != b.heads || a.layers != b.layers || a.mlp_dim != b.mlp_dim ||
       a.window_px != b.window_px || a.out_dim != b.out_dim || plan->head_dim != cap->head_dim ||
-      plan->split != cap->split) {
+      plan->split != cap->split || plan->f8 != cap->f8) {
     set_error("plan was built for another tower configuration than the captured one");
     return VIT_E_ARG;
   }

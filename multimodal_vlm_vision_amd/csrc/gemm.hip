@@ -17,6 +17,18 @@
 // two MFMAs, so the pair costs twice the MFMA work but not twice the B
 // traffic.
 //
+// bf16 + e4m3 residual activations (A8 set): the same compensation with the
+// residual x - bf16(x) stored as OCP e4m3 (times 2^9, one byte) in a separate
+// fp8 matrix, multiplied against an e4m3 copy of the weights whose rows carry
+// power-of-two E8M0 scales.  gfx950's scaled fp8 MFMA (32x32x64, per-row A and
+// per-column B scales) adds that product into the same fp32 accumulators and
+// undoes both scales on the way, at about half the MFMA time of the second bf16
+// product; the residual's own error (e4m3's 3 mantissa bits on a term ~2^-9 of
+// x) stays ~2^-12 of x.  The fp8 MFMA takes 64 K per instruction: with a
+// 32-column stage, each stage's 32 residual bytes of a row fill half of the
+// operand (lanes 0-31 the first 16 bytes of both stages, lanes 32-63 the
+// second: A and B use the same mapping, so the products still pair equal k).
+//
 // Main loop (per workgroup tile BM x BN, 2x2 waves of (BM/2) x (BN/2)):
 //  * K advances 32 columns per stage.  Tiles move global -> LDS with gfx950's
 //    buffer loads into LDS (no VGPR staging): one 64-lane 16-byte load moves
@@ -46,6 +58,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "vit_internal.h"
 
@@ -55,6 +68,8 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 constexpr int BK = 32;             // logical K per stage: LDS rows of 64 bytes
 constexpr int CPR = BK / 8;        // 16-byte chunks per LDS row
@@ -103,15 +118,37 @@ __device__ __forceinline__ float4 f4add(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
+// four floats -> four OCP e4m3 bytes, round to nearest even (two v_cvt_pk_fp8_f32)
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// residual y - hi (exact in fp32) times 2^kLoShift, clamped to e4m3's finite range
+__device__ __forceinline__ float lo_scaled(float y, float hi) {
+  return fminf(fmaxf((y - hi) * (float)(1 << kLoShift), -448.0f), 448.0f);
+}
+
 // bf16 activation store into the blocked layout (ldo columns): hi = bf16(y) of the 8 columns
-// n..n+7 (one 16-byte chunk, n % 8 == 0); with split_off, lo = bf16(y - hi) at n + split_off.
+// n..n+7 (one 16-byte chunk, n % 8 == 0); with split_off, lo = bf16(y - hi) at n + split_off;
+// AM 2: the e4m3 residual of the 8 columns (8 bytes) into out8.
+template <int AM>
 __device__ __forceinline__ void store_act8(const GemmArgs& p, int m, int n, const float (&y)[8]) {
   uint16_t* o = static_cast<uint16_t*>(p.out);
   uint32_t hi[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) hi[i] = pack2(y[2 * i], y[2 * i + 1]);
   *reinterpret_cast<uint4*>(o + kt_index(m, n, p.ldo)) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  if (p.split_off) {
+  if constexpr (AM == 2) {
+    uint32_t l8[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      l8[i] = pack_e4m3x4(lo_scaled(y[4 * i], __builtin_bit_cast(float, hi[2 * i] << 16)),
+                          lo_scaled(y[4 * i + 1], __builtin_bit_cast(float, hi[2 * i] & 0xffff0000u)),
+                          lo_scaled(y[4 * i + 2], __builtin_bit_cast(float, hi[2 * i + 1] << 16)),
+                          lo_scaled(y[4 * i + 3], __builtin_bit_cast(float, hi[2 * i + 1] & 0xffff0000u)));
+    *reinterpret_cast<uint2*>(p.out8 + kt8_index(m, n, p.ldo8)) = make_uint2(l8[0], l8[1]);
+  } else if (p.split_off) {
     uint32_t lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -121,19 +158,27 @@ __device__ __forceinline__ void store_act8(const GemmArgs& p, int m, int n, cons
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT, int OCC = 1>
+// AM (activation mode): 0 single bf16, 1 hi+lo bf16 pairs, 2 bf16 + e4m3 residual
+template <int BM, int BN, int WM, int WN, int AM, int OCC = 1>
 struct Geo {
+  static constexpr bool SPLIT = AM == 1, F8 = AM == 2;
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = BN / WN / 32;
   static constexpr int AR = SPLIT ? 2 * BM : BM;        // A rows per stage: hi rows, then lo rows
   static constexpr int ROWS = AR + BN;
-  static constexpr int kStage = ROWS * BK;               // elements per stage
-  static constexpr int kStageBytes = kStage * 2;
+  static constexpr int kF8Off = ROWS * BK * 2;           // AM 2: e4m3 A8 then B8 rows (32 B) follow
+  static constexpr int NA8 = BM / 32, NB8 = BN / 32;     // AM 2: 1 KB e4m3 blocks per stage
+  static constexpr int kStageBytes = kF8Off + (F8 ? (BM + BN) * 32 : 0);
+  static constexpr int kStage = kStageBytes / 2;         // bf16 elements per stage
   static constexpr int LA = AR / RPL / NW;               // A loads per wave per stage
   static constexpr int LB = BN / RPL / NW;               // B loads per wave per stage
-  static constexpr int LPW = LA + LB;
+  // AM 2: e4m3 block loads per wave (a block count that does not split evenly over the waves
+  // is rounded up; the extra loads repeat the last block into its own slot)
+  static constexpr int LA8 = F8 ? (NA8 + NW - 1) / NW : 0;
+  static constexpr int LB8 = F8 ? (NB8 + NW - 1) / NW : 0;
+  static constexpr int LPW = LA + LB + LA8 + LB8;
   static constexpr int kBudget = kLdsBytes / OCC;          // OCC workgroups share a CU's LDS
   static constexpr int kFit = kBudget / kStageBytes;
   static constexpr int STAGES = kFit >= 4 ? 4 : kFit;
@@ -145,11 +190,12 @@ struct Geo {
   static_assert(AR % (RPL * NW) == 0 && BN % (RPL * NW) == 0, "load split");
   static_assert(kFit >= 2, "two stages must fit in LDS");
   static_assert(kSmem <= kBudget, "LDS budget");
+  static_assert(kStageBytes % 16 == 0 && LA8 <= 4 && LB8 <= 4, "e4m3 stage layout");
   static_assert((STAGES - 1) * LPW < 64, "vmcnt range");
 };
 
 // Applies the epilogue to one staged 32-row slice (rows m_base.., columns n_base.., width W = TN*32).
-template <int EPI, int W>
+template <int EPI, int W, int AM>
 __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const float* sc, int m_base, int n_base,
                                                int lane) {
   constexpr int SST = W + 8;
@@ -211,7 +257,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const f
           y[4 * h + 2] = silu(g.z) * u.z; y[4 * h + 3] = silu(g.w) * u.w;
         }
       }
-      store_act8(p, m, oc, y);
+      store_act8<AM>(p, m, oc, y);
     }
   } else if (EPI == EPI_QKV && n_base < 2 * p.hidden) {
     // q is stored times q_scale (the attention kernel's log2(e) / sqrt(head_dim)), applied
@@ -286,11 +332,13 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const f
 
 // DYN: M comes from device memory at run time (bucketed graphs); a separate instantiation, so
 // the plain path keeps M as a launch constant.
-template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI, int OCC, bool DYN>
+template <int BM, int BN, int WM, int WN, int AM, int EPI, int OCC, bool DYN>
 __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_kernel(GemmArgs p) {
-  using G = Geo<BM, BN, WM, WN, SPLIT, OCC>;
+  using G = Geo<BM, BN, WM, WN, AM, OCC>;
+  constexpr bool SPLIT = G::SPLIT, F8 = G::F8;
   constexpr int TM = G::TM, TN = G::TN, LA = G::LA, LB = G::LB, S = G::STAGES, AR = G::AR;
+  constexpr int LA8 = G::LA8, LB8 = G::LB8;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int lane = threadIdx.x & 63;
@@ -323,22 +371,47 @@ gemm_kernel(GemmArgs p) {
   const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.B), (short)0, (int)p.b_bytes,
                                                     kRsrcWord3);
   // (fixed-size arrays: a dependent bound here fails the host-side instantiation of the split
-  // variants with this clang; only the first LA / LB entries are used)
+  // variants with this clang; only the first LA / LB entries are used).  A load's offset is
+  // the wave-uniform byte offset of its block (scalar offset, with the K advance) plus the
+  // lane's 16 bytes (one vector offset shared by every load).
   static_assert(LA <= 16 && LB <= 16, "load plan");
   uint32_t offa[16], offb[16];
+  const uint32_t lane16 = (uint32_t)lane * 16;
   const int last_ga = (M + 15) / 16 - 1, last_gb = p.N / 16 - 1;
   const int64_t kba = p.lda / BK, kbb = p.ldb / BK;   // blocks per row group
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
     const int r = (wv * LA + j) * RPL;   // hi rows [0, BM), then lo rows [BM, 2BM)
     const int g = min((m0 + r % BM) / 16, last_ga);
-    offa[j] = (uint32_t)((g * kba + (r >= BM ? p.a_group / BK : 0)) * 1024 + lane * 16);
+    offa[j] = (uint32_t)((g * kba + (r >= BM ? p.a_group / BK : 0)) * 1024);
   }
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
     const int g = min((n0 + (wv * LB + j) * RPL) / 16, last_gb);
-    offb[j] = (uint32_t)(g * kbb * 1024 + lane * 16);
+    offb[j] = (uint32_t)(g * kbb * 1024);
   }
+  // AM 2: e4m3 blocks of 32 rows; wave wv's j-th load takes block min(wv * L + j, last) of
+  // the stage (A8 then B8), rows past M read the last 32-row group
+  uint32_t offa8[4], offb8[4], ldsa8[4], ldsb8[4];
+  if constexpr (F8) {
+    const int last_g8 = (M + 31) / 32 - 1;
+#pragma unroll
+    for (int j = 0; j < LA8; ++j) {
+      const int b = min(wv * LA8 + j, G::NA8 - 1);
+      offa8[j] = (uint32_t)(min((m0 + 32 * b) / 32, last_g8) * (p.lda8 / 32) * 1024);
+      ldsa8[j] = (uint32_t)(G::kF8Off + b * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < LB8; ++j) {
+      const int b = min(wv * LB8 + j, G::NB8 - 1);
+      offb8[j] = (uint32_t)(((n0 + 32 * b) / 32) * (p.ldb8 / 32) * 1024);
+      ldsb8[j] = (uint32_t)(G::kF8Off + (G::NA8 + b) * 1024);
+    }
+  }
+  const auto ra8 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(F8 ? p.A8 : nullptr), (short)0,
+                                                     (int)p.a8_bytes, kRsrcWord3);
+  const auto rb8 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(F8 ? p.B8 : nullptr), (short)0,
+                                                     (int)p.b8_bytes, kRsrcWord3);
   const int nk = p.K / BK;
   auto issue = [&](int kt, int buf) {
     kt = min(kt, nk - 1);   // past the end: reload the last stage into a free slot (never read)
@@ -350,12 +423,25 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < LA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(st + (wv * LA + j) * RPL * BK), 16, offa[j], ka, 0, 0);
+          ra, (__attribute__((address_space(3))) void*)(st + (wv * LA + j) * RPL * BK), 16, lane16, offa[j] + ka, 0, 0);
 #pragma unroll
     for (int j = 0; j < LB; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (__attribute__((address_space(3))) void*)(st + (AR + (wv * LB + j) * RPL) * BK), 16, offb[j], kb,
-          0, 0);
+          rb, (__attribute__((address_space(3))) void*)(st + (AR + (wv * LB + j) * RPL) * BK), 16, lane16,
+          offb[j] + kb, 0, 0);
+    if constexpr (F8) {
+      // K block kt of a 32-row group: 1 KB after block kt - 1
+      const uint32_t k8 = (uint32_t)kt * 1024;
+      uint8_t* st8 = reinterpret_cast<uint8_t*>(smem) + buf * G::kStageBytes;
+#pragma unroll
+      for (int j = 0; j < LA8; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra8, (__attribute__((address_space(3))) void*)(st8 + ldsa8[j]), 16,
+                                                 lane16, offa8[j] + k8, 0, 0);
+#pragma unroll
+      for (int j = 0; j < LB8; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb8, (__attribute__((address_space(3))) void*)(st8 + ldsb8[j]), 16,
+                                                 lane16, offb8[j] + k8, 0, 0);
+    }
   };
 
   f32x16 acc[TM][TN];
@@ -366,25 +452,21 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // fragment reads: 32x32x16 operand = 32 rows x 16 K; lane -> row lane & 31, chunk 2*kk + lane/32
+  // fragment reads: 32x32x16 operand = 32 rows x 16 K; lane -> row lane & 31, chunk 2*kk + lane/32.
+  // Fragment rows start at multiples of 32, so a row's chunk permutation (its bits 1-4) is
+  // that of lane & 31: one lane offset per kk, the fragment's row base a constant.
   bf16x8 fa[2][TM], fl[2][TM], fb[2][TN];
+  const int rl = lane & 31;
+  const int lofs[2] = {rl * BK + kt_chunk(rl, lane >> 5) * 8, rl * BK + kt_chunk(rl, 2 + (lane >> 5)) * 8};
   auto lfrag = [&](int buf, int kk, bf16x8 (&xa)[TM], bf16x8 (&xl)[TM], bf16x8 (&xb)[TN]) {
-    const uint16_t* st = smem + buf * G::kStage;
-    const int c = kk * 2 + (lane >> 5);
+    const uint16_t* st = smem + buf * G::kStage + lofs[kk];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int r = wm * TM * 32 + i * 32 + (lane & 31);
-      xa[i] = *reinterpret_cast<const bf16x8*>(st + r * BK + kt_chunk(r, c) * 8);
-      if constexpr (SPLIT) {
-        const int rl = BM + r;
-        xl[i] = *reinterpret_cast<const bf16x8*>(st + rl * BK + kt_chunk(rl, c) * 8);
-      }
+      xa[i] = *reinterpret_cast<const bf16x8*>(st + (wm * TM * 32 + i * 32) * BK);
+      if constexpr (SPLIT) xl[i] = *reinterpret_cast<const bf16x8*>(st + (BM + wm * TM * 32 + i * 32) * BK);
     }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int r = AR + wn * TN * 32 + j * 32 + (lane & 31);
-      xb[j] = *reinterpret_cast<const bf16x8*>(st + r * BK + kt_chunk(r, c) * 8);
-    }
+    for (int j = 0; j < TN; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(st + (AR + wn * TN * 32 + j * 32) * BK);
   };
   auto mfma_step = [&](const bf16x8 (&xa)[TM], const bf16x8 (&xl)[TM], const bf16x8 (&xb)[TN]) {
 #pragma unroll
@@ -410,6 +492,79 @@ gemm_kernel(GemmArgs p) {
   __builtin_amdgcn_s_barrier();
   lfrag(0, 0, fa[0], fl[0], fb[0]);
 
+  if constexpr (F8) {
+    // e4m3 operand halves: h[0] from an even stage, h[1] from the following odd one.  A stage's
+    // half is read right after the barrier that makes it visible (step 1 of the stage before),
+    // and the pair's fp8 MFMAs run in step 0 of the odd stage.
+    i32x4 ha[2][TM], hb[2][TN];
+    // lane -> row lane & 31 of a 32-row block, chunk lane / 32 (swapped when row bit 3 is set)
+    const int lofs8 = rl * 32 + ((((lane >> 5) ^ (rl >> 3)) & 1) << 4);
+    auto lfrag8 = [&](int buf, i32x4 (&xa)[TM], i32x4 (&xb)[TN]) {
+      const uint8_t* s8 = reinterpret_cast<const uint8_t*>(smem) + buf * G::kStageBytes + G::kF8Off + lofs8;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) xa[i] = *reinterpret_cast<const i32x4*>(s8 + (wm * TM + i) * 1024);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) xb[j] = *reinterpret_cast<const i32x4*>(s8 + (G::NA8 + wn * TN + j) * 1024);
+    };
+    // E8M0 scales: A rows 2^-kLoShift, B column n (this lane's column of tile j) 2^(s[n] - 127)
+    constexpr int kScaleA = 127 - kLoShift;
+    int sb[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] = p.b8_scale[n0 + wn * TN * 32 + j * 32 + (lane & 31)];
+    auto mfma8 = [&]() {
+      i32x8 bv[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bv[j] = __builtin_shufflevector(hb[0][j], hb[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const i32x8 av = __builtin_shufflevector(ha[0][i], ha[1][i], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[j], acc[i][j], 0, 0, 0, kScaleA, 0,
+                                                                     sb[j]);
+      }
+    };
+    constexpr int NMF1 = TM * TN;                // bf16 MFMAs of step 1
+    constexpr int NDS1 = 2 * (TM + TN);          // step 1 reads: bf16 and e4m3 fragments
+    lfrag8(0, ha[0], hb[0]);
+    auto stage = [&](int kt, auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const int buf = kt % S;
+      lfrag(buf, 1, fa[1], fl[1], fb[1]);
+      mfma_step(fa[0], fl[0], fb[0]);
+      if constexpr (h == 1) mfma8();
+#pragma unroll
+      for (int i = 0; i < NDS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF * (h + 1), 0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<(S - 2) * G::LPW>();
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      lfrag((kt + 1) % S, 0, fa[0], fl[0], fb[0]);
+      lfrag8((kt + 1) % S, ha[1 - h], hb[1 - h]);
+      issue(kt + S, buf);
+      mfma_step(fa[1], fl[1], fb[1]);
+#pragma unroll
+      for (int i = 0; i < (NDS1 + 1) / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < (G::LPW + 1) / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      stage(kt, std::integral_constant<int, 0>{});
+      stage(kt + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt % S;
     // step 0: MFMAs on K columns [0,16) of stage kt while reading columns [16,32)
@@ -447,6 +602,7 @@ gemm_kernel(GemmArgs p) {
     __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
+  }
   // drain the (redundant) trailing loads before the ring is reused for the epilogue
   wait_vm<0>();
   __syncthreads();
@@ -463,7 +619,7 @@ gemm_kernel(GemmArgs p) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sc[(8 * (e / 4) + lr + (e % 4)) * G::SST + j * 32 + lc] = acc[i][j][e];
-    epilogue_slice<EPI, TN * 32>(p, M, sc, m0 + wm * TM * 32 + i * 32, n0 + wn * TN * 32, lane);
+    epilogue_slice<EPI, TN * 32, AM>(p, M, sc, m0 + wm * TM * 32 + i * 32, n0 + wn * TN * 32, lane);
   }
 }
 
@@ -483,48 +639,48 @@ constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 128, 1, 1.0},   // (order used by
                              {CFG_O, 128, 256, 128, 2, 1.1},
                              {CFG_S, 64, 64, 64, 1, 0.3}};
 
-template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI, int OCC = 1>
+template <int BM, int BN, int WM, int WN, int AM, int EPI, int OCC = 1>
 hipError_t run(const GemmArgs& a, hipStream_t st) {
-  using G = Geo<BM, BN, WM, WN, SPLIT, OCC>;
+  using G = Geo<BM, BN, WM, WN, AM, OCC>;
   const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (a.m_dev)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC, true>), dim3((unsigned)tiles), dim3(G::NT),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, AM, EPI, OCC, true>), dim3((unsigned)tiles), dim3(G::NT),
                        G::kSmem, st, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC, false>), dim3((unsigned)tiles), dim3(G::NT),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, AM, EPI, OCC, false>), dim3((unsigned)tiles), dim3(G::NT),
                        G::kSmem, st, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI, int OCC = 1>
+template <int BM, int BN, int WM, int WN, int AM, int EPI, int OCC = 1>
 hipError_t allow_smem() {
-  using G = Geo<BM, BN, WM, WN, SPLIT, OCC>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC, false>),
+  using G = Geo<BM, BN, WM, WN, AM, OCC>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, AM, EPI, OCC, false>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, SPLIT, EPI, OCC, true>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, AM, EPI, OCC, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
   return e;
 }
 
-template <bool SPLIT, int EPI>
+template <int AM, int EPI>
 hipError_t allow_smem_all() {
-  hipError_t e = allow_smem<256, 256, 2, 2, SPLIT, EPI>();
-  if (e == hipSuccess) e = allow_smem<192, 256, 2, 2, SPLIT, EPI>();
-  if (e == hipSuccess) e = allow_smem<128, 256, 2, 2, SPLIT, EPI>();
-  if (e == hipSuccess) e = allow_smem<128, 256, 2, 2, SPLIT, EPI, 2>();
-  if (e == hipSuccess) e = allow_smem<64, 64, 2, 1, SPLIT, EPI>();
+  hipError_t e = allow_smem<256, 256, 2, 2, AM, EPI>();
+  if (e == hipSuccess) e = allow_smem<192, 256, 2, 2, AM, EPI>();
+  if (e == hipSuccess) e = allow_smem<128, 256, 2, 2, AM, EPI>();
+  if (e == hipSuccess) e = allow_smem<128, 256, 2, 2, AM, EPI, 2>();
+  if (e == hipSuccess) e = allow_smem<64, 64, 2, 1, AM, EPI>();
   return e;
 }
 
-template <bool SPLIT, int EPI>
+template <int AM, int EPI>
 hipError_t run_cfg(int cfg, const GemmArgs& a, hipStream_t st) {
   switch (cfg) {
-    case CFG_L: return run<256, 256, 2, 2, SPLIT, EPI>(a, st);
-    case CFG_T: return run<192, 256, 2, 2, SPLIT, EPI>(a, st);
-    case CFG_H: return run<128, 256, 2, 2, SPLIT, EPI>(a, st);
-    case CFG_O: return run<128, 256, 2, 2, SPLIT, EPI, 2>(a, st);
-    default: return run<64, 64, 2, 1, SPLIT, EPI>(a, st);
+    case CFG_L: return run<256, 256, 2, 2, AM, EPI>(a, st);
+    case CFG_T: return run<192, 256, 2, 2, AM, EPI>(a, st);
+    case CFG_H: return run<128, 256, 2, 2, AM, EPI>(a, st);
+    case CFG_O: return run<128, 256, 2, 2, AM, EPI, 2>(a, st);
+    default: return run<64, 64, 2, 1, AM, EPI>(a, st);
   }
 }
 
@@ -542,7 +698,7 @@ int pick_cfg(int epi, const GemmArgs& a) {
   const CfgInfo& o = kCfgs[3];
   const CfgInfo& t = kCfgs[1];
   if (fits(o) && tiles_of(o) >= 256.0) {
-    const int k_eff = a.K * (a.a_group > 0 ? 2 : 1);
+    const int k_eff = a.K * (a.a_group > 0 || a.A8 ? 2 : 1);   // compensated products: two MFMA passes' worth
     const double t_fill = tiles_of(t) / (256.0 * std::ceil(tiles_of(t) / 256.0));
     if (k_eff >= 8192 && fits(t) && t_fill >= 0.85) return t.cfg;
     return o.cfg;
@@ -565,35 +721,41 @@ int pick_cfg(int epi, const GemmArgs& a) {
   return best;
 }
 
-template <bool SPLIT>
+template <int AM>
 hipError_t dispatch(int epi, int cfg, const GemmArgs& a, hipStream_t st, bool* bad_epi) {
   switch (epi) {
-    case EPI_F32: return run_cfg<SPLIT, EPI_F32>(cfg, a, st);
-    case EPI_RES: return run_cfg<SPLIT, EPI_RES>(cfg, a, st);
-    case EPI_GELU: return run_cfg<SPLIT, EPI_GELU>(cfg, a, st);
-    case EPI_SWIGLU: return run_cfg<SPLIT, EPI_SWIGLU>(cfg, a, st);
-    case EPI_QKV: return run_cfg<SPLIT, EPI_QKV>(cfg, a, st);
-    case EPI_OUT: return run_cfg<SPLIT, EPI_OUT>(cfg, a, st);
-    default: *bad_epi = true; return hipSuccess;
+    case EPI_F32:   // (not built for compensated activations: no product of the tower has it)
+      if constexpr (AM == 2) break;
+      else return run_cfg<AM, EPI_F32>(cfg, a, st);
+    case EPI_RES: return run_cfg<AM, EPI_RES>(cfg, a, st);
+    case EPI_GELU: return run_cfg<AM, EPI_GELU>(cfg, a, st);
+    case EPI_SWIGLU: return run_cfg<AM, EPI_SWIGLU>(cfg, a, st);
+    case EPI_QKV: return run_cfg<AM, EPI_QKV>(cfg, a, st);
+    case EPI_OUT: return run_cfg<AM, EPI_OUT>(cfg, a, st);
+    default: break;
   }
+  *bad_epi = true;
+  return hipSuccess;
 }
 
-template <bool SPLIT>
+template <int AM>
 hipError_t allow_all() {
-  hipError_t e = allow_smem_all<SPLIT, EPI_F32>();
-  if (e == hipSuccess) e = allow_smem_all<SPLIT, EPI_RES>();
-  if (e == hipSuccess) e = allow_smem_all<SPLIT, EPI_GELU>();
-  if (e == hipSuccess) e = allow_smem_all<SPLIT, EPI_SWIGLU>();
-  if (e == hipSuccess) e = allow_smem_all<SPLIT, EPI_QKV>();
-  if (e == hipSuccess) e = allow_smem_all<SPLIT, EPI_OUT>();
+  hipError_t e = hipSuccess;
+  if constexpr (AM != 2) e = allow_smem_all<AM, EPI_F32>();
+  if (e == hipSuccess) e = allow_smem_all<AM, EPI_RES>();
+  if (e == hipSuccess) e = allow_smem_all<AM, EPI_GELU>();
+  if (e == hipSuccess) e = allow_smem_all<AM, EPI_SWIGLU>();
+  if (e == hipSuccess) e = allow_smem_all<AM, EPI_QKV>();
+  if (e == hipSuccess) e = allow_smem_all<AM, EPI_OUT>();
   return e;
 }
 
 }  // namespace
 
 vit_status prepare_gemm_kernels() {
-  hipError_t e = allow_all<false>();
-  if (e == hipSuccess) e = allow_all<true>();
+  hipError_t e = allow_all<0>();
+  if (e == hipSuccess) e = allow_all<1>();
+  if (e == hipSuccess) e = allow_all<2>();
   if (e != hipSuccess) {
     set_error("gemm LDS attribute: %s", hipGetErrorString(e));
     return VIT_E_HIP;
@@ -605,6 +767,7 @@ vit_status launch_gemm(int epi, const GemmArgs& in, void* stream) {
   if (in.M <= 0) return VIT_OK;
   GemmArgs a = in;
   const bool split = a.a_group > 0;
+  const bool f8 = a.A8 != nullptr;
   const int64_t a_cols = split ? 2 * (int64_t)a.K : a.K;
   const bool bf16_out = epi == EPI_GELU || epi == EPI_SWIGLU;
   if (a.N % 64 || a.K % BK || a.K <= 0 || a.lda % BK || a.ldb % BK || a.lda < a_cols || a.ldb < a.K ||
@@ -612,6 +775,17 @@ vit_status launch_gemm(int epi, const GemmArgs& in, void* stream) {
       (split && (a.a_group % BK || a.K % a.a_group))) {
     set_error("gemm: unsupported shape M=%d N=%d K=%d group=%d (N a multiple of 64; K, the hi/lo group and "
               "the blocked operand widths multiples of 32)", a.M, a.N, a.K, a.a_group);
+    return VIT_E_ARG;
+  }
+  if (f8 && (split || !a.B8 || !a.b8_scale || a.K % 64 || a.lda8 % BK || a.ldb8 % BK || a.lda8 < a.K ||
+             a.ldb8 < a.K || (bf16_out && (!a.out8 || a.ldo8 % BK)) || (!bf16_out && a.out8) || epi == EPI_F32)) {
+    set_error("gemm: e4m3 residual operands need B8, its scales, K a multiple of 64, fp8 widths multiples of 32 "
+              "and an e4m3 output exactly for the GELU / SwiGLU epilogues (M=%d N=%d K=%d epi %d)", a.M, a.N,
+              a.K, epi);
+    return VIT_E_ARG;
+  }
+  if (!f8 && a.out8) {
+    set_error("gemm: an e4m3 residual output needs e4m3 residual inputs");
     return VIT_E_ARG;
   }
   // byte extents of the blocked operands (rows padded to 16), addressed with 32-bit buffer offsets
@@ -623,6 +797,15 @@ vit_status launch_gemm(int epi, const GemmArgs& in, void* stream) {
   }
   a.a_bytes = (uint32_t)a_bytes;
   a.b_bytes = (uint32_t)b_bytes;
+  if (f8) {   // e4m3 rows padded to 32
+    const int64_t a8 = round_up(a.M, 32) * a.lda8, b8 = (int64_t)a.N * a.ldb8;
+    if (a8 >= (int64_t)1 << 31 || b8 >= (int64_t)1 << 31) {
+      set_error("gemm: e4m3 operand larger than 2 GiB (M=%d N=%d K=%d)", a.M, a.N, a.K);
+      return VIT_E_ARG;
+    }
+    a.a8_bytes = (uint32_t)a8;
+    a.b8_bytes = (uint32_t)b8;
+  }
   const int cfg = pick_cfg(epi, a);
   if (cfg < 0) {
     set_error("gemm: no tile configuration for N=%d (epilogue %d)", a.N, epi);
@@ -639,7 +822,9 @@ vit_status launch_gemm(int epi, const GemmArgs& in, void* stream) {
   a.group_m = (ci->occ == 1 && gn <= 8) ? std::max(1, 32 / gn) : 8;
   hipStream_t st = static_cast<hipStream_t>(stream);
   bool bad_epi = false;
-  const hipError_t e = split ? dispatch<true>(epi, cfg, a, st, &bad_epi) : dispatch<false>(epi, cfg, a, st, &bad_epi);
+  const hipError_t e = f8      ? dispatch<2>(epi, cfg, a, st, &bad_epi)
+                      : split ? dispatch<1>(epi, cfg, a, st, &bad_epi)
+                              : dispatch<0>(epi, cfg, a, st, &bad_epi);
   if (bad_epi) {
     set_error("gemm: bad epilogue %d", epi);
     return VIT_E_ARG;

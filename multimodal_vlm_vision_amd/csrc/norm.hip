@@ -36,14 +36,25 @@ __device__ __forceinline__ float bf16_lo(float x) {
   return x - (float)(__bf16)x;
 }
 
-// VPL = float4 chunks per lane (d <= 256 * VPL).  SPLIT: each output row is
-// [hi | lo] with hi = bf16(y) and lo = bf16(y - hi).  Input row `row` lands in blocked row
+// residual x - bf16(x) times 2^kLoShift, clamped to e4m3's finite range, for four values -> four
+// OCP e4m3 bytes (round to nearest even)
+__device__ __forceinline__ uint32_t lo_e4m3x4(float4 y) {
+  constexpr float s = (float)(1 << kLoShift);
+  auto f = [](float x) { return fminf(fmaxf(bf16_lo(x) * s, -448.0f), 448.0f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f(y.x), f(y.y), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f(y.z), f(y.w), lo, true);
+}
+
+// VPL = float4 chunks per lane (d <= 256 * VPL).  AM 1: each output row is [hi | lo] with
+// hi = bf16(y) and lo = bf16(y - hi); AM 2: hi rows, and the e4m3 residuals (times
+// 2^kLoShift) at the same place of out8 (kt8_index).  Input row `row` lands in blocked row
 // row / group at column offset (row % group) * S * d of a group * S * d wide matrix.
-template <int KIND, int VPL, bool SPLIT, bool DYN>
+template <int KIND, int VPL, int AM, bool DYN>
 __global__ void __launch_bounds__(kThreads)
 rownorm_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __restrict__ rows_dev, int d,
                const float* __restrict__ g, const float* __restrict__ b, float eps, int group,
-               uint16_t* __restrict__ out) {
+               uint16_t* __restrict__ out, uint8_t* __restrict__ out8) {
+  constexpr bool SPLIT = AM == 1;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= (DYN ? (int64_t)*rows_dev : rows)) return;   // DYN: run-time count (bucketed graph)
@@ -93,6 +104,7 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __restr
       if (SPLIT)
         *reinterpret_cast<uint2*>(out + kt_index(orow, ocol + d + 4 * c, ocols)) =
             make_uint2(pack_bf16(bf16_lo(y.x), bf16_lo(y.y)), pack_bf16(bf16_lo(y.z), bf16_lo(y.w)));
+      if (AM == 2) *reinterpret_cast<uint32_t*>(out8 + kt8_index(orow, ocol + 4 * c, ocols)) = lo_e4m3x4(y);
     }
   }
 }
@@ -100,10 +112,12 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __restr
 // Two rows per wave (rows 2w, 2w + 1 of a 16-row group share each 128-byte line of the blocked
 // layout): lanes 0-31 take the even row, lanes 32-63 the odd one, so every store instruction
 // writes whole lines.  VPL2 = float4 chunks per lane per row (d <= 128 * VPL2).
-template <int KIND, int VPL2, bool SPLIT, bool DYN>
+template <int KIND, int VPL2, int AM, bool DYN>
 __global__ void __launch_bounds__(kThreads)
 rownorm2_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __restrict__ rows_dev, int d,
-                const float* __restrict__ g, const float* __restrict__ b, float eps, uint16_t* __restrict__ out) {
+                const float* __restrict__ g, const float* __restrict__ b, float eps, uint16_t* __restrict__ out,
+                uint8_t* __restrict__ out8) {
+  constexpr bool SPLIT = AM == 1;
   const int lane = threadIdx.x & 63, hl = lane >> 5, c32 = lane & 31;
   const int64_t row = ((int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6)) * 2 + hl;
   const int64_t nrows = DYN ? (int64_t)*rows_dev : rows;
@@ -158,32 +172,33 @@ rownorm2_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __rest
       if (SPLIT)
         *reinterpret_cast<uint2*>(out + kt_index(row, d + 4 * c, w)) =
             make_uint2(pack_bf16(bf16_lo(y.x), bf16_lo(y.y)), pack_bf16(bf16_lo(y.z), bf16_lo(y.w)));
+      if (AM == 2) *reinterpret_cast<uint32_t*>(out8 + kt8_index(row, 4 * c, d)) = lo_e4m3x4(y);
     }
   }
 }
 
-template <int KIND, bool SPLIT>
+template <int KIND, int AM>
 vit_status launch_kind(const float* r, int64_t rows, const int32_t* rows_dev, int d, const float* g,
-                       const float* b, float eps, int group, uint16_t* out, hipStream_t st) {
+                       const float* b, float eps, int group, uint16_t* out, uint8_t* out8, hipStream_t st) {
   if (group == 1 && d == 1280) {   // the tower's width: two rows per wave
     const dim3 grid2((unsigned)((rows + 2 * kRowsPerBlock - 1) / (2 * kRowsPerBlock)));
     if (rows_dev)
-      hipLaunchKernelGGL((rownorm2_kernel<KIND, 10, SPLIT, true>), grid2, dim3(kThreads), 0, st, r, rows, rows_dev,
-                         d, g, b, eps, out);
+      hipLaunchKernelGGL((rownorm2_kernel<KIND, 10, AM, true>), grid2, dim3(kThreads), 0, st, r, rows, rows_dev,
+                         d, g, b, eps, out, out8);
     else
-      hipLaunchKernelGGL((rownorm2_kernel<KIND, 10, SPLIT, false>), grid2, dim3(kThreads), 0, st, r, rows, rows_dev,
-                         d, g, b, eps, out);
+      hipLaunchKernelGGL((rownorm2_kernel<KIND, 10, AM, false>), grid2, dim3(kThreads), 0, st, r, rows, rows_dev,
+                         d, g, b, eps, out, out8);
     return VIT_OK;
   }
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   const int vpl = (d / 4 + 63) / 64;
 #define VIT_ROWNORM(V)                                                                                  \
   if (rows_dev)                                                                                         \
-    hipLaunchKernelGGL((rownorm_kernel<KIND, V, SPLIT, true>), grid, dim3(kThreads), 0, st, r, rows,    \
-                       rows_dev, d, g, b, eps, group, out);                                             \
+    hipLaunchKernelGGL((rownorm_kernel<KIND, V, AM, true>), grid, dim3(kThreads), 0, st, r, rows,       \
+                       rows_dev, d, g, b, eps, group, out, out8);                                       \
   else                                                                                                  \
-    hipLaunchKernelGGL((rownorm_kernel<KIND, V, SPLIT, false>), grid, dim3(kThreads), 0, st, r, rows,   \
-                       rows_dev, d, g, b, eps, group, out);
+    hipLaunchKernelGGL((rownorm_kernel<KIND, V, AM, false>), grid, dim3(kThreads), 0, st, r, rows,      \
+                       rows_dev, d, g, b, eps, group, out, out8);
   if (vpl <= 1) {
     VIT_ROWNORM(1)
   } else if (vpl <= 2) {
@@ -213,7 +228,45 @@ unblock_kernel(const uint16_t* __restrict__ src, int64_t rows, int cols, int gro
   *reinterpret_cast<uint2*>(dst + m * out_cols + c) = *reinterpret_cast<const uint2*>(src + s);
 }
 
+// Debug copy of a bf16 + e4m3-residual activation: row m -> [hi(out_cols) | residual(out_cols)]
+// as bf16, the residual decoded (v_cvt_f32_fp8) and scaled back by 2^-kLoShift (exact in bf16).
+__global__ void __launch_bounds__(kThreads)
+unblock_f8_kernel(const uint16_t* __restrict__ src, const uint8_t* __restrict__ src8, int64_t rows, int cols,
+                  int group, int out_cols, uint16_t* __restrict__ dst) {
+  const int q4 = out_cols / 4;
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= rows * q4) return;
+  const int64_t m = j / q4;
+  const int c = (int)(j % q4) * 4;
+  const int64_t ld = (int64_t)group * cols, rr = m / group, cc = (m % group) * cols + c;
+  uint16_t* o = dst + m * 2 * out_cols;
+  *reinterpret_cast<uint2*>(o + c) = *reinterpret_cast<const uint2*>(src + kt_index(rr, cc, ld));
+  const int v = *reinterpret_cast<const int*>(src8 + kt8_index(rr, cc, ld));
+  constexpr float s = 1.0f / (float)(1 << kLoShift);
+  *reinterpret_cast<uint2*>(o + out_cols + c) =
+      make_uint2(pack_bf16(__builtin_amdgcn_cvt_f32_fp8(v, 0) * s, __builtin_amdgcn_cvt_f32_fp8(v, 1) * s),
+                 pack_bf16(__builtin_amdgcn_cvt_f32_fp8(v, 2) * s, __builtin_amdgcn_cvt_f32_fp8(v, 3) * s));
+}
+
 }  // namespace
+
+vit_status launch_unblock_f8(const uint16_t* src, const uint8_t* src8, int64_t rows, int cols, int group,
+                             int out_cols, uint16_t* dst, void* stream) {
+  if (rows <= 0) return VIT_OK;
+  if (cols % 32 || out_cols % 4 || out_cols > cols || group < 1) {
+    set_error("unblock_f8: bad shape cols=%d out_cols=%d group=%d", cols, out_cols, group);
+    return VIT_E_ARG;
+  }
+  const int64_t blocks = (rows * (out_cols / 4) + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(unblock_f8_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), src, src8, rows, cols, group, out_cols, dst);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("unblock_f8 launch: %s", hipGetErrorString(e));
+    return VIT_E_HIP;
+  }
+  return VIT_OK;
+}
 
 vit_status launch_unblock(const uint16_t* src, int64_t rows, int cols, int group, int out_cols,
                           uint16_t* dst, void* stream) {
@@ -235,21 +288,22 @@ vit_status launch_unblock(const uint16_t* src, int64_t rows, int cols, int group
 
 vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
                           const float* b, float eps, uint16_t* out, bool split, int group,
-                          void* stream, const int32_t* rows_dev) {
+                          void* stream, const int32_t* rows_dev, uint8_t* out8) {
   if (rows <= 0) return VIT_OK;
-  if (d % 32 || group < 1 || rows % group) {
-    set_error("rownorm: hidden %d must be a multiple of 32 and rows %lld a multiple of the group %d", d,
-              (long long)rows, group);
+  if (d % 32 || group < 1 || rows % group || (split && out8)) {
+    set_error("rownorm: hidden %d must be a multiple of 32 and rows %lld a multiple of the group %d "
+              "(and at most one of split / out8)", d, (long long)rows, group);
     return VIT_E_ARG;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int am = out8 ? 2 : split ? 1 : 0;
   vit_status s;
-  if (kind == VIT_NORM_LAYER)
-    s = split ? launch_kind<VIT_NORM_LAYER, true>(r, rows, rows_dev, d, g, b, eps, group, out, st)
-              : launch_kind<VIT_NORM_LAYER, false>(r, rows, rows_dev, d, g, b, eps, group, out, st);
-  else
-    s = split ? launch_kind<VIT_NORM_RMS, true>(r, rows, rows_dev, d, g, b, eps, group, out, st)
-              : launch_kind<VIT_NORM_RMS, false>(r, rows, rows_dev, d, g, b, eps, group, out, st);
+#define VIT_NORM_AM(K)                                                                   \
+  (am == 2   ? launch_kind<K, 2>(r, rows, rows_dev, d, g, b, eps, group, out, out8, st) \
+   : am == 1 ? launch_kind<K, 1>(r, rows, rows_dev, d, g, b, eps, group, out, out8, st) \
+             : launch_kind<K, 0>(r, rows, rows_dev, d, g, b, eps, group, out, out8, st))
+  s = kind == VIT_NORM_LAYER ? VIT_NORM_AM(VIT_NORM_LAYER) : VIT_NORM_AM(VIT_NORM_RMS);
+#undef VIT_NORM_AM
   if (s != VIT_OK) return s;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -68,6 +68,7 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   p->head_dim = ctx->head_dim;
   p->mlp_pad = ctx->mlp_pad;
   p->split = ctx->split;
+  p->f8 = ctx->f8;
   if (n_items < 0) {
     set_error("n_items must be >= 0 (got %d)", n_items);
     return VIT_E_ARG;
@@ -218,6 +219,11 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   p->off_vt = take((size_t)p->vt_ld * d * 2);
   p->off_o = take((size_t)Np * d * 2);
   p->off_f = take((size_t)std::max(Np * S * p->mlp_pad, Up * 4 * S * d) * 2);
+  if (p->f8) {   // e4m3 residuals of H and F: rows padded to whole 32-row groups
+    const int64_t N32 = round_up(N, 32), U32 = round_up(N / 4, 32);
+    p->off_h8 = take((size_t)std::max(N32 * d, U32 * 4 * d));
+    p->off_f8 = take((size_t)std::max(N32 * p->mlp_pad, U32 * 4 * d));
+  }
   p->off_pix = take(px);
   p->off_out = take((size_t)p->n_units * c.out_dim * 4);
   p->ws_bytes = off;

@@ -42,8 +42,24 @@ constexpr int64_t kt_index(int64_t r, int64_t c, int64_t cols) {
           ((int64_t)kt_chunk(r, (int)((c >> 3) & 3)) << 3) | (c & 7));
 }
 
+// fp8 (OCP E4M3) matrices -- the residuals x - bf16(x) of the compensated activations and the
+// weights' e4m3 copies -- use 1 KB blocks of 32 rows x 32 one-byte columns, ordered like
+// kt_index (32-row group, then column block); inside a block row r takes 32 bytes and its two
+// 16-byte chunks swap places when bit 3 of r is set, so a fragment read (32 consecutive rows,
+// one chunk each) touches distinct banks in every 16-lane group.  Rows are padded to 32.
+constexpr int64_t kt8_index(int64_t r, int64_t c, int64_t cols) {
+  return ((((r >> 5) * (cols >> 5) + (c >> 5)) << 10) | ((r & 31) << 5) |
+          ((((c >> 4) ^ (r >> 3)) & 1) << 4) | (c & 15));
+}
+// The residuals are stored times 2^kLoShift: |x - bf16(x)| <= 2^-8 |x|, so they stay within
+// e4m3's maximum (448) for |x| <= 224 (larger ones saturate), and where they fall into e4m3's
+// subnormal range their absolute error is at most 2^-10 * 2^-kLoShift = 2^-19.
+constexpr int kLoShift = 9;
+
 // bfloat16 round-to-nearest-even of a float, as raw bits (host side).
 uint16_t f32_to_bf16_bits(float f);
+// OCP E4M3 round-to-nearest-even of a float, saturating at +-448, as raw bits (host side).
+uint8_t f32_to_e4m3_bits(float f);
 
 // ---------------------------------------------------------------- device-side records
 
@@ -107,6 +123,11 @@ struct LayerW {
   const uint16_t* proj_w = nullptr; const float* proj_b = nullptr;  // [d][d]
   const uint16_t* fc1_w = nullptr;  const float* fc1_b = nullptr;   // GELU [mlp_pad][d]; SwiGLU [2*mlp_pad][d]
   const uint16_t* fc2_w = nullptr;  const float* fc2_b = nullptr;   // [d][mlp_pad]
+  // VIT_ACT_BF16F8: e4m3 copies of the weights that multiply compensated activations
+  // (kt8_index layout, same shapes) and their per-row E8M0 scales (row n holds W[n] * 2^(127 - s[n]))
+  const uint8_t* qkv_w8 = nullptr;  const uint8_t* qkv_s8 = nullptr;
+  const uint8_t* fc1_w8 = nullptr;  const uint8_t* fc1_s8 = nullptr;
+  const uint8_t* fc2_w8 = nullptr;  const uint8_t* fc2_s8 = nullptr;
 };
 
 struct DeviceWeights {
@@ -118,6 +139,8 @@ struct DeviceWeights {
   const float *mq_g = nullptr, *mq_b = nullptr;
   const uint16_t* m1_w = nullptr; const float* m1_b = nullptr;   // [4d][4d]
   const uint16_t* m2_w = nullptr; const float* m2_b = nullptr;   // [out][4d]
+  const uint8_t* m1_w8 = nullptr; const uint8_t* m1_s8 = nullptr;   // VIT_ACT_BF16F8 copies
+  const uint8_t* m2_w8 = nullptr; const uint8_t* m2_s8 = nullptr;
 };
 
 }  // namespace vitmi
@@ -127,6 +150,7 @@ struct vit_ctx {
   int head_dim = 0;
   int mlp_pad = 0;       // mlp_dim rounded up to 64
   int split = 1;         // 2 with hi+lo activation pairs, else 1
+  bool f8 = false;       // compensated activations as bf16 + e4m3 residual (VIT_ACT_BF16F8)
   uint16_t lut[3][256];  // bf16 bits of ((x/255) - mean_c) / std_c, exactly rounded
   bool norm_affine = false;     // fma(x, a_c, b_c) verified equal to lut for every byte
   vitmi::NormAffine affine{};
@@ -140,6 +164,7 @@ struct vit_ctx {
 struct vit_plan {
   vit_config cfg{};
   int head_dim = 0, mlp_pad = 0, split = 1;
+  bool f8 = false;
   int32_t n_items = 0;
   std::vector<int32_t> grid;      // [n][3]
   std::vector<int32_t> nframes;   // [n]
@@ -160,6 +185,7 @@ struct vit_plan {
 
   // workspace layout (byte offsets; all 256-byte aligned)
   size_t off_x = 0, off_r = 0, off_h = 0, off_q = 0, off_k = 0, off_vt = 0, off_o = 0, off_f = 0;
+  size_t off_h8 = 0, off_f8 = 0;  // e4m3 residuals of H and F (VIT_ACT_BF16F8)
   size_t off_pix = 0, off_out = 0, ws_bytes = 0;
   int64_t vt_ld = 0;              // V^T row pitch (tokens), N rounded up to 8
 };
@@ -221,6 +247,16 @@ struct GemmArgs {
   const int32_t* row_map = nullptr;
   // GELU / SwiGLU: when nonzero, also store lo = bf16(y - bf16(y)) at column + split_off
   int split_off = 0;
+  // Compensated activations as bf16 + e4m3 residual (A8 set, a_group 0): the product is
+  // sum_k (A[m][k] + 2^-kLoShift A8[m][k]) * B[n][k], the residual term taken against B8 =
+  // e4m3(B[n][k] * 2^(127 - b8_scale[n])) with the scaled fp8 MFMA.  K a multiple of 64.
+  const uint8_t* A8 = nullptr; int64_t lda8 = 0;   // kt8_index [M][lda8], rows padded to 32
+  const uint8_t* B8 = nullptr; int64_t ldb8 = 0;   // kt8_index [N][ldb8]
+  const uint8_t* b8_scale = nullptr;               // [N] E8M0 bytes
+  uint32_t a8_bytes = 0, b8_bytes = 0;             // (set by launch_gemm)
+  // GELU / SwiGLU with A8 mode outputs: the e4m3 residual of each stored activation, times
+  // 2^kLoShift, into a kt8_index matrix of ldo8 columns
+  uint8_t* out8 = nullptr; int64_t ldo8 = 0;
 };
 
 vit_status launch_gemm(int epi, const GemmArgs& a, void* stream);
@@ -238,14 +274,20 @@ vit_status launch_normrows_u8(const uint8_t* patches, int64_t n_rows, const uint
 // [hi(d) | lo(d)].  group > 1 stores `group` consecutive rows as one row of group * S * d
 // columns (the merger's view of 2x2 patch blocks).
 // rows_dev (optional): row count read at run time; rows is then the capacity.
+// out8 (instead of split): bf16 rows plus their e4m3 residuals (times 2^kLoShift) in a
+// kt8_index matrix of the same view.
 vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
                           const float* b, float eps, uint16_t* out, bool split, int group,
-                          void* stream, const int32_t* rows_dev = nullptr);
+                          void* stream, const int32_t* rows_dev = nullptr, uint8_t* out8 = nullptr);
 // Blocked bf16 matrix -> row-major [rows][out_cols] (debug copies): row m of the result is
 // row m / group, columns (m % group) * cols + [0, out_cols) of a blocked matrix with
 // group * cols columns.
 vit_status launch_unblock(const uint16_t* src, int64_t rows, int cols, int group, int out_cols,
                           uint16_t* dst, void* stream);
+// Debug copy of a compensated activation in the bf16 + e4m3 form: row m of dst (2 * out_cols
+// bf16) = [hi | residual], the residual converted exactly to bf16 (e4m3 value * 2^-kLoShift).
+vit_status launch_unblock_f8(const uint16_t* src, const uint8_t* src8, int64_t rows, int cols, int group,
+                             int out_cols, uint16_t* dst, void* stream);
 
 struct AttnArgs {
   const uint16_t* q = nullptr; const uint16_t* k = nullptr; const uint16_t* vt = nullptr;

@@ -10,6 +10,7 @@
 //  - the patch-embed K (1176) and the MLP width are zero-padded to multiples of 64.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -24,6 +25,28 @@ uint16_t f32_to_bf16_bits(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);   // quiet NaN
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// OCP 8-bit floating point E4M3 (OFP8 specification, 2023): sign, 4 exponent bits with bias
+// 7, 3 mantissa bits, no infinities, S.1111.111 the only NaN, largest finite value 448.
+// Round to nearest even; magnitudes at or above 448 saturate to 448.
+uint8_t f32_to_e4m3_bits(float f) {
+  const uint8_t sign = std::signbit(f) ? 0x80 : 0;
+  const double a = std::fabs((double)f);
+  if (std::isnan(f)) return 0x7f;
+  if (a >= 448.0) return sign | 0x7e;
+  int e2;
+  (void)std::frexp(a, &e2);                  // a in [2^(e2-1), 2^e2)
+  const int E = a == 0.0 ? -6 : std::max(e2 - 1, -6);   // below 2^-6: subnormal quantum 2^-9
+  const double q = std::ldexp(1.0, E - 3);
+  const double r = std::nearbyint(a / q) * q;   // the default rounding mode is to nearest even
+  if (r >= 448.0) return sign | 0x7e;
+  if (r < std::ldexp(1.0, -6)) return sign | (uint8_t)(r / std::ldexp(1.0, -9));   // subnormal (or 0)
+  int er;
+  (void)std::frexp(r, &er);
+  const int Er = er - 1;                     // r may have rounded up into the next binade
+  const int mant = (int)(r / std::ldexp(1.0, Er - 3)) - 8;
+  return sign | (uint8_t)((Er + 7) << 3) | (uint8_t)mant;
 }
 
 static float bf16_bits_to_f32(uint16_t b) {
@@ -112,6 +135,36 @@ struct Packer {
       for (int64_t c = 0; c < cols; ++c) d[kt_index(r, c, cols)] = f32_to_bf16_bits(src(r, c));
     return off;
   }
+  // e4m3 copy of the same matrix for the compensated products (kt8_index layout; rows a
+  // multiple of 64): the bf16-rounded value of row r times 2^e_r, e_r the largest power that
+  // keeps the row's largest magnitude within 448; scale_off receives the rows' E8M0 bytes
+  // 127 - e_r (so the GEMM's scaled MFMA multiplies row r back by 2^-e_r).
+  template <class F>
+  size_t mat8(int64_t rows, int64_t cols, F src, size_t& scale_off) {
+    std::vector<float> row(cols);
+    std::vector<uint8_t> sc(rows);
+    size_t off = reserve((size_t)rows * cols);
+    for (int64_t r = 0; r < rows; ++r) {
+      double mx = 0;
+      for (int64_t c = 0; c < cols; ++c) {
+        row[c] = bf16_bits_to_f32(f32_to_bf16_bits(src(r, c)));
+        mx = std::max(mx, (double)std::fabs(row[c]));
+      }
+      int e = 0;
+      if (mx > 0) {
+        int e2;
+        const double m = std::frexp(mx, &e2);   // mx = m 2^e2, m in [0.5, 1)
+        e = (m * 512.0 <= 448.0 ? 9 : 8) - e2;
+        e = std::min(std::max(e, -127), 127);
+      }
+      sc[r] = (uint8_t)(127 - e);
+      uint8_t* d = blob.data() + off;
+      for (int64_t c = 0; c < cols; ++c) d[kt8_index(r, c, cols)] = f32_to_e4m3_bits(std::ldexp(row[c], e));
+    }
+    scale_off = reserve((size_t)rows);
+    std::memcpy(blob.data() + scale_off, sc.data(), rows);
+    return off;
+  }
   template <class F>
   size_t vec(int64_t n, F src) {
     size_t off = reserve((size_t)n * 4);
@@ -136,7 +189,9 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
 
   struct LayerOff {
     size_t n1g, n1b, n2g, n2b, qkv_w, qkv_b, proj_w, proj_b, fc1_w, fc1_b, fc2_w, fc2_b;
+    size_t qkv_w8 = 0, qkv_s8 = 0, fc1_w8 = 0, fc1_s8 = 0, fc2_w8 = 0, fc2_s8 = 0;
   };
+  const bool f8 = ctx->f8;
   std::vector<LayerOff> lo(c.layers);
 
   size_t lut_off = P.reserve(3 * 256 * 2);
@@ -193,7 +248,9 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
       const int64_t head = pair / r, kk = pair % r;
       return part * d + head * hd + kk + (s < 32 ? 0 : r);
     };
-    L.qkv_w = P.mat(3 * d, d, [&](int64_t j, int64_t k) { return wq[src_row(j) * d + k]; });
+    auto qkv_src = [&](int64_t j, int64_t k) { return wq[src_row(j) * d + k]; };
+    L.qkv_w = P.mat(3 * d, d, qkv_src);
+    if (f8) L.qkv_w8 = P.mat8(3 * d, d, qkv_src, L.qkv_s8);
     L.qkv_b = P.vec(3 * d, [&](int64_t j) { return bq[src_row(j)]; });
 
     const HostTensor* pw = P.get(p + "proj.w", {d, d});
@@ -208,9 +265,15 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
       const HostTensor* w2 = P.get(p + "fc2.w", {d, mlp});
       const HostTensor* b2 = P.get(p + "fc2.b", {d});
       if (!w1 || !b1 || !w2 || !b2) goto fail;
-      L.fc1_w = P.mat(mp, d, [&](int64_t o, int64_t k) { return o < mlp ? w1->data[o * d + k] : 0.f; });
+      auto fc1_src = [&](int64_t o, int64_t k) { return o < mlp ? w1->data[o * d + k] : 0.f; };
+      auto fc2_src = [&](int64_t o, int64_t k) { return k < mlp ? w2->data[o * mlp + k] : 0.f; };
+      L.fc1_w = P.mat(mp, d, fc1_src);
       L.fc1_b = P.vec(mp, [&](int64_t o) { return o < mlp ? b1->data[o] : 0.f; });
-      L.fc2_w = P.mat(d, mp, [&](int64_t o, int64_t k) { return k < mlp ? w2->data[o * mlp + k] : 0.f; });
+      L.fc2_w = P.mat(d, mp, fc2_src);
+      if (f8) {
+        L.fc1_w8 = P.mat8(mp, d, fc1_src, L.fc1_s8);
+        L.fc2_w8 = P.mat8(d, mp, fc2_src, L.fc2_s8);
+      }
       L.fc2_b = P.vec(d, [&](int64_t i) { return b2->data[i]; });
     } else {
       const HostTensor* wg = P.get(p + "gate.w", {mlp, d});
@@ -226,24 +289,30 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
         is_up = s >= 32;
         return 32 * (j / 64) + s % 32;
       };
-      L.fc1_w = P.mat(2 * mp, d, [&](int64_t j, int64_t k) {
+      auto fc1_src = [&](int64_t j, int64_t k) {
         bool up;
         const int64_t o = gu(j, up);
         if (o >= mlp) return 0.f;
         return (up ? wu : wg)->data[o * d + k];
-      });
+      };
+      auto fc2_src = [&](int64_t o, int64_t k) { return k < mlp ? wd->data[o * mlp + k] : 0.f; };
+      L.fc1_w = P.mat(2 * mp, d, fc1_src);
       L.fc1_b = P.vec(2 * mp, [&](int64_t j) {
         bool up;
         const int64_t o = gu(j, up);
         if (o >= mlp) return 0.f;
         return (up ? bu : bg)->data[o];
       });
-      L.fc2_w = P.mat(d, mp, [&](int64_t o, int64_t k) { return k < mlp ? wd->data[o * mlp + k] : 0.f; });
+      L.fc2_w = P.mat(d, mp, fc2_src);
       L.fc2_b = P.vec(d, [&](int64_t i) { return bd->data[i]; });
+      if (f8) {
+        L.fc1_w8 = P.mat8(2 * mp, d, fc1_src, L.fc1_s8);
+        L.fc2_w8 = P.mat8(d, mp, fc2_src, L.fc2_s8);
+      }
     }
   }
 
-  size_t mqg, mqb, m1w, m1b, m2w, m2b;
+  size_t mqg, mqb, m1w, m1b, m2w, m2b, m1w8, m1s8, m2w8, m2s8;
   {
     const HostTensor* g = P.get("mrg.nq.g", {d});
     if (!g) goto fail;
@@ -262,9 +331,16 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
     if (!w1 || !b1 || !w2 || !b2) goto fail;
     // merger input row = the merge unit's 4 patch rows concatenated (each stored as
     // [hi(d) | lo(d)] when split; the GEMM maps logical columns onto that layout)
-    m1w = P.mat(md, md, [&](int64_t o, int64_t k) { return w1->data[o * md + k]; });
+    m1w8 = m1s8 = m2w8 = m2s8 = 0;
+    auto m1_src = [&](int64_t o, int64_t k) { return w1->data[o * md + k]; };
+    auto m2_src = [&](int64_t o, int64_t k) { return w2->data[o * md + k]; };
+    m1w = P.mat(md, md, m1_src);
     m1b = P.vec(md, [&](int64_t i) { return b1->data[i]; });
-    m2w = P.mat(od, md, [&](int64_t o, int64_t k) { return w2->data[o * md + k]; });
+    m2w = P.mat(od, md, m2_src);
+    if (f8) {
+      m1w8 = P.mat8(md, md, m1_src, m1s8);
+      m2w8 = P.mat8(od, md, m2_src, m2s8);
+    }
     m2b = P.vec(od, [&](int64_t i) { return b2->data[i]; });
   }
 
@@ -293,6 +369,7 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
     char* base = static_cast<char*>(arena);
     auto bf = [&](size_t o) { return reinterpret_cast<const uint16_t*>(base + o); };
     auto fl = [&](size_t o) { return reinterpret_cast<const float*>(base + o); };
+    auto b8 = [&](size_t o) { return f8 ? reinterpret_cast<const uint8_t*>(base + o) : nullptr; };
     DeviceWeights& W = ctx->w;
     W.arena = arena;
     W.bytes = P.blob.size();
@@ -307,10 +384,15 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
       X.proj_w = bf(L.proj_w); X.proj_b = fl(L.proj_b);
       X.fc1_w = bf(L.fc1_w); X.fc1_b = fl(L.fc1_b);
       X.fc2_w = bf(L.fc2_w); X.fc2_b = fl(L.fc2_b);
+      X.qkv_w8 = b8(L.qkv_w8); X.qkv_s8 = b8(L.qkv_s8);
+      X.fc1_w8 = b8(L.fc1_w8); X.fc1_s8 = b8(L.fc1_s8);
+      X.fc2_w8 = b8(L.fc2_w8); X.fc2_s8 = b8(L.fc2_s8);
     }
     W.mq_g = fl(mqg); W.mq_b = fl(mqb);
     W.m1_w = bf(m1w); W.m1_b = fl(m1b);
     W.m2_w = bf(m2w); W.m2_b = fl(m2b);
+    W.m1_w8 = b8(m1w8); W.m1_s8 = b8(m1s8);
+    W.m2_w8 = b8(m2w8); W.m2_s8 = b8(m2s8);
   }
   ctx->host.clear();
   ctx->finalized = true;

@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_support import GpuRun, assert_close_bf16, assert_encoder_tolerance  # noqa: E402
+from gpu_support import GpuRun, assert_close_bf16, assert_encoder_tolerance, f8_extra  # noqa: E402
 
 _RUNS = {}
 
@@ -36,14 +36,27 @@ def say(msg):
     sys.stdout.flush()
 
 
-def get_run(idx: int, layers=None) -> GpuRun:
-    key = (idx, layers)
+# compensated activations: hi+lo bf16 pairs, or bf16 + e4m3 residual
+PRECS = ["bf16x2", "bf16f8"]
+
+
+def get_run(idx: int, layers=None, prec="bf16f8") -> GpuRun:
+    key = (idx, layers, prec)
     if key not in _RUNS:
-        say(f"building workload {idx} layers={layers}")
+        say(f"building workload {idx} layers={layers} activations={prec}")
         _RUNS.clear()
         torch.cuda.empty_cache()
-        _RUNS[key] = GpuRun(make_workload(idx, layers=layers))
+        _RUNS[key] = GpuRun(make_workload(idx, layers=layers), activation_precision=prec)
     return _RUNS[key]
+
+
+def rope_pairs(e, heads, hd):
+    """Error bound of RoPE'd columns: each output mixes its rotary pair (k, k + hd/2)."""
+    if np.isscalar(e):
+        return e
+    e = e.reshape(-1, heads, hd)
+    s = e[..., : hd // 2] + e[..., hd // 2:]
+    return np.concatenate([s, s], axis=-1)
 
 
 def W64(run, name):
@@ -119,8 +132,11 @@ def check_block(run, layer):
     q = O.apply_rope(qkv[:, :d].reshape(-1, H, hd), ang)
     k = O.apply_rope(qkv[:, d:2 * d].reshape(-1, H, hd), ang)
     v = qkv[:, 2 * d:].reshape(-1, H, hd)
-    for nm, got, want in (("q", qg, q), ("k", kg, k), ("v", vg, v)):
-        assert_close_bf16(got, want, rel=2.0 ** -8, abs_=2e-4, what=f"L{layer} {nm}+rope")
+    e = f8_extra(run, h1, W64(run, p + ".qkv.w"))
+    ex = (0.0, 0.0, 0.0) if np.isscalar(e) else \
+        (rope_pairs(e[:, :d], H, hd), rope_pairs(e[:, d:2 * d], H, hd), e[:, 2 * d:].reshape(-1, H, hd))
+    for (nm, got, want), x in zip((("q", qg, q), ("k", kg, k), ("v", vg, v)), ex):
+        assert_close_bf16(got, want, rel=2.0 ** -8, abs_=2e-4, what=f"L{layer} {nm}+rope", extra=x)
 
     og = run.stage(layer, 5)
     o = O.attention(qg, kg, vg, segs, rows=rows).reshape(-1, d)
@@ -139,26 +155,33 @@ def check_block(run, layer):
     if c.mlp_kind == "gelu":
         a = O.gelu(h2 @ W64(run, p + ".fc1.w").T + W64(run, p + ".fc1.b"))
         w2, b2 = W64(run, p + ".fc2.w"), W64(run, p + ".fc2.b")
+        ea = 1.13 * f8_extra(run, h2, W64(run, p + ".fc1.w"))   # |gelu'| <= 1.13
     else:
-        a = O.silu(h2 @ W64(run, p + ".gate.w").T + W64(run, p + ".gate.b")) * \
-            (h2 @ W64(run, p + ".up.w").T + W64(run, p + ".up.b"))
+        g = h2 @ W64(run, p + ".gate.w").T + W64(run, p + ".gate.b")
+        u = h2 @ W64(run, p + ".up.w").T + W64(run, p + ".up.b")
+        a = O.silu(g) * u
         w2, b2 = W64(run, p + ".down.w"), W64(run, p + ".down.b")
-    assert_close_bf16(ag, a, rel=2.0 ** -7, abs_=2e-4, what=f"L{layer} mlp activation")
+        eg, eu = f8_extra(run, h2, W64(run, p + ".gate.w")), f8_extra(run, h2, W64(run, p + ".up.w"))
+        ea = 1.1 * np.abs(u) * eg + np.abs(O.silu(g)) * eu + eg * eu   # |silu'| <= 1.1
+    assert_close_bf16(ag, a, rel=2.0 ** -7, abs_=2e-4, what=f"L{layer} mlp activation", extra=ea)
 
     r2g = run.stage(layer, 9)
-    assert_close_bf16(r2g, r1g + ag @ w2.T + b2, rel=1e-5, abs_=2e-4, what=f"L{layer} mlp out+residual")
+    assert_close_bf16(r2g, r1g + ag @ w2.T + b2, rel=1e-5, abs_=2e-4, what=f"L{layer} mlp out+residual",
+                      extra=f8_extra(run, ag, w2))
 
 
+@pytest.mark.parametrize("prec", PRECS)
 @pytest.mark.parametrize("idx,layer", [(1, 0), (2, 0), (2, 3), (3, 0), (5, 0), (5, 7)])
-def test_block_kernels_layer_local(idx, layer):
-    run = get_run(idx, layers=max(1, layer + 1) if idx >= 3 else None)
-    say(f"block kernels workload {idx} layer {layer}")
+def test_block_kernels_layer_local(idx, layer, prec):
+    run = get_run(idx, layers=max(1, layer + 1) if idx >= 3 else None, prec=prec)
+    say(f"block kernels workload {idx} layer {layer} activations {prec}")
     check_block(run, layer)
 
 
+@pytest.mark.parametrize("prec", PRECS)
 @pytest.mark.parametrize("idx", [1, 2, 5])
-def test_patch_embed_and_merger_layer_local(idx):
-    run = get_run(idx, layers=1 if idx >= 3 else None)
+def test_patch_embed_and_merger_layer_local(idx, prec):
+    run = get_run(idx, layers=1 if idx >= 3 else None, prec=prec)
     c = run.cfg
     say(f"patch embed + merger workload {idx}")
     x = run.stage(-1, 0)
@@ -170,36 +193,42 @@ def test_patch_embed_and_merger_layer_local(idx):
     assert_close_bf16(u, O.norm(rl, run.wl.weights, "mrg.nq", c.norm_kind, c.norm_eps),
                       rel=2.0 ** -8, abs_=1e-5, what="merger norm")
     z1 = run.stage(c.layers, 2)
-    ref1 = O.gelu(u.reshape(-1, 4 * c.hidden) @ W64(run, "mrg.fc1.w").T + W64(run, "mrg.fc1.b"))
-    assert_close_bf16(z1, ref1, rel=2.0 ** -7, abs_=2e-4, what="merger fc1+gelu")
+    u4 = u.reshape(-1, 4 * c.hidden)
+    ref1 = O.gelu(u4 @ W64(run, "mrg.fc1.w").T + W64(run, "mrg.fc1.b"))
+    assert_close_bf16(z1, ref1, rel=2.0 ** -7, abs_=2e-4, what="merger fc1+gelu",
+                      extra=1.13 * f8_extra(run, u4, W64(run, "mrg.fc1.w")))
     out = run.encode()
     ref2 = z1 @ W64(run, "mrg.fc2.w").T + W64(run, "mrg.fc2.b")
-    assert_close_bf16(out, ref2, rel=1e-5, abs_=2e-4, what="merger fc2 (item order)")
+    assert_close_bf16(out, ref2, rel=1e-5, abs_=2e-4, what="merger fc2 (item order)",
+                      extra=f8_extra(run, z1, W64(run, "mrg.fc2.w")))
 
 
 # ------------------------------------------------------------------ whole tower
 
 
+@pytest.mark.parametrize("prec", PRECS)
 @pytest.mark.parametrize("idx", [1, 2])
-def test_encoder_full_workload(idx):
-    run = get_run(idx)
-    say(f"encoder workload {idx} N={run.n} layers={run.cfg.layers}")
+def test_encoder_full_workload(idx, prec):
+    run = get_run(idx, prec=prec)
+    say(f"encoder workload {idx} N={run.n} layers={run.cfg.layers} activations {prec}")
     got = run.encode()
     ref = O.forward_workload(run.wl)
-    assert_encoder_tolerance(got, ref, what=f"workload {idx}")
+    assert_encoder_tolerance(got, ref, what=f"workload {idx} ({prec})")
 
 
+@pytest.mark.parametrize("prec", PRECS)
 @pytest.mark.parametrize("idx", [3, 5])
-def test_encoder_full_depth_sampled_items(idx):
+def test_encoder_full_depth_sampled_items(idx, prec):
     """32-layer tower on the whole batch; the oracle recomputes the smallest item(s) alone."""
-    run = get_run(idx)
-    say(f"encoder workload {idx} N={run.n} (32 layers), oracle on the smallest item")
+    run = get_run(idx, prec=prec)
+    say(f"encoder workload {idx} N={run.n} (32 layers), oracle on the smallest item, activations {prec}")
     got = run.encode()
     sizes = [it.n_patches for it in run.wl.items]
     pick = [int(np.argmin(sizes))]
     ref = O.forward_workload(run.wl, items=pick)
     start = sum(sizes[:pick[0]]) // 4
-    assert_encoder_tolerance(got[start:start + sizes[pick[0]] // 4], ref, what=f"workload {idx} item {pick[0]}")
+    assert_encoder_tolerance(got[start:start + sizes[pick[0]] // 4], ref,
+                             what=f"workload {idx} item {pick[0]} ({prec})")
 
 
 def test_video_workload_last_block_and_merger():

@@ -250,6 +250,25 @@ def test_video_shaped_short_clip_end_to_end():
     assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="video 4 frames, 2 layers")
 
 
+_TILE_REFS = {}
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("side", [672, 1120])
+def test_tile_configs_across_batch_sizes(side, prec):
+    """One-layer towers on single images whose patch counts (2304, 6400) make the GEMMs pick
+    other tile configurations than the bench batch (128x256 at one workgroup per CU for fc2,
+    the out-projection and the merger, two per CU for qkv and fc1); whole tower against the
+    oracle (computed once per size)."""
+    cfg = tower_config(2).with_layers(1)
+    wl = make_custom_workload(cfg, [(1, side, side)], seed=71)
+    run = GpuRun(wl, activation_precision=prec)
+    say(f"tile configs: {side}x{side} image N={run.n} activations {prec}")
+    if side not in _TILE_REFS:
+        _TILE_REFS[side] = O.forward_workload(wl)
+    assert_encoder_tolerance(run.encode(), _TILE_REFS[side], what=f"{side} px, 1 layer ({prec})")
+
+
 def test_edge_items_end_to_end():
     """One-unit items, ragged segment lengths, a 2-frame video and a wide strip."""
     cfg = tower_config(2).with_layers(2)

@@ -33,12 +33,11 @@
 //  * K advances 32 columns per stage.  Tiles move global -> LDS with gfx950's
 //    buffer loads into LDS (no VGPR staging): one 64-lane 16-byte load moves
 //    one 1 KB operand block (whole cache lines: rows of 64-byte K slices would
-//    touch twice as many lines and halve the CU's load rate), every lane keeps
-//    one fixed 32-bit block offset per load and the K advance rides in the
-//    scalar offset.  LDS rows are 64 bytes; the blocked layout already puts
-//    the four 16-byte chunks of row r at chunk ^ (((r >> 1) ^ (r >> 3)) & 3),
-//    so the 32x32x16 fragment reads (32 rows, one chunk) touch distinct banks
-//    in every 8- and 16-lane group.
+//    touch twice as many lines and halve the CU's load rate); the block's
+//    wave-uniform offset and the K advance ride in the scalar offset, the
+//    lane's 16 bytes in one vector offset shared by every load.  LDS rows are 64 bytes; the blocked layout already puts
+//    the four 16-byte chunks of row r at chunk ^ ((r >> 3) & 3), which keeps
+//    the 32x32x16 fragment reads (32 rows, one chunk) free of bank conflicts.
 //  * A ring of 2-4 stages: a stage's slot is refilled as soon as every wave
 //    has read it (the barrier in the middle of the next stage), so each load
 //    has S-1 whole stages to land; one barrier per stage, preceded by an

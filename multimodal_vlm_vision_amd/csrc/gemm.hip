@@ -194,29 +194,43 @@ struct Geo {
 };
 
 // Applies the epilogue to one staged 32-row slice (rows m_base.., columns n_base.., width W = TN*32).
+// Every global read of a slice (bias, residual rows, scatter rows, rotary tables) is issued
+// before its first store: the compiler cannot tell the outputs from the inputs, so a read
+// placed after a store would wait for that store to complete (one memory round trip per
+// 16-byte piece instead of one or two per slice).
 template <int EPI, int W, int AM>
 __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const float* sc, int m_base, int n_base,
                                                int lane) {
   constexpr int SST = W + 8;
   constexpr int C4 = W / 4;   // float4 chunks per row
   if (EPI == EPI_F32 || EPI == EPI_RES || EPI == EPI_OUT) {
+    constexpr int NQ = 32 * C4 / 64;
+    static_assert(64 % C4 == 0, "a lane keeps its columns through the slice");
+    const int c4 = lane % C4, n = n_base + 4 * c4;
+    float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (EPI != EPI_F32) b = *reinterpret_cast<const float4*>(p.bias + n);
+    float4 res[NQ];
+    int orow[NQ];
 #pragma unroll
-    for (int q = 0; q < 32 * C4 / 64; ++q) {
-      const int id = lane + 64 * q, r = id / C4, c4 = id % C4;
-      const int m = m_base + r, n = n_base + 4 * c4;
+    for (int q = 0; q < NQ; ++q) {
+      const int m = m_base + (lane + 64 * q) / C4;
+      if (EPI == EPI_RES)
+        res[q] = m < M ? *reinterpret_cast<const float4*>(static_cast<const float*>(p.out) + (int64_t)m * p.ldo + n)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (EPI == EPI_OUT) orow[q] = m < M ? p.row_map[m] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int r = (lane + 64 * q) / C4, m = m_base + r;
       if (m >= M) continue;
       const float4 v = *reinterpret_cast<const float4*>(sc + r * SST + 4 * c4);
-      if (EPI == EPI_F32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)m * p.ldo + n) = v;
-      } else {
-        const float4 b = *reinterpret_cast<const float4*>(p.bias + n);
-        if (EPI == EPI_RES) {
-          float4* o = reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)m * p.ldo + n);
-          *o = f4add(*o, f4add(v, b));
-        } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)p.row_map[m] * p.ldo + n) = f4add(v, b);
-        }
-      }
+      float* o = static_cast<float*>(p.out);
+      if (EPI == EPI_F32)
+        *reinterpret_cast<float4*>(o + (int64_t)m * p.ldo + n) = v;
+      else if (EPI == EPI_RES)
+        *reinterpret_cast<float4*>(o + (int64_t)m * p.ldo + n) = f4add(res[q], f4add(v, b));
+      else
+        *reinterpret_cast<float4*>(o + (int64_t)orow[q] * p.ldo + n) = f4add(v, b);
     }
   } else if (EPI == EPI_GELU || EPI == EPI_SWIGLU) {
     // bf16 activations into the blocked layout: a lane produces one 16-byte chunk (8 columns)
@@ -224,9 +238,26 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const f
     // chunk position in the block is q; it holds logical chunk kt_chunk(row, q).
     constexpr int OW = EPI == EPI_SWIGLU ? W / 2 : W;   // output columns of the slice
     constexpr int OB = OW / 32;                          // output column blocks
+    constexpr int NB = 2 * OB;                           // (row group, column block) pairs
     const int r16 = lane >> 2, q = lane & 3;
+    // GELU: bias of the 8 columns; SwiGLU: bias of the 8 gate and the 8 up columns
+    float4 bg[NB][2], bu[NB][2];
 #pragma unroll
-    for (int blk = 0; blk < 2 * OB; ++blk) {
+    for (int blk = 0; blk < NB; ++blk) {
+      const int rg = blk / OB, ob = blk % OB;
+      const int c = kt_chunk(m_base + 16 * rg + r16, q);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (EPI == EPI_GELU) {
+          bg[blk][h] = *reinterpret_cast<const float4*>(p.bias + n_base + 32 * ob + 8 * c + 4 * h);
+        } else {
+          bg[blk][h] = *reinterpret_cast<const float4*>(p.bias + n_base + 64 * ob + 8 * c + 4 * h);
+          bu[blk][h] = *reinterpret_cast<const float4*>(p.bias + n_base + 64 * ob + 8 * c + 32 + 4 * h);
+        }
+      }
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
       const int rg = blk / OB, ob = blk % OB;
       const int r = 16 * rg + r16, m = m_base + r;
       if (m >= M) continue;
@@ -238,8 +269,7 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const f
         oc = n_base + cl;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const float4 x = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 4 * h),
-                                 *reinterpret_cast<const float4*>(p.bias + oc + 4 * h));
+          const float4 x = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 4 * h), bg[blk][h]);
           y[4 * h] = gelu(x.x); y[4 * h + 1] = gelu(x.y); y[4 * h + 2] = gelu(x.z); y[4 * h + 3] = gelu(x.w);
         }
       } else {
@@ -248,10 +278,8 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const f
         oc = n_base / 2 + 32 * ob + 8 * c;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const float4 g = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 4 * h),
-                                 *reinterpret_cast<const float4*>(p.bias + n_base + cl + 4 * h));
-          const float4 u = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 32 + 4 * h),
-                                 *reinterpret_cast<const float4*>(p.bias + n_base + cl + 32 + 4 * h));
+          const float4 g = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 4 * h), bg[blk][h]);
+          const float4 u = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 32 + 4 * h), bu[blk][h]);
           y[4 * h] = silu(g.x) * u.x; y[4 * h + 1] = silu(g.y) * u.y;
           y[4 * h + 2] = silu(g.z) * u.z; y[4 * h + 3] = silu(g.w) * u.w;
         }
@@ -264,36 +292,55 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const f
     // pairs: columns c (c % 64 < 32) and c + 32 of each 64-column block.  A lane rotates 8
     // consecutive rotary pairs of one head (head_dim/2 is a multiple of 8 and the frequency
     // count per axis, head_dim/4, a multiple of 4, so each group of 4 has one axis) and writes
-    // each member half as one 16-byte store.
+    // each member half as one 16-byte store.  The lane's columns are the same in every row.
     constexpr int G8 = W / 16;   // first-member groups of 8 per row
+    constexpr int NQ = 32 * G8 / 64;
+    static_assert(64 % G8 == 0, "a lane keeps its columns through the slice");
     const int d = p.hidden, hd = p.head_dim, rr = hd / 2, nf = p.nfreq;
+    const int g = lane % G8;
+    const int cl = (g / 4) * 64 + (g % 4) * 8;          // local column of the first member
+    const int n = n_base + cl;
+    const int part = n / d, jj = n - part * d;
+    const int pair = 32 * (jj / 64) + (jj % 64);
+    const int head = pair / rr, kk = pair % rr;
+    const float qs = part == 0 ? p.q_scale : 1.0f;
+    float4 ba[2], bb[2];
 #pragma unroll
-    for (int q = 0; q < 32 * G8 / 64; ++q) {
-      const int id = lane + 64 * q, r = id / G8, g = id % G8;
-      const int cl = (g / 4) * 64 + (g % 4) * 8;          // local column of the first member
-      const int m = m_base + r, n = n_base + cl;
+    for (int hf = 0; hf < 2; ++hf) {
+      ba[hf] = *reinterpret_cast<const float4*>(p.bias + n + 4 * hf);
+      bb[hf] = *reinterpret_cast<const float4*>(p.bias + n + 32 + 4 * hf);
+    }
+    int pos[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int m = m_base + (lane + 64 * q) / G8;
+      pos[q] = m < M ? p.row_pos[m] : 0;
+    }
+    float4 cs[NQ][2], sn[NQ][2];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int k4 = kk + 4 * hf;
+        const int ax = k4 < nf ? (pos[q] >> 16) : (pos[q] & 0xffff);
+        const int fi = k4 < nf ? k4 : k4 - nf;
+        cs[q][hf] = *reinterpret_cast<const float4*>(p.cos_tab + ax * nf + fi);
+        sn[q][hf] = *reinterpret_cast<const float4*>(p.sin_tab + ax * nf + fi);
+      }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int r = (lane + 64 * q) / G8, m = m_base + r;
       if (m >= M) continue;
-      const int part = n / d, jj = n - part * d;
-      const int pair = 32 * (jj / 64) + (jj % 64);
-      const int head = pair / rr, kk = pair % rr;
-      const int pos = p.row_pos[m];
-      const float qs = part == 0 ? p.q_scale : 1.0f;
       uint32_t w1[4], w2[4];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const float4 a = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 4 * hf),
-                               *reinterpret_cast<const float4*>(p.bias + n + 4 * hf));
-        const float4 b = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 32 + 4 * hf),
-                               *reinterpret_cast<const float4*>(p.bias + n + 32 + 4 * hf));
-        const int k4 = kk + 4 * hf;
-        const int ax = k4 < nf ? (pos >> 16) : (pos & 0xffff);
-        const int fi = k4 < nf ? k4 : k4 - nf;
-        const float4 cs = *reinterpret_cast<const float4*>(p.cos_tab + ax * nf + fi);
-        const float4 sn = *reinterpret_cast<const float4*>(p.sin_tab + ax * nf + fi);
-        const uint2 u1 = pack4(make_float4((a.x * cs.x - b.x * sn.x) * qs, (a.y * cs.y - b.y * sn.y) * qs,
-                                           (a.z * cs.z - b.z * sn.z) * qs, (a.w * cs.w - b.w * sn.w) * qs));
-        const uint2 u2 = pack4(make_float4((b.x * cs.x + a.x * sn.x) * qs, (b.y * cs.y + a.y * sn.y) * qs,
-                                           (b.z * cs.z + a.z * sn.z) * qs, (b.w * cs.w + a.w * sn.w) * qs));
+        const float4 a = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 4 * hf), ba[hf]);
+        const float4 b = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 32 + 4 * hf), bb[hf]);
+        const float4 c = cs[q][hf], s = sn[q][hf];
+        const uint2 u1 = pack4(make_float4((a.x * c.x - b.x * s.x) * qs, (a.y * c.y - b.y * s.y) * qs,
+                                           (a.z * c.z - b.z * s.z) * qs, (a.w * c.w - b.w * s.w) * qs));
+        const uint2 u2 = pack4(make_float4((b.x * c.x + a.x * s.x) * qs, (b.y * c.y + a.y * s.y) * qs,
+                                           (b.z * c.z + a.z * s.z) * qs, (b.w * c.w + a.w * s.w) * qs));
         w1[2 * hf] = u1.x; w1[2 * hf + 1] = u1.y;
         w2[2 * hf] = u2.x; w2[2 * hf + 1] = u2.y;
       }
@@ -305,13 +352,17 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const f
     // V part: transposed store [head][dim][token]; an item is 8 consecutive rows of one column,
     // one 16-byte store (the V^T pitch is a multiple of 8).  A last group with only 4 valid
     // rows (row counts are multiples of 4) stores those 4: the pad columns must stay zero.
+    constexpr int NQ = 4 * W / 64;
     const int d = p.hidden, hd = p.head_dim;
+    float bv[NQ];
 #pragma unroll
-    for (int q = 0; q < 4 * W / 64; ++q) {
+    for (int q = 0; q < NQ; ++q) bv[q] = p.bias[n_base + (lane + 64 * q) / 4];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
       const int id = lane + 64 * q, rg = id % 4, c = id / 4;
       const int m = m_base + 8 * rg, n = n_base + c;
       if (m >= M) continue;
-      const float b = p.bias[n];
+      const float b = bv[q];
       const float4 v0 = make_float4(sc[(8 * rg + 0) * SST + c] + b, sc[(8 * rg + 1) * SST + c] + b,
                                     sc[(8 * rg + 2) * SST + c] + b, sc[(8 * rg + 3) * SST + c] + b);
       const float4 v1 = make_float4(sc[(8 * rg + 4) * SST + c] + b, sc[(8 * rg + 5) * SST + c] + b,

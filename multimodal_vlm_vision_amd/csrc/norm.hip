@@ -60,12 +60,17 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __restr
   if (row >= (DYN ? (int64_t)*rows_dev : rows)) return;   // DYN: run-time count (bucketed graph)
   const float4* src = reinterpret_cast<const float4*>(r + row * d);
   const int n4 = d >> 2;
-  float4 v[VPL];
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+  // the row, its gains and shifts all read before the first store
+  float4 v[VPL], gv[VPL], bv[VPL];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int c = lane + 64 * i;
     v[i] = c < n4 ? src[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    gv[i] = c < n4 ? g4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    bv[i] = (KIND == VIT_NORM_LAYER && c < n4) ? b4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
     if (KIND == VIT_NORM_LAYER) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   }
   float mean = 0.f;
@@ -83,20 +88,18 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __restr
   const int w = d * (SPLIT ? 2 : 1);
   const int64_t orow = row / group;
   const int ocol = (int)(row % group) * w, ocols = group * w;
-  const float4* g4 = reinterpret_cast<const float4*>(g);
-  const float4* b4 = reinterpret_cast<const float4*>(b);
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int c = lane + 64 * i;
     if (c < n4) {
-      const float4 gg = g4[c];
+      const float4 gg = gv[i];
       float4 y;
       y.x = (v[i].x - mean) * rstd * gg.x;
       y.y = (v[i].y - mean) * rstd * gg.y;
       y.z = (v[i].z - mean) * rstd * gg.z;
       y.w = (v[i].w - mean) * rstd * gg.w;
       if (KIND == VIT_NORM_LAYER) {
-        const float4 bb = b4[c];
+        const float4 bb = bv[i];
         y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
       }
       *reinterpret_cast<uint2*>(out + kt_index(orow, ocol + 4 * c, ocols)) =
@@ -124,12 +127,18 @@ rownorm2_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __rest
   const bool live = row < nrows;
   const float4* src = reinterpret_cast<const float4*>(r + (live ? row : 0) * d);
   const int n4 = d >> 2;
-  float4 v[VPL2];
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+  // the row, its gains and shifts all read before the first store (a read after a store would
+  // wait for it: the compiler cannot tell the output from the inputs)
+  float4 v[VPL2], gv[VPL2], bv[VPL2];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < VPL2; ++i) {
     const int c = c32 + 32 * i;
     v[i] = (live && c < n4) ? src[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    gv[i] = c < n4 ? g4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    bv[i] = (KIND == VIT_NORM_LAYER && c < n4) ? b4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
     if (KIND == VIT_NORM_LAYER) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   }
   auto half_sum = [](float x) {
@@ -151,20 +160,18 @@ rownorm2_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __rest
   const float rstd = 1.0f / sqrtf(half_sum(q) / (float)d + eps);
   if (!live) return;
   const int w = d * (SPLIT ? 2 : 1);
-  const float4* g4 = reinterpret_cast<const float4*>(g);
-  const float4* b4 = reinterpret_cast<const float4*>(b);
 #pragma unroll
   for (int i = 0; i < VPL2; ++i) {
     const int c = c32 + 32 * i;
     if (c < n4) {
-      const float4 gg = g4[c];
+      const float4 gg = gv[i];
       float4 y;
       y.x = (v[i].x - mean) * rstd * gg.x;
       y.y = (v[i].y - mean) * rstd * gg.y;
       y.z = (v[i].z - mean) * rstd * gg.z;
       y.w = (v[i].w - mean) * rstd * gg.w;
       if (KIND == VIT_NORM_LAYER) {
-        const float4 bb = b4[c];
+        const float4 bb = bv[i];
         y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
       }
       *reinterpret_cast<uint2*>(out + kt_index(row, 4 * c, w)) =

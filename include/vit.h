@@ -312,8 +312,9 @@ vit_status vit_encode_profiled(const vit_ctx* ctx, const vit_plan* plan, const u
  *               9 block output f32 [N][hidden]
  *   layer = layers: 1 merger norm bf16 [N][S*hidden]; 2 merger hidden bf16 [N/4][S*4*hidden];
  *               3 output f32 [N/4][out_dim] (item order)
- * where S = 2 with VIT_ACT_BF16X2 (each row holds hi then lo halves; for the
- * merger norm each patch row is [hi | lo]) and 1 otherwise, and mlp_pad is
+ * where S = 2 with VIT_ACT_BF16X2 and VIT_ACT_BF16F8 (each row holds hi then lo
+ * halves, the e4m3 residual converted exactly to bfloat16; for the merger norm
+ * each patch row is [hi | lo]) and 1 otherwise, and mlp_pad is
  * mlp_dim rounded up to a multiple of 64 (columns past mlp_dim are zero).
  * dst_bytes must cover the tensor; VIT_E_WORKSPACE otherwise. */
 vit_status vit_debug_stage(const vit_ctx* ctx, const vit_plan* plan, const uint8_t* pixels_u8,

@@ -22,7 +22,7 @@
 // fp8 matrix, multiplied against an e4m3 copy of the weights whose rows carry
 // power-of-two E8M0 scales.  gfx950's scaled fp8 MFMA (32x32x64, per-row A and
 // per-column B scales) adds that product into the same fp32 accumulators and
-// undoes both scales on the way, at about half the MFMA time of the second bf16
+// undoes both scales on the way, at ~0.43 of the MFMA time of a second bf16
 // product; the residual's own error (e4m3's 3 mantissa bits on a term ~2^-9 of
 // x) stays ~2^-12 of x.  The fp8 MFMA takes 64 K per instruction: with a
 // 32-column stage, each stage's 32 residual bytes of a row fill half of the
@@ -35,9 +35,10 @@
 //    one 1 KB operand block (whole cache lines: rows of 64-byte K slices would
 //    touch twice as many lines and halve the CU's load rate); the block's
 //    wave-uniform offset and the K advance ride in the scalar offset, the
-//    lane's 16 bytes in one vector offset shared by every load.  LDS rows are 64 bytes; the blocked layout already puts
-//    the four 16-byte chunks of row r at chunk ^ ((r >> 3) & 3), which keeps
-//    the 32x32x16 fragment reads (32 rows, one chunk) free of bank conflicts.
+//    lane's 16 bytes in one vector offset shared by every load.  LDS rows are
+//    64 bytes; the blocked layout already puts the four 16-byte chunks of row
+//    r at chunk ^ ((r >> 3) & 3), which keeps the 32x32x16 fragment reads
+//    (32 rows, one chunk) free of bank conflicts.
 //  * A ring of 2-4 stages: a stage's slot is refilled as soon as every wave
 //    has read it (the barrier in the middle of the next stage), so each load
 //    has S-1 whole stages to land; one barrier per stage, preceded by an
@@ -52,7 +53,8 @@
 // Epilogue: the accumulators are staged through LDS one 32-row slice at a
 // time, so every global access of the epilogue is a 16-byte (fp32) or 8-byte
 // (bf16) vector: residual read-modify-write, bias, activations, RoPE pairs
-// and the transposed V store all run on 4 consecutive columns (or rows).
+// and the transposed V store all run on 4 consecutive columns (or rows).  A
+// slice issues all its global reads before its first store.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

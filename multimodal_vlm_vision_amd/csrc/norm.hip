@@ -4,9 +4,11 @@
 // width with eps 1e-6 (vLLM PR #55370 report, key code: the towers take a
 // norm epsilon defaulting to 1e-6; "vLLM multimodal inference | ViT
 // performance optimisation", section 3.5 names RMSNorm among the fused ops).
-// One wave per row; the row stays in registers, so the statistics are exact
+// One wave per row (two rows per wave at the tower's width 1280, so every store
+// writes whole lines); the row stays in registers, so the statistics are exact
 // two-pass sums in float32; output is rounded to nearest-even bfloat16 and
-// stored in the blocked layout the GEMMs load (kt_index).
+// stored in the blocked layout the GEMMs load (kt_index), with the compensated
+// forms' second part (a bfloat16 lo half, or an e4m3 residual in kt8_index).
 #include <hip/hip_runtime.h>
 
 #include "vit_internal.h"

@@ -269,6 +269,30 @@ def test_tile_configs_across_batch_sizes(side, prec):
     assert_encoder_tolerance(run.encode(), _TILE_REFS[side], what=f"{side} px, 1 layer ({prec})")
 
 
+def test_e4m3_residual_saturation():
+    """MLP activations far beyond 224, where the e4m3 residual (times 2^9) saturates at 448:
+    fc1 weights scaled by 2^7 (exact in bf16).  The output stays finite, and the compensated
+    forms stay closer to the oracle than single bf16 rounding (a saturated residual still
+    carries the right sign and most of its size, so it never does worse than no residual)."""
+    cfg = tower_config(2).with_layers(1)
+    wl = make_custom_workload(cfg, [(1, 224, 336)], seed=79)
+    wl.weights["blk0.fc1.w"] = wl.weights["blk0.fc1.w"] * np.float32(128.0)
+    ref = O.forward_workload(wl)
+    errs = {}
+    for prec in ("bf16", "bf16x2", "bf16f8"):
+        run = GpuRun(wl, activation_precision=prec)
+        if prec == "bf16f8":
+            a = run.stage(0, 8)
+            say(f"saturation: largest MLP activation {np.abs(a).max():.1f}, "
+                f"{(np.abs(a) > 224).mean() * 100:.1f}% above 224")
+            assert (np.abs(a) > 224).any(), "the workload must reach the saturation range"
+        got = run.encode()
+        assert np.all(np.isfinite(got)), f"{prec}: non-finite output"
+        errs[prec] = float(np.abs(got - ref).sum() / np.abs(ref).sum())
+        say(f"saturation {prec}: mean_rel={errs[prec]:.3e}")
+    assert errs["bf16f8"] < errs["bf16"] and errs["bf16x2"] < errs["bf16"], errs
+
+
 def test_edge_items_end_to_end():
     """One-unit items, ragged segment lengths, a 2-frame video and a wide strip."""
     cfg = tower_config(2).with_layers(2)

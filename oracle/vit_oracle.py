@@ -46,10 +46,43 @@ segments.
 from __future__ import annotations
 
 import math
-from typing import Dict, List, Optional, Sequence
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Callable, Dict, List, Optional, Sequence
 
 import numpy as np
 from scipy.special import erf
+from threadpoolctl import threadpool_limits
+
+# ----------------------------------------------------------------------------
+# scheduling only: independent rows and independent (segment, query block)
+# pieces of attention run on a thread pool (NumPy and SciPy release the GIL
+# inside their loops).  Every element is computed by the same operations in
+# the same order as in a serial run; only which thread computes it changes.
+# ----------------------------------------------------------------------------
+
+_POOL: Optional[ThreadPoolExecutor] = None
+_ROW_BLOCK = 2048
+
+
+def _threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def _pool() -> ThreadPoolExecutor:
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(_threads())
+    return _POOL
+
+
+def _rowwise(f: Callable[[np.ndarray], np.ndarray], x: np.ndarray) -> np.ndarray:
+    """f applied to x, where f acts on each row (leading index) on its own."""
+    if x.ndim < 2 or x.shape[0] <= _ROW_BLOCK or _threads() == 1:
+        return f(x)
+    parts = list(_pool().map(f, [x[i:i + _ROW_BLOCK] for i in range(0, x.shape[0], _ROW_BLOCK)]))
+    return np.concatenate(parts, axis=0)
+
 
 # ----------------------------------------------------------------------------
 # 1. normalisation
@@ -170,6 +203,10 @@ def apply_rope(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
     r = x.shape[-1] // 2
     c = np.cos(angles)[:, None, :]
     s = np.sin(angles)[:, None, :]
+    if x.ndim == 3 and x.shape[0] > _ROW_BLOCK and _threads() > 1:
+        blocks = range(0, x.shape[0], _ROW_BLOCK)
+        return np.concatenate(list(_pool().map(
+            lambda i: apply_rope(x[i:i + _ROW_BLOCK], angles[i:i + _ROW_BLOCK]), blocks)), axis=0)
     x1, x2 = x[..., :r], x[..., r:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
@@ -180,21 +217,23 @@ def apply_rope(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
 
 
 def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float) -> np.ndarray:
-    mu = x.mean(axis=-1, keepdims=True)
-    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
-    return (x - mu) / np.sqrt(var + eps) * g + b
+    def f(x):
+        mu = x.mean(axis=-1, keepdims=True)
+        var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+        return (x - mu) / np.sqrt(var + eps) * g + b
+    return _rowwise(f, x)
 
 
 def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
-    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * g
+    return _rowwise(lambda x: x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * g, x)
 
 
 def gelu(x: np.ndarray) -> np.ndarray:
-    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+    return _rowwise(lambda x: 0.5 * x * (1.0 + erf(x / math.sqrt(2.0))), x)
 
 
 def silu(x: np.ndarray) -> np.ndarray:
-    return x / (1.0 + np.exp(-x))
+    return _rowwise(lambda x: x / (1.0 + np.exp(-x)), x)
 
 
 def norm(x: np.ndarray, weights: Dict[str, np.ndarray], prefix: str, kind: str, eps: float,
@@ -232,7 +271,7 @@ def window_segments(pos: Dict[str, np.ndarray], window_patches: int) -> List[np.
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, segments: Sequence[np.ndarray],
-              rows: Optional[np.ndarray] = None, chunk: int = 1024) -> np.ndarray:
+              rows: Optional[np.ndarray] = None, chunk: int = 256) -> np.ndarray:
     """softmax(Q K^T / sqrt(head_dim)) V inside each segment, per head.
 
     q, k, v: [N][H][head_dim].  If `rows` is given only those query rows are
@@ -246,24 +285,35 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, segments: Sequence[np
     if rows is not None:
         where = np.full(n_rows, -1, dtype=np.int64)
         where[rows] = np.arange(len(rows))
+    tasks = []
     for seg in segments:
         qrows = seg if where is None else seg[where[seg] >= 0]
-        if qrows.size == 0:
-            continue
+        for c0 in range(0, qrows.size, chunk):
+            tasks.append((seg, qrows[c0:c0 + chunk]))
+
+    def one(task):
+        seg, qr = task
         kt = np.ascontiguousarray(k[seg].transpose(1, 2, 0))          # [H][hd][n]
         vs = np.ascontiguousarray(v[seg].transpose(1, 0, 2))          # [H][n][hd]
-        for c0 in range(0, qrows.size, chunk):
-            qr = qrows[c0:c0 + chunk]
-            qh = np.ascontiguousarray(q[qr].transpose(1, 0, 2))       # [H][nq][hd]
-            s = (qh @ kt) * scale                                     # [H][nq][n]
-            s = s - s.max(axis=-1, keepdims=True)
-            p = np.exp(s)
-            p = p / p.sum(axis=-1, keepdims=True)
-            o = (p @ vs).transpose(1, 0, 2)                           # [nq][H][hd]
-            if where is None:
-                out[qr] = o
-            else:
-                out[where[qr]] = o
+        qh = np.ascontiguousarray(q[qr].transpose(1, 0, 2))           # [H][nq][hd]
+        s = qh @ kt                                                   # [H][nq][n]
+        s *= scale
+        s -= s.max(axis=-1, keepdims=True)
+        p = np.exp(s, out=s)
+        p /= p.sum(axis=-1, keepdims=True)
+        o = (p @ vs).transpose(1, 0, 2)                               # [nq][H][hd]
+        if where is None:
+            out[qr] = o
+        else:
+            out[where[qr]] = o
+
+    if len(tasks) > 1 and _threads() > 1:
+        # one BLAS thread per task: the pieces themselves run in parallel
+        with threadpool_limits(limits=1, user_api="blas"):
+            list(_pool().map(one, tasks))
+    else:
+        for t in tasks:
+            one(t)
     return out
 
 

@@ -336,6 +336,72 @@ def test_window_mask_equals_permuted_contiguous_windows():
     assert np.allclose(o[perm], o_perm, atol=1e-14)
 
 
+def _segments_by_key(keys):
+    """Brute force: rows grouped by equal key tuples, as sorted row-index sets."""
+    groups = {}
+    for row, key in enumerate(keys):
+        groups.setdefault(tuple(int(v) for v in key), []).append(row)
+    return sorted(tuple(g) for g in groups.values())
+
+
+def _as_sets(segs):
+    return sorted(tuple(sorted(int(r) for r in s)) for s in segs)
+
+
+def test_layer_schedule_full_layers_7_15_23_31_else_windows():
+    """The Qwen2.5-shaped workload: 112 px windows in every layer except the full-attention
+    layers 7, 15, 23 and 31 (0-based, as the workload states them).  Expected segments are
+    built here by brute force from each row's (item, frame, window) or item alone; an
+    inverted, shifted (1-based) or missing schedule fails."""
+    cfg = tower_config(5)
+    assert cfg.layers == 32 and tuple(cfg.full_attn_layers) == (7, 15, 23, 31)
+    grid = np.array([[1, 18, 22], [2, 10, 6], [1, 4, 4]])
+    pos = O.patch_positions(grid)
+    wp = cfg.window_px // cfg.patch
+    n = len(pos["item"])
+    by_item = _segments_by_key([(pos["item"][r],) for r in range(n)])
+    by_window = _segments_by_key([(pos["item"][r], pos["t"][r], pos["hpos"][r] // wp, pos["wpos"][r] // wp)
+                                  for r in range(n)])
+    assert len(by_item) == 3 and len(by_window) == 3 * 3 + 2 * (2 * 1) + 1   # ceil(h/8) * ceil(w/8) per frame
+    full = []
+    for layer in range(cfg.layers):
+        got = _as_sets(O.layer_segments(layer, cfg, pos))
+        if got == by_item:
+            full.append(layer)
+        else:
+            assert got == by_window, f"layer {layer}: neither item nor window segments"
+    assert full == [7, 15, 23, 31]
+    # a tower without windows attends over whole items in every layer
+    cfg3 = tower_config(3)
+    assert all(_as_sets(O.layer_segments(l, cfg3, pos)) == by_item for l in (0, 7, 31))
+
+
+def test_forward_applies_the_layer_schedule():
+    """forward() on a 2-layer window tower (layer 1 full) equals two blocks composed by hand
+    with brute-force segments: windows in layer 0, whole items in layer 1."""
+    cfg = _tiny_cfg(layers=2, window_px=56, full_attn_layers=(1,), mlp_kind="swiglu", norm_kind="rms")
+    wl = make_custom_workload(cfg, [(1, 112, 84), (2, 84, 56)], seed=23)
+    x = O.patchify([it.frames for it in wl.items], wl.grid_thw, O.normalize_table(cfg.mean, cfg.std))
+    pos = O.patch_positions(wl.grid_thw)
+    ang = O.rope_angles(pos["hpos"], pos["wpos"], cfg.head_dim)
+    n = len(pos["item"])
+    wp = cfg.window_px // cfg.patch
+    win = [np.array(s) for s in _segments_by_key(
+        [(pos["item"][r], pos["t"][r], pos["hpos"][r] // wp, pos["wpos"][r] // wp) for r in range(n)])]
+    items = [np.array(s) for s in _segments_by_key([(pos["item"][r],) for r in range(n)])]
+    assert len(win) > len(items)
+    r = O.patch_embed(x, wl.weights["pe.w"].astype(np.float64))
+    r = O.block(r, wl.weights, 0, cfg, ang, win)
+    r = O.block(r, wl.weights, 1, cfg, ang, items)
+    want = O.merger(r, wl.weights, cfg)
+    assert np.allclose(O.forward_workload(wl), want, rtol=0, atol=1e-12)
+    # and the schedule matters: swapping the two layers' segments changes the output
+    r2 = O.patch_embed(x, wl.weights["pe.w"].astype(np.float64))
+    r2 = O.block(r2, wl.weights, 0, cfg, ang, items)
+    r2 = O.block(r2, wl.weights, 1, cfg, ang, win)
+    assert not np.allclose(O.merger(r2, wl.weights, cfg), want, atol=1e-6)
+
+
 # ---------------------------------------------------------------- block, merger, tower
 
 

@@ -121,11 +121,27 @@ typedef struct vit_cache vit_cache;
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char* vit_last_error(void);
 
-/* Validates cfg and builds the exact normalise table on the host.  No GPU call. */
+/* Validates cfg and builds the exact normalise table on the host.  No GPU call.
+ * Defined by: "vLLM multimodal inference | ViT performance optimisation",
+ * section 2.2 (patch size, temporal patch, merge size, encoder and patch
+ * merger) and section 3.3 (2D RoPE base, window-attention layers); vLLM PR
+ * #55370 report, implementation breakdown item 1 (the normaliser's rescale,
+ * mean and std are parameters of the tower, injected at construction).
+ * Errors: VIT_E_ARG for a NULL pointer or any out-of-range field; *out is
+ * NULL then.  The caller releases the context with vit_destroy. */
 vit_status vit_create(const vit_config* cfg, vit_ctx** out);
 
 /* Copies one host tensor into the context (host buffer may be freed after
- * the call).  Canonical names and shapes ([out, in] for linears):
+ * the call).  Defined by: vLLM PR #55370 report, key code (the tower's
+ * stacked-parameter mapping loads separate q, k, v projections into one qkv
+ * matrix) and "vLLM multimodal inference | ViT performance optimisation",
+ * section 3.2 (the patch-embedding conv weight reshaped to a 2D matrix).
+ * Errors: VIT_E_WEIGHTS for a duplicate name, VIT_E_SHAPE for a non-positive
+ * dimension, VIT_E_STATE after vit_finalize_weights, VIT_E_ARG for a NULL
+ * pointer or a dtype other than VIT_F32 / VIT_BF16 (bf16 given as raw uint16
+ * bits).  Names and shapes are checked against the tower by
+ * vit_finalize_weights.
+ * Canonical names and shapes ([out, in] for linears):
  *   pe.w [hidden][3][2][14][14] (or [hidden][1176])
  *   blk{l}.n1.g, blk{l}.n1.b (LayerNorm only), blk{l}.n2.g, blk{l}.n2.b  [hidden]
  *   blk{l}.qkv.w [3*hidden][hidden], blk{l}.qkv.b [3*hidden]
@@ -142,12 +158,25 @@ vit_status vit_load_weight(vit_ctx* ctx, const char* name, int32_t dtype, const 
 
 /* Checks completeness, packs (q/k/v stacking, RoPE pair order, K padding,
  * gate/up interleave) and uploads the weights into a device arena owned by
- * ctx.  Synchronises `stream` before returning.  ctx is read-only afterwards. */
+ * ctx.  Synchronises `stream` before returning.  ctx is read-only afterwards.
+ * Defined by: the same passages as vit_load_weight.  Errors: VIT_E_WEIGHTS
+ * names the first missing, unknown or mis-shaped tensor; VIT_E_HIP if the
+ * arena cannot be allocated or uploaded; VIT_E_STATE if called twice. */
 vit_status vit_finalize_weights(vit_ctx* ctx, void* stream);
 
 /* Pure host: validates the batch and builds every piece of per-forward
  * metadata (cu_seqlens, merge-ordered positions, window order, attention
- * work lists, RoPE cos/sin cache, workspace layout).
+ * work lists, RoPE cos/sin cache, workspace layout).  Defined by: "vLLM
+ * multimodal inference | ViT performance optimisation", section 2.2
+ * (grid_thw records each item's patch counts), section 3.3 (positions from
+ * grid_thw, cos/sin cache, window-attention order) and section 3.4
+ * (cu_seqlens built once per forward and shared by every layer).
+ * Errors (nothing allocated on the device, *out NULL): VIT_E_SHAPE for a bad
+ * (t, h, w) / n_frames pair, a side above 16384 patches, more than 2^28
+ * patches, a video frame of 2^31 bytes or more, or a batch whose largest
+ * device operand (normalised patches, norm output, MLP activation, merger
+ * views, their e4m3 residuals, per-head q / k / V^T) would reach 2 GiB
+ * (32-bit buffer addressing); VIT_E_ARG for NULL pointers.
  *   grid_thw [n_items][3] = (t, h, w) in patches; h, w even, t >= 1.
  *   n_frames [n_items]: 1 for an image (t must be 1; the frame is used for
  *     both temporal slots), or 2*t for a video.
@@ -156,7 +185,9 @@ vit_status vit_plan_create(const vit_ctx* ctx, const int32_t* grid_thw, const in
                            int32_t n_items, vit_plan** out);
 void vit_plan_destroy(vit_plan* plan);
 
-/* pixel_bytes = sum over items of n_frames*H*W*3 (H = 14h, W = 14w);
+/* Sizes of a plan ("vLLM multimodal inference | ViT performance
+ * optimisation", section 2.2: every 2x2 merge unit becomes one output token).
+ * pixel_bytes = sum over items of n_frames*H*W*3 (H = 14h, W = 14w);
  * ws_bytes = workspace the plan needs; out_rows = N/4 merged tokens;
  * out_cols = out_dim.  Any output pointer may be NULL. */
 vit_status vit_plan_sizes(const vit_plan* plan, size_t* pixel_bytes, size_t* ws_bytes,
@@ -168,6 +199,17 @@ vit_status vit_plan_sizes(const vit_plan* plan, size_t* pixel_bytes, size_t* ws_
 vit_status vit_plan_rows(const vit_plan* plan, int64_t* n_patches, int32_t* dst);
 
 /* Enqueues the whole forward on `stream` and returns without synchronising.
+ * Defined by: "vLLM multimodal inference | ViT performance optimisation",
+ * section 2.2 (encoding steps 1-4: patchify, patch embedding, 2D RoPE,
+ * encoder, patch merger); vLLM PR #55370 report, implementation breakdown
+ * items 1-2 (rescale + normalise of integer pixels is the tower's own first
+ * step, so every path normalises exactly once); "GPUModelRunner.execute_model"
+ * notes (an empty batch runs no forward).  Errors: VIT_E_STATE before
+ * vit_finalize_weights; VIT_E_ARG for a plan of another configuration, NULL
+ * pixels / out with patches to encode, or an unaligned workspace;
+ * VIT_E_WORKSPACE if ws_bytes is too small; VIT_E_HIP for a launch failure
+ * (earlier asynchronous faults also surface here).  A plan with no items
+ * returns VIT_OK and enqueues nothing (ws, pixels and out may then be NULL).
  *   pixels_u8: device, pixel_bytes; items in order, each n_frames frames of
  *              H x W x 3 uint8, HWC, RGB, row-major.
  *   ws:        device, >= ws_bytes, 256-byte aligned; contents are scratch.
@@ -175,7 +217,12 @@ vit_status vit_plan_rows(const vit_plan* plan, int64_t* n_patches, int32_t* dst)
 vit_status vit_encode(const vit_ctx* ctx, const vit_plan* plan, const uint8_t* pixels_u8, void* ws,
                       size_t ws_bytes, float* out, void* stream);
 
-/* Same forward from uint8 flatten_patches instead of frames:
+/* Same forward from uint8 flatten_patches instead of frames (the pages' own
+ * tower input: vLLM PR #55370 report, implementation breakdown item 2 and
+ * review highlights -- the tower receives integer pixels already cut into
+ * flatten_patches; "vLLM multimodal inference | ViT performance
+ * optimisation", sections 2.2 and 3.2).  Errors as vit_encode, plus VIT_E_ARG
+ * for a patches pointer that is not 8-byte aligned:
  *   patches_u8: device [N][1176] uint8 rows in merge order, features
  *   (channel, temporal slot, row, column). */
 vit_status vit_encode_patches_u8(const vit_ctx* ctx, const vit_plan* plan,
@@ -185,12 +232,23 @@ vit_status vit_encode_patches_u8(const vit_ctx* ctx, const vit_plan* plan,
 /* Captures the whole forward (normalisation included) into a HIP graph that
  * reads pixels from, and writes the output into, regions inside `ws`
  * (see vit_graph_io).  The plan's metadata is uploaded into ws before the
- * capture begins; the graph is bound to (ctx, plan, ws). */
+ * capture begins; the graph is bound to (ctx, plan, ws).  Defined by: vLLM
+ * PR #55370 report, implementation breakdown item 2 (normalisation captured
+ * with the encoder graph, the same call chain as eager) and review
+ * highlights item 3 (a uint8 graph input buffer: no per-replay cast);
+ * "GPUModelRunner.execute_model" notes, key files (graphs captured once at
+ * start against a locked workspace).  Errors as vit_encode; VIT_E_SHAPE for
+ * an empty plan; VIT_E_HIP if capture or instantiation fails.  The caller
+ * releases the graph with vit_graph_destroy before freeing ws. */
 vit_status vit_graph_capture(const vit_ctx* ctx, const vit_plan* plan, void* ws, size_t ws_bytes,
                              void* stream, vit_graph** out);
 /* Device addresses of the graph's uint8 pixel input (pixel_bytes) and
- * float32 output ([N/4][out_dim]) regions. */
+ * float32 output ([N/4][out_dim]) regions (same passages as
+ * vit_graph_capture).  Either output pointer may be NULL. */
 vit_status vit_graph_io(const vit_graph* g, uint8_t** pixels_in, float** out);
+/* Replays the captured forward on `stream` (asynchronous).  Replays of one
+ * graph share its workspace: issue them on one stream.  VIT_E_HIP if the
+ * launch fails. */
 vit_status vit_graph_launch(vit_graph* g, void* stream);
 void vit_graph_destroy(vit_graph* g);
 
@@ -224,7 +282,10 @@ vit_status vit_graph_launch_plan(vit_graph* g, const vit_plan* plan, void* strea
 
 /* Vision-embedding cache ("vLLM multimodal inference | ViT performance
  * optimisation", section 2.3: a vision-embedding cache shared across
- * requests).  Merged embeddings of items are kept in `arena` (device,
+ * requests).  Trusted input only: a hit is decided by the 128-bit content
+ * key (vit_pixel_keys) without comparing pixel bytes, and that key is not
+ * collision resistant against a deliberate search, so a cache shared between
+ * mutually untrusting clients could be fed crafted colliding pixels.  Merged embeddings of items are kept in `arena` (device,
  * caller-owned, 256-byte aligned, arena_bytes may be 0) and reused when an
  * item with the same pixel content key and the same grid (t, h, w, n_frames)
  * is encoded again through vit_encode_cached.  The arena is a ring with

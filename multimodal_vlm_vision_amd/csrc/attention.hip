@@ -176,8 +176,12 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
 
   // Direct global -> LDS tile loads through buffer resources over this head's K and V^T:
   // each lane keeps one 32-bit offset per load and the block's key offset rides in the
-  // scalar offset.  Keys past the segment end read the next segment's keys (or zeros past
-  // the end of the buffer); their scores are masked to -inf, so they contribute P = 0.
+  // scalar offset.  The buffer range check covers the lane offset only, not the scalar one,
+  // so reads past a segment's end are kept in bounds by the layout instead: K rows past the
+  // end are the next segment's (or, for the last head, the V^T region that follows K), and
+  // their scores are masked to -inf; a V^T row has at least 40 zeroed columns past the last
+  // token (the planner's pitch), which covers the farthest read (39 tokens past a segment),
+  // so the keys that get P = 0 multiply finite zeros, never stale memory.
   constexpr int KLW = (KLOADS + NW - 1) / NW, VLW = (VLOADS + NW - 1) / NW;
   const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kh), (short)0,
                                                     (int)(a.n_tok * HD * 2), kRsrcWord3);
@@ -349,7 +353,7 @@ hipError_t run_hd(const AttnArgs& a, hipStream_t st) {
 }
 
 // Zeroes V^T columns [n, n + 64) (clipped to the pitch) of every row: the attention's tile
-// loads read at most 40 keys past the last token.  n is the token count, read at run time
+// loads read at most 39 keys past the last token, and the pitch leaves at least 40 columns.  n is the token count, read at run time
 // when n_tok_dev is set (bucketed graph).
 __global__ void vt_pad_zero_kernel(uint16_t* vt, int rows, int64_t n_tok, const int32_t* n_tok_dev, int64_t vt_ld) {
   const int64_t n = n_tok_dev ? (int64_t)*n_tok_dev : n_tok;
@@ -377,9 +381,9 @@ vit_status launch_vt_pad_zero(uint16_t* vt, int rows, int64_t n_tok, int64_t vt_
 
 vit_status launch_attention(const AttnArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (a.vt_ld < a.n_tok || a.vt_ld % 8) {
-    set_error("attention: V^T pitch %lld must be a multiple of 8 and cover %lld tokens", (long long)a.vt_ld,
-              (long long)a.n_tok);
+  if (a.vt_ld < a.n_tok + 40 || a.vt_ld % 8) {
+    set_error("attention: V^T pitch %lld must be a multiple of 8 and cover %lld tokens plus 40 pad columns",
+              (long long)a.vt_ld, (long long)a.n_tok);
     return VIT_E_ARG;
   }
   if (a.vt_ld * a.head_dim * 2 >= ((int64_t)1 << 31)) {

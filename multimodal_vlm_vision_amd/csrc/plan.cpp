@@ -12,6 +12,7 @@
 //  - segment bounds for block-diagonal attention, computed once per forward
 //    and shared by every layer (section 3.4), as attention work lists.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 
@@ -115,6 +116,35 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   p->max_pos = max_pos;
   p->nfreq = ctx->head_dim / 4;
 
+  // ---- device operand extents: the GEMM and attention kernels address each operand with
+  // 32-bit buffer offsets, so every one must stay below 2 GiB.  Checked here so that a batch
+  // too large for them fails before anything is enqueued.
+  {
+    const int64_t N = n_rows, d = c.hidden;
+    const int64_t S = p->split, mp = p->mlp_pad, hd = p->head_dim, U = n_rows / 4;
+    const int64_t N16 = round_up(N, 16), U16 = round_up(U, 16), N32 = round_up(N, 32), U32 = round_up(U, 32);
+    const int64_t vt_ld = round_up(N, 8) + 40;
+    struct Extent {
+      const char* what;
+      int64_t bytes;
+    } ext[] = {{"normalised patches", N16 * kFeatPad * 2},
+               {"norm output", N16 * S * d * 2},
+               {"merger input", U16 * 4 * S * d * 2},
+               {"attention output", N16 * d * 2},
+               {"MLP activation", N16 * S * mp * 2},
+               {"merger hidden", U16 * 4 * S * d * 2},
+               {"e4m3 norm residual", p->f8 ? std::max(N32 * d, U32 * 4 * d) : 0},
+               {"e4m3 MLP residual", p->f8 ? std::max(N32 * mp, U32 * 4 * d) : 0},
+               {"per-head q or k", N * hd * 2},
+               {"per-head V^T", vt_ld * hd * 2}};
+    for (const Extent& e : ext)
+      if (e.bytes >= ((int64_t)1 << 31)) {
+        set_error("batch of %lld patches: the %s operand would take %lld bytes; at most 2^31 - 1 are "
+                  "addressable", (long long)N, e.what, (long long)e.bytes);
+        return VIT_E_SHAPE;
+      }
+  }
+
   // ---- rows in internal order
   const int wu = c.window_px > 0 ? c.window_px / kUnitPx : 0;   // window side in merge units
   std::vector<UnitDesc> units;
@@ -131,6 +161,12 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
     const int32_t nf = n_frames[i];
     const int64_t W = (int64_t)kPatch * w, H = (int64_t)kPatch * h;
     const int64_t frame_bytes = H * W * 3;
+    if (nf > 1 && frame_bytes > INT32_MAX) {
+      // the unit descriptors hold the frame stride as a 32-bit byte count
+      set_error("item %d: a %lld x %lld video frame (%lld bytes) exceeds the 2^31-byte frame limit", i,
+                (long long)H, (long long)W, (long long)frame_bytes);
+      return VIT_E_SHAPE;
+    }
     const int32_t uh = h / kMerge, uw = w / kMerge;
     item_segs.push_back({(int32_t)(unit_base * 4), t * h * w});
     for (int32_t ti = 0; ti < t; ++ti) {
@@ -215,7 +251,11 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   p->off_h = take((size_t)std::max(Np * S * d, Up * 4 * S * d) * 2);
   p->off_q = take((size_t)N * d * 2);
   p->off_k = take((size_t)N * d * 2);
-  p->vt_ld = round_up(N, 8);   // 16-byte aligned V^T rows for the attention's tile loads
+  // V^T rows: 16-byte aligned for the attention's whole-chunk tile loads, with at least 40
+  // columns past the last token that are zeroed every forward.  A key block's load reaches up
+  // to 39 tokens past a segment's last key (keys that get probability 0); those columns must
+  // hold finite values, since 0 * NaN is NaN inside the MFMA, and must stay inside the row.
+  p->vt_ld = round_up(N, 8) + 40;
   p->off_vt = take((size_t)p->vt_ld * d * 2);
   p->off_o = take((size_t)Np * d * 2);
   p->off_f = take((size_t)std::max(Np * S * p->mlp_pad, Up * 4 * S * d) * 2);

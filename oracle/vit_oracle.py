@@ -66,7 +66,11 @@ _ROW_BLOCK = 2048
 
 
 def _threads() -> int:
-    return max(1, len(os.sched_getaffinity(0)))
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:   # the CPU share this process is given
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def _pool() -> ThreadPoolExecutor:
@@ -395,11 +399,13 @@ def merger(r: np.ndarray, weights: Dict[str, np.ndarray], cfg, trace: Optional[d
 
 def forward(items_frames: Sequence[np.ndarray], grid_thw: np.ndarray, cfg,
             weights: Dict[str, np.ndarray], dtype=np.float64, layers: Optional[int] = None,
-            trace: Optional[dict] = None) -> np.ndarray:
+            trace: Optional[dict] = None, progress: Optional[Callable[[int], None]] = None
+            ) -> np.ndarray:
     """uint8 frames -> merged embeddings [N/4][out_dim], items in order.
 
     trace (optional dict) receives: "x" (normalised patches), "r0" (patch
     embedding), "r" (list of block outputs), "merger" (merger intermediates).
+    progress (optional) is called with each layer index once that block is done.
     """
     n_layers = cfg.layers if layers is None else layers
     table = normalize_table(cfg.mean, cfg.std)
@@ -413,6 +419,8 @@ def forward(items_frames: Sequence[np.ndarray], grid_thw: np.ndarray, cfg,
         r = block(r, weights, l, cfg, angles, layer_segments(l, cfg, pos))
         if trace is not None:
             trace["r"].append(r.copy())
+        if progress is not None:
+            progress(l)
     mt = {} if trace is not None else None
     out = merger(r, weights, cfg, trace=mt)
     if trace is not None:
@@ -421,10 +429,11 @@ def forward(items_frames: Sequence[np.ndarray], grid_thw: np.ndarray, cfg,
 
 
 def forward_workload(wl, dtype=np.float64, layers: Optional[int] = None,
-                     items: Optional[Sequence[int]] = None, trace: Optional[dict] = None
-                     ) -> np.ndarray:
+                     items: Optional[Sequence[int]] = None, trace: Optional[dict] = None,
+                     progress: Optional[Callable[[int], None]] = None) -> np.ndarray:
     """forward() on a `workloads.Workload`, optionally on a subset of its items."""
     sel = list(range(len(wl.items))) if items is None else list(items)
     frames = [wl.items[i].frames for i in sel]
     grid = np.array([wl.items[i].grid_thw for i in sel], dtype=np.int64).reshape(-1, 3)
-    return forward(frames, grid, wl.cfg, wl.weights, dtype=dtype, layers=layers, trace=trace)
+    return forward(frames, grid, wl.cfg, wl.weights, dtype=dtype, layers=layers, trace=trace,
+                   progress=progress)

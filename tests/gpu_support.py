@@ -41,6 +41,34 @@ class GpuRun:
         torch.cuda.synchronize()
         return self.out[: self.plan.out_rows].cpu().numpy().astype(np.float64)
 
+    def graph_encode(self, replays: int = 2) -> np.ndarray:
+        """The output of the captured whole-encoder graph (vit_graph_capture, then
+        vit_graph_launch): the pixels are written into the graph's uint8 input region and the
+        graph is replayed `replays` times, with eager work between replays; every replay must
+        give the same bytes.  Returns the first replay's output."""
+        gws = torch.empty(self.plan.ws_bytes, dtype=torch.uint8, device="cuda")
+        g = self.tower.capture(self.plan, gws)
+        try:
+            off = g.pixels_ptr - gws.data_ptr()
+            gws[off:off + self.pixels.numel()].copy_(self.pixels)
+            out_off = g.out_ptr - gws.data_ptr()
+            rows, cols = self.plan.out_rows, self.cfg.out_dim
+            first = None
+            for rep in range(replays):
+                g.launch()
+                torch.cuda.synchronize()
+                got = gws[out_off:out_off + rows * cols * 4].view(torch.float32).reshape(rows, cols).cpu().numpy()
+                if first is None:
+                    first = got
+                else:
+                    assert np.array_equal(got, first), f"graph replay {rep} differs from replay 0"
+                if rep + 1 < replays:
+                    self.encode()          # eager work on another workspace between replays
+        finally:
+            g.close()
+            del gws
+        return first.astype(np.float64)
+
     def _join(self, a: np.ndarray, width: int, keep: int) -> np.ndarray:
         """[rows][S*width] stored activations -> values (hi + lo when split), first `keep` columns."""
         if self.S == 2:
@@ -85,6 +113,29 @@ class GpuRun:
         else:
             out[self.perm] = a
         return out
+
+
+def progress_log(msg: str):
+    """Appends a progress line of a long test step to gpurun_out/gpu_tests_progress.log (test
+    output is captured until a test ends; this file shows a long oracle run advancing)."""
+    import os
+    import time
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    d = os.path.join(root, "gpurun_out")
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "gpu_tests_progress.log"), "a") as f:
+        f.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
+
+
+def per_item_errors(got: np.ndarray, ref: np.ndarray, items) -> list:
+    """(max_abs, mean_rel) of each item's merged rows (output rows are in item order)."""
+    out, r0 = [], 0
+    for it in items:
+        r1 = r0 + it.n_patches // 4
+        g, r = got[r0:r1], ref[r0:r1]
+        out.append((float(np.abs(g - r).max()), rel_err(g, r)))
+        r0 = r1
+    return out
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -78,6 +78,40 @@ def test_plan_validation(lib, grid, frames, status):
     assert _status(lambda: t.plan(grid, frames)) == status
 
 
+def test_plan_rejects_batches_beyond_32bit_operand_addressing(lib):
+    """Every GEMM / attention operand is addressed with 32-bit buffer offsets.  A batch whose
+    largest operand would reach 2 GiB is refused by vit_plan_create (pure host), so it never
+    fails half-way through an enqueued forward.  bf16 + e4m3 activations, GELU width 5120:
+    the MLP activation [N][5120] bf16 crosses 2 GiB at N = 209,716 patches."""
+    t = B.VisionTower(tower_config(3), lib, activation_precision="bf16f8")
+    limit = (1 << 31) // (5120 * 2)            # largest N (multiple of 16) whose activation fits
+    side = 2 * int(np.sqrt(limit / 4))         # an even square grid just below it
+    ok = t.plan([[1, side, side]], [1])
+    assert ok.n_patches == side * side < limit
+    # the same patch count plus one more image of 16 rows of 2x2 units crosses the limit
+    rows = (limit - side * side) // side + 2
+    rows += rows % 2
+    assert side * (side + rows) > limit
+    assert _status(lambda: t.plan([[1, side, side], [1, rows, side]], [1, 1])) == B.VIT_E_SHAPE
+    assert b"MLP activation" in lib.vit_last_error()
+    # hi+lo pairs double the activation width: the limit halves
+    t2 = B.VisionTower(tower_config(3), lib, activation_precision="bf16x2")
+    assert _status(lambda: t2.plan([[1, side, side]], [1])) == B.VIT_E_SHAPE
+
+
+def test_plan_rejects_video_frames_beyond_32bit_stride(lib):
+    """A video frame of 2^31 bytes or more cannot be described by the unit descriptors'
+    32-bit frame stride; the planner refuses it (the operand-extent check, which comes
+    first, already covers every such frame at these tower widths)."""
+    t = B.VisionTower(tower_config(4), lib)
+    side = 2 * 1024                             # 28672 px square frames, 2.47 GB each
+    assert 3 * (14 * side) ** 2 > (1 << 31)
+    assert _status(lambda: t.plan([[1, side, side]], [2])) == B.VIT_E_SHAPE
+    # an image of the same size is read once per slot and has no frame stride; it is still
+    # refused, by the operand extents
+    assert _status(lambda: t.plan([[1, side, side]], [1])) == B.VIT_E_SHAPE
+
+
 def test_empty_batch_is_a_noop(lib):
     t = B.VisionTower(tower_config(1), lib)
     p = t.plan(np.zeros((0, 3), np.int32), np.zeros(0, np.int32))

@@ -98,18 +98,16 @@ typedef struct vit_config {
   int32_t window_px;        /* 0: no window attention; else window side in pixels (multiple of 28) */
   int32_t n_full_attn_layers;
   int32_t full_attn_layers[VIT_MAX_FULL_LAYERS]; /* 0-based layers that attend over whole items */
-  /* VIT_ACT_BF16X2: each norm output, MLP activation and merger activation x is
-   * stored as hi = bf16(x), lo = bf16(x - hi) and the GEMM that consumes it runs
-   * over both halves against the same bf16 weights (twice the MFMA work of the
-   * qkv, MLP and merger products), which removes their activation rounding;
-   * q, k, v, the attention probabilities and the attention output stay
-   * single bf16.  VIT_ACT_BF16F8 keeps the same activations as hi = bf16(x)
-   * plus the residual x - hi in OCP e4m3 (scaled by 2^9); the GEMM adds the
-   * residual's product against an e4m3 copy of the weights (per-row power-of-two
-   * scales) through the scaled fp8 MFMA, so the residual costs half the MFMA
-   * time of a second bf16 product and 1 instead of 2 bytes per element (its
-   * error, ~2^-12 of x, stays far below the bf16 rounding it compensates).
-   * VIT_ACT_BF16 rounds every GEMM activation once. */
+  /* VIT_ACT_BF16X2: each norm output, attention output, MLP activation and merger
+   * activation x is stored as hi = bf16(x), lo = bf16(x - hi) and the GEMM that consumes it
+   * runs over both halves against the same bf16 weights (twice the MFMA work of those
+   * products), which removes their activation rounding; q, k, v and the attention
+   * probabilities stay single bf16.  VIT_ACT_BF16F8 keeps the same activations as
+   * hi = bf16(x) plus the residual x - hi in OCP e4m3 (scaled by 2^9); the GEMM adds the
+   * residual's product against an e4m3 copy of the weights (per-row power-of-two scales)
+   * through the scaled fp8 MFMA, so the residual costs half the MFMA time of a second bf16
+   * product and 1 instead of 2 bytes per element (its error, ~2^-12 of x, stays far below
+   * the bf16 rounding it compensates).  VIT_ACT_BF16 rounds every GEMM activation once. */
   int32_t activation_precision;
 } vit_config;
 
@@ -368,7 +366,7 @@ vit_status vit_encode_profiled(const vit_ctx* ctx, const vit_plan* plan, const u
  *               2 q after RoPE, times log2(e)/sqrt(head_dim) (the scale the attention
  *                 kernel expects, applied before rounding), bf16 [heads][N][head_dim];
  *               3 k bf16 [heads][N][head_dim]; 4 v bf16 [heads][head_dim][N];
- *               5 attention bf16 [N][hidden]; 6 residual after out-proj f32 [N][hidden];
+ *               5 attention bf16 [N][S*hidden]; 6 residual after out-proj f32 [N][hidden];
  *               7 norm2 bf16 [N][S*hidden]; 8 MLP activation bf16 [N][S*mlp_pad];
  *               9 block output f32 [N][hidden]
  *   layer = layers: 1 merger norm bf16 [N][S*hidden]; 2 merger hidden bf16 [N/4][S*4*hidden];

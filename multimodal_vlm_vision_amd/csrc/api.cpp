@@ -188,6 +188,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   uint16_t* F = reinterpret_cast<uint16_t*>(ws + pl->off_f);
   uint8_t* H8 = f8 ? reinterpret_cast<uint8_t*>(ws + pl->off_h8) : nullptr;
   uint8_t* F8 = f8 ? reinterpret_cast<uint8_t*>(ws + pl->off_f8) : nullptr;
+  uint8_t* O8 = f8 ? reinterpret_cast<uint8_t*>(ws + pl->off_o8) : nullptr;
   // debug copies of the compensated activations: [hi | lo] rows in either form
   auto copy_act = [&](const uint16_t* src, const uint8_t* src8, int64_t rows, int cols, int group) {
     return f8 ? copy_blocked_f8(stop, src, src8, rows, cols, group, cols, st)
@@ -248,7 +249,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     const bool windowed = c.window_px > 0 && !ctx->is_full_layer(l);
     const AttnLists& lists = windowed ? pl->win : pl->full;
     AttnArgs at;
-    at.q = Q; at.k = K; at.vt = VT; at.o = O; at.n_tok = N; at.vt_ld = pl->vt_ld;
+    at.q = Q; at.k = K; at.vt = VT; at.o = O; at.o_split = split; at.o8 = O8; at.n_tok = N; at.vt_ld = pl->vt_ld;
     at.heads = c.heads; at.head_dim = hd;
     at.work_long = reinterpret_cast<const AttnWork*>(ws + lists.off_long);
     at.work_short = reinterpret_cast<const AttnWork*>(ws + lists.off_short);
@@ -264,11 +265,16 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
       if (dims) a2.n_short_dev = windowed ? &dims->win_short : &dims->full_short;
       LAUNCH("attention_short", 4.0 * dd * lists.sq_short, 0, true, launch_attention(a2, st));
     }
-    if (stop.hit(l, 5)) return copy_blocked(stop, O, N, d, 1, d, st);
+    if (stop.hit(l, 5)) return copy_act(O, O8, N, d, 1);
 
+    // the attention output is compensated like the other GEMM activations: its bf16 rounding
+    // is the largest single error source at depth once those are compensated
     GemmArgs pj;
-    pj.A = O; pj.lda = d; pj.B = L.proj_w; pj.ldb = d;
+    pj.A = O; pj.lda = S * d; pj.B = L.proj_w; pj.ldb = d; pj.a_group = split ? d : 0;
     pj.M = (int)N; pj.N = d; pj.K = d; pj.bias = L.proj_b; pj.out = R; pj.ldo = d; pj.m_dev = rows_dev;
+    if (f8) {
+      pj.A8 = O8; pj.lda8 = d; pj.B8 = L.proj_w8; pj.ldb8 = d; pj.b8_scale = L.proj_s8;
+    }
     LAUNCH("gemm_proj_residual", 2.0 * Nd * dd * dd, 0, true, launch_gemm(EPI_RES, pj, st));
     if (stop.hit(l, 6)) return copy_out(stop, R, (size_t)N * d * 4, st);
 

@@ -90,6 +90,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+// x - bf16(x): what the bf16 rounding of x leaves out
+__device__ __forceinline__ float bf16_rest(float x) { return x - (float)(__bf16)x; }
+
+// four residuals x - bf16(x), times 2^kLoShift and clamped to e4m3's finite range, as four OCP
+// e4m3 bytes (round to nearest even): the compensated-activation format the GEMMs read
+__device__ __forceinline__ uint32_t rest_e4m3x4(float a, float b, float c, float d) {
+  constexpr float s = (float)(1 << kLoShift);
+  auto f = [](float x) { return fminf(fmaxf(bf16_rest(x) * s, -448.0f), 448.0f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f(a), f(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f(c), f(d), lo, true);
+}
+
 // DYN: the work-list length comes from device memory at run time (bucketed graphs); a separate
 // instantiation, so the plain path keeps it a launch constant.
 template <int HD, int NW, bool DYN>
@@ -308,7 +320,8 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
   }
 
   if (qbase >= n) return;
-  const int ld = a.heads * HD;
+  const int hid = a.heads * HD;
+  const int ld = a.o_split ? 2 * hid : hid;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int q = qbase + 32 * t + l32;
@@ -317,7 +330,8 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
     const float lsum = LHALF == 0 ? from_lower_half(lsum_own) : from_upper_half(lsum_own);
     if (q < n) {
       const float inv = 1.0f / lsum;
-      // output row in the blocked GEMM layout (the out-projection's A operand); 4 values per store
+      // output row in the blocked GEMM layout (the out-projection's A operand); 4 values per
+      // store, plus what their bf16 rounding leaves out when the out-projection compensates it
       const int64_t orow = seg0 + q;
       const int ocol = head * HD + 4 * h;
 #pragma unroll
@@ -327,9 +341,15 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
           const int d = 32 * dt + 8 * g;   // + 4h + e
           if (d + 8 > HD) continue;
           const f32x16& o = O[t][dt];
+          const float y0 = o[4 * g] * inv, y1 = o[4 * g + 1] * inv, y2 = o[4 * g + 2] * inv,
+                      y3 = o[4 * g + 3] * inv;
           *reinterpret_cast<uint2*>(a.o + kt_index(orow, ocol + d, ld)) =
-              make_uint2(pack_bf16(o[4 * g] * inv, o[4 * g + 1] * inv),
-                         pack_bf16(o[4 * g + 2] * inv, o[4 * g + 3] * inv));
+              make_uint2(pack_bf16(y0, y1), pack_bf16(y2, y3));
+          if (a.o_split)
+            *reinterpret_cast<uint2*>(a.o + kt_index(orow, hid + ocol + d, ld)) =
+                make_uint2(pack_bf16(bf16_rest(y0), bf16_rest(y1)), pack_bf16(bf16_rest(y2), bf16_rest(y3)));
+          if (a.o8)
+            *reinterpret_cast<uint32_t*>(a.o8 + kt8_index(orow, ocol + d, hid)) = rest_e4m3x4(y0, y1, y2, y3);
         }
     }
   }

@@ -130,7 +130,8 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
     } ext[] = {{"normalised patches", N16 * kFeatPad * 2},
                {"norm output", N16 * S * d * 2},
                {"merger input", U16 * 4 * S * d * 2},
-               {"attention output", N16 * d * 2},
+               {"attention output", N16 * S * d * 2},
+               {"e4m3 attention residual", p->f8 ? N32 * d : 0},
                {"MLP activation", N16 * S * mp * 2},
                {"merger hidden", U16 * 4 * S * d * 2},
                {"e4m3 norm residual", p->f8 ? std::max(N32 * d, U32 * 4 * d) : 0},
@@ -257,12 +258,13 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   // hold finite values, since 0 * NaN is NaN inside the MFMA, and must stay inside the row.
   p->vt_ld = round_up(N, 8) + 40;
   p->off_vt = take((size_t)p->vt_ld * d * 2);
-  p->off_o = take((size_t)Np * d * 2);
+  p->off_o = take((size_t)Np * S * d * 2);
   p->off_f = take((size_t)std::max(Np * S * p->mlp_pad, Up * 4 * S * d) * 2);
   if (p->f8) {   // e4m3 residuals of H and F: rows padded to whole 32-row groups
     const int64_t N32 = round_up(N, 32), U32 = round_up(N / 4, 32);
     p->off_h8 = take((size_t)std::max(N32 * d, U32 * 4 * d));
     p->off_f8 = take((size_t)std::max(N32 * p->mlp_pad, U32 * 4 * d));
+    p->off_o8 = take((size_t)N32 * d);
   }
   p->off_pix = take(px);
   p->off_out = take((size_t)p->n_units * c.out_dim * 4);

@@ -130,6 +130,7 @@ struct LayerW {
   // VIT_ACT_BF16F8: e4m3 copies of the weights that multiply compensated activations
   // (kt8_index layout, same shapes) and their per-row E8M0 scales (row n holds W[n] * 2^(127 - s[n]))
   const uint8_t* qkv_w8 = nullptr;  const uint8_t* qkv_s8 = nullptr;
+  const uint8_t* proj_w8 = nullptr; const uint8_t* proj_s8 = nullptr;
   const uint8_t* fc1_w8 = nullptr;  const uint8_t* fc1_s8 = nullptr;
   const uint8_t* fc2_w8 = nullptr;  const uint8_t* fc2_s8 = nullptr;
 };
@@ -190,6 +191,7 @@ struct vit_plan {
   // workspace layout (byte offsets; all 256-byte aligned)
   size_t off_x = 0, off_r = 0, off_h = 0, off_q = 0, off_k = 0, off_vt = 0, off_o = 0, off_f = 0;
   size_t off_h8 = 0, off_f8 = 0;  // e4m3 residuals of H and F (VIT_ACT_BF16F8)
+  size_t off_o8 = 0;              // e4m3 residual of the attention output O (VIT_ACT_BF16F8)
   size_t off_pix = 0, off_out = 0, ws_bytes = 0;
   int64_t vt_ld = 0;              // V^T row pitch (tokens), N rounded up to 8
 };
@@ -295,7 +297,12 @@ vit_status launch_unblock_f8(const uint16_t* src, const uint8_t* src8, int64_t r
 
 struct AttnArgs {
   const uint16_t* q = nullptr; const uint16_t* k = nullptr; const uint16_t* vt = nullptr;
+  // output in the blocked GEMM layout: hi = bf16(o) rows of o_ld columns; with o_split the
+  // row is [hi(hidden) | lo(hidden)] (o_ld = 2 * hidden, lo = bf16(o - hi)); with o8 the
+  // e4m3 residual (o - hi) * 2^kLoShift goes to a kt8_index matrix of hidden columns
   uint16_t* o = nullptr;
+  bool o_split = false;
+  uint8_t* o8 = nullptr;
   int64_t n_tok = 0;
   int64_t vt_ld = 0;   // V^T row pitch in tokens: a multiple of 8, pad columns finite (zero)
   int heads = 0, head_dim = 0;

@@ -189,7 +189,7 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
 
   struct LayerOff {
     size_t n1g, n1b, n2g, n2b, qkv_w, qkv_b, proj_w, proj_b, fc1_w, fc1_b, fc2_w, fc2_b;
-    size_t qkv_w8 = 0, qkv_s8 = 0, fc1_w8 = 0, fc1_s8 = 0, fc2_w8 = 0, fc2_s8 = 0;
+    size_t qkv_w8 = 0, qkv_s8 = 0, proj_w8 = 0, proj_s8 = 0, fc1_w8 = 0, fc1_s8 = 0, fc2_w8 = 0, fc2_s8 = 0;
   };
   const bool f8 = ctx->f8;
   std::vector<LayerOff> lo(c.layers);
@@ -256,7 +256,9 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
     const HostTensor* pw = P.get(p + "proj.w", {d, d});
     const HostTensor* pb = P.get(p + "proj.b", {d});
     if (!pw || !pb) goto fail;
-    L.proj_w = P.mat(d, d, [&](int64_t o, int64_t k) { return pw->data[o * d + k]; });
+    auto proj_src = [&](int64_t o, int64_t k) { return pw->data[o * d + k]; };
+    L.proj_w = P.mat(d, d, proj_src);
+    if (f8) L.proj_w8 = P.mat8(d, d, proj_src, L.proj_s8);
     L.proj_b = P.vec(d, [&](int64_t i) { return pb->data[i]; });
 
     if (c.mlp_kind == VIT_MLP_GELU) {
@@ -385,6 +387,7 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
       X.fc1_w = bf(L.fc1_w); X.fc1_b = fl(L.fc1_b);
       X.fc2_w = bf(L.fc2_w); X.fc2_b = fl(L.fc2_b);
       X.qkv_w8 = b8(L.qkv_w8); X.qkv_s8 = b8(L.qkv_s8);
+      X.proj_w8 = b8(L.proj_w8); X.proj_s8 = b8(L.proj_s8);
       X.fc1_w8 = b8(L.fc1_w8); X.fc1_s8 = b8(L.fc1_s8);
       X.fc2_w8 = b8(L.fc2_w8); X.fc2_s8 = b8(L.fc2_s8);
     }

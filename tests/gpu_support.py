@@ -88,14 +88,14 @@ class GpuRun:
         else:
             shape, dt = {1: ((n, S * d), torch.bfloat16), 2: ((h, n, hd), torch.bfloat16),
                          3: ((h, n, hd), torch.bfloat16), 4: ((h, hd, n), torch.bfloat16),
-                         5: ((n, d), torch.bfloat16), 6: ((n, d), torch.float32),
+                         5: ((n, S * d), torch.bfloat16), 6: ((n, d), torch.float32),
                          7: ((n, S * d), torch.bfloat16), 8: ((n, S * self.mlp_pad), torch.bfloat16),
                          9: ((n, d), torch.float32)}[step]
         dst = torch.empty(shape, dtype=dt, device="cuda")
         self.tower.debug_stage(self.plan, self.pixels, self.ws, layer, step, dst)
         torch.cuda.synchronize()
         a = to_np(dst)
-        if (layer == L and step == 1) or (0 <= layer < L and step in (1, 7)):
+        if (layer == L and step == 1) or (0 <= layer < L and step in (1, 5, 7)):
             a = self._join(a, d, d)
         elif 0 <= layer < L and step == 8:
             a = self._join(a, self.mlp_pad, c.mlp_dim)

@@ -148,7 +148,8 @@ def check_block(run, layer):
 
     r1g = run.stage(layer, 6)
     r1 = r_in + og @ W64(run, p + ".proj.w").T + W64(run, p + ".proj.b")
-    assert_close_bf16(r1g, r1, rel=1e-5, abs_=2e-4, what=f"L{layer} out-proj+residual")
+    assert_close_bf16(r1g, r1, rel=1e-5, abs_=2e-4, what=f"L{layer} out-proj+residual",
+                      extra=f8_extra(run, og, W64(run, p + ".proj.w")))
 
     h2 = run.stage(layer, 7)
     assert_close_bf16(h2, O.norm(r1g, run.wl.weights, p + ".n2", c.norm_kind, c.norm_eps),

@@ -39,23 +39,22 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, n_items=3):
+def cpu_baseline(wl, items=None):
+    """The CPU oracle (float32 NumPy, the precision it uses for the 1280-wide towers) on the
+    headline batch -- every item, or the given subset -- timed around the forward only
+    (inputs drawn beforehand), on this host's cores.  `cores` = the oracle's worker threads."""
     import numpy as np
     from oracle import vit_oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    sizes = [it.n_patches for it in wl.items]
-    pick = sorted(range(len(sizes)), key=lambda i: sizes[i])[:n_items]
-    n = sum(sizes[i] for i in pick)
+    sel = list(range(len(wl.items))) if items is None else list(items)
+    n = sum(wl.items[i].n_patches for i in sel)
+    threads = vit_oracle._threads()
     t0 = time.perf_counter()
-    vit_oracle.forward_workload(wl, items=pick, dtype=np.float64)
+    vit_oracle.forward_workload(wl, items=sel, dtype=np.float32)
     dt = time.perf_counter() - t0
+    what = "the whole batch" if len(sel) == len(wl.items) else f"items {sel} of the batch"
     return {"value": n / dt, "unit": "patches/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(pick)} smallest images of the batch ({n} patches), all 32 layers + merger, "
-                      f"float64 NumPy, {dt:.1f} s"}
+            "sample": f"{what} ({n} patches), all {wl.cfg.layers} layers + merger, float32 NumPy "
+                      f"(BLAS and a {threads}-thread pool), {dt:.1f} s"}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen2vl-8img-mixed-32L.md")
@@ -250,6 +249,107 @@ def bucket_replay(tower, plan, wl, steps, warmup, stream):
             "subset_overhead_pct": 100.0 * (sub_ms / exact_ms - 1.0)}
 
 
+def kernel_breakdown(tower, plan, pixels, ws, out, stream, steps):
+    """Per-kernel-class totals from hipEvents around every launch (vit_encode_profiled) over
+    `steps` eager forwards: {name: {launches, total_ms, flops, bytes, mfma_bound}}."""
+    agg = {}
+    for _ in range(steps):
+        for k in tower.encode_profiled(plan, pixels, ws, out, stream):
+            a = agg.setdefault(k["name"], {"launches": 0, "total_ms": 0.0, "flops": 0.0, "bytes": 0.0,
+                                           "mfma_bound": k["mfma_bound"]})
+            for f in ("launches", "total_ms", "flops", "bytes"):
+                a[f] += k[f]
+    return agg
+
+
+def kernel_table(agg, steps):
+    kern = {}
+    tot_ms = sum(a["total_ms"] for a in agg.values())
+    for name, a in sorted(agg.items(), key=lambda kv: -kv[1]["total_ms"]):
+        avg_ms = a["total_ms"] / a["launches"]
+        e = {"launches_per_step": a["launches"] // steps, "avg_us": avg_ms * 1e3,
+             "share_pct": 100.0 * a["total_ms"] / tot_ms}
+        if a["mfma_bound"]:
+            e["tflops"] = a["flops"] / (a["total_ms"] * 1e-3) / 1e12
+            e["mfma_pct"] = 100.0 * e["tflops"] / PEAK_BF16_TFLOPS
+        else:
+            e["gbs"] = a["bytes"] / (a["total_ms"] * 1e-3) / 1e9
+            e["hbm_pct"] = 100.0 * e["gbs"] / PEAK_HBM_GBS
+        kern[name] = e
+    return kern
+
+
+def roofline_of(agg, name):
+    a = agg[name]
+    per_launch_ms = a["total_ms"] / a["launches"]
+    if a["mfma_bound"]:
+        achieved = a["flops"] / a["launches"] / (per_launch_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "kernel": name,
+                "avg_launch_us": per_launch_ms * 1e3}
+    achieved = a["bytes"] / a["launches"] / (per_launch_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": name,
+            "avg_launch_us": per_launch_ms * 1e3}
+
+
+def measure_workload(index, steps, warmup, activations, stream):
+    """Graph and eager throughput of one of the other workloads, with its per-kernel breakdown
+    and the roofline fraction of its dominant kernel."""
+    import torch
+    from multimodal_vlm_vision_amd import VisionTower
+    from workloads import make_workload, pack_pixels
+
+    t0 = time.perf_counter()
+    wl = make_workload(index)
+    cfg = wl.cfg
+    tower = VisionTower(cfg, activation_precision=activations)
+    tower.load_weights(wl.weights)
+    tower.finalize()
+    plan = tower.plan(wl.grid_thw, wl.n_frames)
+    pixels = torch.from_numpy(pack_pixels(wl.items)).cuda()
+    ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(plan.out_rows, plan.out_cols, dtype=torch.float32, device="cuda")
+    gws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device="cuda")
+    graph = tower.capture(plan, gws)
+    off = graph.pixels_ptr - gws.data_ptr()
+    gws[off:off + pixels.numel()].copy_(pixels)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / steps * 1e3
+
+    graph_ms = timed(lambda: graph.launch(stream))
+    eager_ms = timed(lambda: tower.encode(plan, pixels, ws, out, stream))
+    graph.close()
+    del gws
+    agg = kernel_breakdown(tower, plan, pixels, ws, out, stream, steps)
+    kern = kernel_table(agg, steps)
+    dom = max(agg, key=lambda n: agg[n]["total_ms"])
+    flops_step = sum(a["flops"] for a in agg.values()) / steps
+    res = {"workload": cfg.name, "items": len(wl.items), "patches": wl.n_patches, "layers": cfg.layers,
+           "graph_ms": graph_ms, "eager_ms": eager_ms, "graph_patches_per_s": wl.n_patches / (graph_ms * 1e-3),
+           "eager_patches_per_s": wl.n_patches / (eager_ms * 1e-3),
+           "mfma_util_pct": 100.0 * flops_step / (graph_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+           "algorithmic_tflop_per_step": flops_step / 1e12, "roofline": roofline_of(agg, dom),
+           "kernels": kern}
+    log(f"workload {cfg.name}: N={wl.n_patches}, graph {graph_ms:.3f} ms ({res['graph_patches_per_s']:,.0f} "
+        f"patches/s), eager {eager_ms:.3f} ms, MFMA {res['mfma_util_pct']:.1f}% of peak "
+        f"({time.perf_counter() - t0:.1f} s)")
+    for name, e in kern.items():
+        log(f"    {name:24s} {e['share_pct']:5.1f}%  avg {e['avg_us']:9.1f} us  " +
+            (f"{e['tflops']:7.1f} TFLOP/s ({e['mfma_pct']:.1f}% MFMA)" if "tflops" in e
+             else f"{e['gbs']:7.1f} GB/s ({e['hbm_pct']:.1f}% HBM)"))
+    tower.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +364,10 @@ def main():
     ap.add_argument("--no-bucket", action="store_true", help="skip the shape-bucketed graph measurement")
     ap.add_argument("--no-cache", action="store_true", help="skip the embedding-cache measurement")
     ap.add_argument("--no-resize", action="store_true", help="skip the device-resize measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (448 px tower, 16-frame video, Qwen2.5-shaped batch)")
+    ap.add_argument("--cpu-items", default="all",
+                    help="items of the batch the CPU oracle runs on: 'all' or a comma list of indices")
     ap.add_argument("--activations", default="bf16f8", choices=["bf16f8", "bf16x2"],
                     help="form of the compensated GEMM activations (bf16 + e4m3 residual, or hi+lo bf16 pairs)")
     args = ap.parse_args()
@@ -322,42 +426,14 @@ def main():
     eager_ms = (time.perf_counter() - t2) / args.steps * 1e3
 
     # ---- per-kernel breakdown: hipEvents around every launch, same stream
-    agg = {}
-    for _ in range(args.steps):
-        for k in tower.encode_profiled(plan, pixels, ws, out, stream):
-            a = agg.setdefault(k["name"], {"launches": 0, "total_ms": 0.0, "flops": 0.0, "bytes": 0.0,
-                                           "mfma_bound": k["mfma_bound"]})
-            for f in ("launches", "total_ms", "flops", "bytes"):
-                a[f] += k[f]
-    kern = {}
-    tot_ms = sum(a["total_ms"] for a in agg.values())
-    for name, a in sorted(agg.items(), key=lambda kv: -kv[1]["total_ms"]):
-        avg_ms = a["total_ms"] / a["launches"]
-        e = {"launches_per_step": a["launches"] // args.steps, "avg_us": avg_ms * 1e3,
-             "share_pct": 100.0 * a["total_ms"] / tot_ms}
-        if a["mfma_bound"]:
-            e["tflops"] = a["flops"] / (a["total_ms"] * 1e-3) / 1e12
-            e["mfma_pct"] = 100.0 * e["tflops"] / PEAK_BF16_TFLOPS
-        else:
-            e["gbs"] = a["bytes"] / (a["total_ms"] * 1e-3) / 1e9
-            e["hbm_pct"] = 100.0 * e["gbs"] / PEAK_HBM_GBS
-        kern[name] = e
+    agg = kernel_breakdown(tower, plan, pixels, ws, out, stream, args.steps)
+    kern = kernel_table(agg, args.steps)
+    for name, e in kern.items():
         log(f"  {name:24s} {e['share_pct']:5.1f}%  avg {e['avg_us']:9.1f} us  " +
-            (f"{e['tflops']:7.1f} TFLOP/s ({e['mfma_pct']:.1f}% MFMA)" if a["mfma_bound"]
+            (f"{e['tflops']:7.1f} TFLOP/s ({e['mfma_pct']:.1f}% MFMA)" if "tflops" in e
              else f"{e['gbs']:7.1f} GB/s ({e['hbm_pct']:.1f}% HBM)"))
     dom = max(agg, key=lambda n: agg[n]["total_ms"])
-    da = agg[dom]
-    per_launch_ms = da["total_ms"] / da["launches"]
-    if da["mfma_bound"]:
-        achieved = da["flops"] / da["launches"] / (per_launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "kernel": dom,
-                "avg_launch_us": per_launch_ms * 1e3}
-    else:
-        achieved = da["bytes"] / da["launches"] / (per_launch_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom,
-                "avg_launch_us": per_launch_ms * 1e3}
+    roof = roofline_of(agg, dom)
     flops_step = sum(a["flops"] for a in agg.values()) / args.steps
     mfma_util = 100.0 * flops_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
 
@@ -408,9 +484,19 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("calibration copy: 3 x 512 MiB device-to-device")
+    if not args.no_configs:
+        del ws, gws
+        tower.close()
+        torch.cuda.empty_cache()
+        line["workloads"] = {}
+        for idx in (2, 4, 5):
+            line["workloads"][f"w{idx}"] = measure_workload(idx, args.steps, args.warmup, args.activations,
+                                                            stream)
+            torch.cuda.empty_cache()
     if not args.no_cpu:
         log("CPU oracle baseline ...")
-        line["cpu_baseline"] = cpu_baseline(wl)
+        items = None if args.cpu_items == "all" else [int(i) for i in args.cpu_items.split(",")]
+        line["cpu_baseline"] = cpu_baseline(wl, items)
         log(f"CPU oracle: {line['cpu_baseline']['value']:.1f} patches/s on {line['cpu_baseline']['cores']} threads")
     print(json.dumps(line), flush=True)
 

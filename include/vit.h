@@ -215,6 +215,22 @@ vit_status vit_plan_rows(const vit_plan* plan, int64_t* n_patches, int32_t* dst)
 vit_status vit_encode(const vit_ctx* ctx, const vit_plan* plan, const uint8_t* pixels_u8, void* ws,
                       size_t ws_bytes, float* out, void* stream);
 
+/* Size of the static device scratch that vit_encode_noalloc uses as its workspace. */
+#define VIT_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* vit_encode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same forward, same kernels, same
+ * arguments minus the workspace: the workspace is a static device array of
+ * VIT_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one per GPU, held until the process
+ * ends; the call allocates nothing.  Enough for a plan whose ws_bytes (vit_plan_sizes) fit:
+ * for a 1280-wide tower with a 5120-wide MLP, about 1600 patches (a 448 x 448 image needs
+ * 40 MiB).  Errors as vit_encode, plus VIT_E_WORKSPACE when the plan needs more than the
+ * scratch (nothing is enqueued) and VIT_E_STATE when the current device is not the one the
+ * weights were uploaded to.  Every call on a GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU race, so issue them on one stream or order them. */
+vit_status vit_encode_noalloc(const vit_ctx* ctx, const vit_plan* plan, const uint8_t* pixels_u8,
+                              float* out, void* stream);
+
 /* Same forward from uint8 flatten_patches instead of frames (the pages' own
  * tower input: vLLM PR #55370 report, implementation breakdown item 2 and
  * review highlights -- the tower receives integer pixels already cut into

@@ -69,6 +69,7 @@ _SIGS = {
     "vit_plan_rows": (ctypes.c_int32, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]),
     "vit_encode": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "vit_encode_patches_u8": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
+    "vit_encode_noalloc": (ctypes.c_int32, [_P, _P, _P, _P, _P]),
     "vit_graph_capture": (ctypes.c_int32, [_P, _P, _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
     "vit_graph_io": (ctypes.c_int32, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
     "vit_graph_launch": (ctypes.c_int32, [_P, _P]),
@@ -310,6 +311,11 @@ class VisionTower:
         _check(self.lib, self.lib.vit_encode(self.handle, plan.handle, _ptr(pixels), _ptr(ws),
                                              ws.numel() if ws is not None else 0, _ptr(out),
                                              _stream_handle(stream)))
+
+    def encode_noalloc(self, plan: Plan, pixels, out, stream=None):
+        """vit_encode with the library's static device scratch as the workspace (no allocation)."""
+        _check(self.lib, self.lib.vit_encode_noalloc(self.handle, plan.handle, _ptr(pixels), _ptr(out),
+                                                     _stream_handle(stream)))
 
     def encode_patches_u8(self, plan: Plan, patches, ws, out, stream=None):
         _check(self.lib, self.lib.vit_encode_patches_u8(self.handle, plan.handle, _ptr(patches), _ptr(ws),

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libvitmi.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "plan.cpp", "weights.cpp", "cache.cpp", "normpatch.hip", "norm.hip", "gemm.hip",
-           "attention.hip", "pixel_hash.hip", "resize.hip"]
+           "attention.hip", "pixel_hash.hip", "resize.hip", "noalloc.hip"]
 
 # packed fp32 VALU forms are disabled for every HIP translation unit (the host
 # pass warns that it does not know the feature; that is harmless)

@@ -368,8 +368,9 @@ def main():
                     help="skip the other workloads (448 px tower, 16-frame video, Qwen2.5-shaped batch)")
     ap.add_argument("--cpu-items", default="all",
                     help="items of the batch the CPU oracle runs on: 'all' or a comma list of indices")
-    ap.add_argument("--activations", default="bf16f8", choices=["bf16f8", "bf16x2"],
-                    help="form of the compensated GEMM activations (bf16 + e4m3 residual, or hi+lo bf16 pairs)")
+    ap.add_argument("--activations", default="f16", choices=["f16", "bf16f8", "bf16x2"],
+                    help="form of the GEMM / attention activations: float16 (default), or bf16 compensated "
+                         "by an e4m3 residual or by hi+lo bf16 pairs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the vision tower is not sharded "
@@ -440,11 +441,11 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": "patches/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f16" if args.activations == "f16" else "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "items": len(wl.items), "patches": wl.n_patches,
                    "layers": cfg.layers, "hidden": cfg.hidden, "heads": cfg.heads, "mlp": cfg.mlp_dim,
                    "out_dim": cfg.out_dim, "mode": "hipgraph", "parallelism": "single-gpu",
-                   "activations": args.activations},
+                   "weights": "bf16", "activations": args.activations},
         "mfma_util_pct": mfma_util,
         "algorithmic_tflop_per_step": flops_step / 1e12,
         "eager_ms_per_step": eager_ms,

@@ -74,6 +74,7 @@ typedef int32_t vit_status;
 #define VIT_ACT_BF16     0  /* GEMM activation operands rounded once to bfloat16 */
 #define VIT_ACT_BF16X2   1  /* norm, MLP and merger activations kept as hi+lo bfloat16 pairs */
 #define VIT_ACT_BF16F8   2  /* the same activations kept as bfloat16 + e4m3 residual */
+#define VIT_ACT_F16      3  /* every GEMM / attention activation in float16 (the default form) */
 
 #define VIT_MAX_FULL_LAYERS 64
 
@@ -107,7 +108,14 @@ typedef struct vit_config {
    * residual's product against an e4m3 copy of the weights (per-row power-of-two scales)
    * through the scaled fp8 MFMA, so the residual costs half the MFMA time of a second bf16
    * product and 1 instead of 2 bytes per element (its error, ~2^-12 of x, stays far below
-   * the bf16 rounding it compensates).  VIT_ACT_BF16 rounds every GEMM activation once. */
+   * the bf16 rounding it compensates).  VIT_ACT_BF16 rounds every GEMM activation once.
+   * VIT_ACT_F16 (recommended) stores every GEMM and attention activation -- norm outputs,
+   * q, k, v, the attention probabilities and output, MLP and merger activations -- in IEEE
+   * float16, rounded once (relative error 2^-12, the compensated forms' level, with no
+   * second product), and multiplies them on the float16 MFMA (the bf16 rate) against float16
+   * copies of the weights: each matrix's bf16 values times one power of two, exact for every
+   * weight above 2^-39 of the matrix's largest.  Only the patch embedding stays bf16 (its
+   * input, the normalised pixels, is bf16 by definition). */
   int32_t activation_precision;
 } vit_config;
 

@@ -24,7 +24,7 @@ VIT_OK, VIT_E_ARG, VIT_E_SHAPE, VIT_E_WEIGHTS, VIT_E_WORKSPACE, VIT_E_STATE, VIT
 VIT_MLP_GELU, VIT_MLP_SWIGLU = 0, 1
 VIT_NORM_LAYER, VIT_NORM_RMS = 0, 1
 VIT_F32, VIT_BF16 = 0, 1
-VIT_ACT_BF16, VIT_ACT_BF16X2, VIT_ACT_BF16F8 = 0, 1, 2
+VIT_ACT_BF16, VIT_ACT_BF16X2, VIT_ACT_BF16F8, VIT_ACT_F16 = 0, 1, 2, 3
 MAX_FULL_LAYERS = 64
 
 _STATUS_NAMES = {0: "VIT_OK", 1: "VIT_E_ARG", 2: "VIT_E_SHAPE", 3: "VIT_E_WEIGHTS",
@@ -124,15 +124,16 @@ def _check(lib, status: int):
         raise VitError(status, lib.vit_last_error().decode())
 
 
-def make_config(cfg, activation_precision: str = "bf16f8") -> vit_config:
+def make_config(cfg, activation_precision: str = "f16") -> vit_config:
     """vit_config from any object with the tower fields (e.g. workloads.TowerConfig).
 
-    activation_precision: "bf16f8" (the norm, MLP and merger GEMM inputs as bf16 plus
-    an e4m3 residual; the default), "bf16x2" (the same activations as hi+lo bf16
-    pairs) or "bf16" (rounded once)."""
+    activation_precision: "f16" (every GEMM and attention activation in float16 against
+    float16 weight copies; the default), "bf16f8" (the norm, attention-output, MLP and
+    merger GEMM inputs as bf16 plus an e4m3 residual), "bf16x2" (the same activations as
+    hi+lo bf16 pairs) or "bf16" (rounded once)."""
     c = vit_config()
     c.activation_precision = {"bf16": VIT_ACT_BF16, "bf16x2": VIT_ACT_BF16X2,
-                              "bf16f8": VIT_ACT_BF16F8}[activation_precision]
+                              "bf16f8": VIT_ACT_BF16F8, "f16": VIT_ACT_F16}[activation_precision]
     c.hidden, c.heads, c.layers, c.mlp_dim = cfg.hidden, cfg.heads, cfg.layers, cfg.mlp_dim
     c.mlp_kind = VIT_MLP_GELU if cfg.mlp_kind == "gelu" else VIT_MLP_SWIGLU
     c.norm_kind = VIT_NORM_LAYER if cfg.norm_kind == "layer" else VIT_NORM_RMS
@@ -281,7 +282,7 @@ class EmbeddingCache:
 class VisionTower:
     """Owns one vit_ctx: configuration, weights (host copies until finalize, then a device arena)."""
 
-    def __init__(self, cfg, lib: Optional[ctypes.CDLL] = None, activation_precision: str = "bf16f8"):
+    def __init__(self, cfg, lib: Optional[ctypes.CDLL] = None, activation_precision: str = "f16"):
         self.lib = lib or load_library()
         self.cfg = cfg
         self.activation_precision = activation_precision

@@ -99,7 +99,8 @@ vit_status check_common(const vit_ctx* ctx, const vit_plan* plan, const void* ws
   }
   if (plan->cfg.hidden != ctx->cfg.hidden || plan->cfg.layers != ctx->cfg.layers ||
       plan->cfg.window_px != ctx->cfg.window_px || plan->head_dim != ctx->head_dim ||
-      plan->split != ctx->split || plan->f8 != ctx->f8) {
+      plan->split != ctx->split || plan->f8 != ctx->f8 ||
+      plan->cfg.activation_precision != ctx->cfg.activation_precision) {
     set_error("plan was built for a different tower configuration");
     return VIT_E_ARG;
   }
@@ -168,6 +169,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   const int S = ctx->split;            // 2: activations stored as [hi | lo] rows
   const bool split = S == 2;
   const bool f8 = ctx->f8;             // activations stored as bf16 rows + e4m3 residuals
+  const bool f16 = ctx->f16;           // float16 activations against float16 weight copies
   const double Nd = (double)N, dd = (double)d;
   if (N == 0) return VIT_OK;
   if (prof) prof->st = st;
@@ -224,7 +226,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   for (int l = 0; l < c.layers; ++l) {
     const LayerW& L = W.layers[l];
     LAUNCH("rownorm", 0, norm_bytes, false,
-           launch_rownorm(c.norm_kind, R, N, d, L.n1g, L.n1b, c.norm_eps, H, split, 1, st, rows_dev, H8));
+           launch_rownorm(c.norm_kind, R, N, d, L.n1g, L.n1b, c.norm_eps, H, split, 1, st, rows_dev, H8, f16));
     if (stop.hit(l, 1)) return copy_act(H, H8, N, d, 1);
 
     GemmArgs q;
@@ -234,6 +236,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     q.row_pos = rowpos; q.cos_tab = cos_t; q.sin_tab = sin_t;
     q.nfreq = pl->nfreq; q.head_dim = hd; q.hidden = d;
     q.q_scale = (float)(1.4426950408889634 / std::sqrt((double)hd));   // log2(e) / sqrt(head_dim)
+    q.f16 = f16; q.acc_scale = L.qkv_sc;
     if (f8) {
       q.A8 = H8; q.lda8 = d; q.B8 = L.qkv_w8; q.ldb8 = d; q.b8_scale = L.qkv_s8;
     }
@@ -249,7 +252,8 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     const bool windowed = c.window_px > 0 && !ctx->is_full_layer(l);
     const AttnLists& lists = windowed ? pl->win : pl->full;
     AttnArgs at;
-    at.q = Q; at.k = K; at.vt = VT; at.o = O; at.o_split = split; at.o8 = O8; at.n_tok = N; at.vt_ld = pl->vt_ld;
+    at.q = Q; at.k = K; at.vt = VT; at.o = O; at.o_split = split; at.o8 = O8; at.f16 = f16;
+    at.n_tok = N; at.vt_ld = pl->vt_ld;
     at.heads = c.heads; at.head_dim = hd;
     at.work_long = reinterpret_cast<const AttnWork*>(ws + lists.off_long);
     at.work_short = reinterpret_cast<const AttnWork*>(ws + lists.off_short);
@@ -272,6 +276,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     GemmArgs pj;
     pj.A = O; pj.lda = S * d; pj.B = L.proj_w; pj.ldb = d; pj.a_group = split ? d : 0;
     pj.M = (int)N; pj.N = d; pj.K = d; pj.bias = L.proj_b; pj.out = R; pj.ldo = d; pj.m_dev = rows_dev;
+    pj.f16 = f16; pj.acc_scale = L.proj_sc;
     if (f8) {
       pj.A8 = O8; pj.lda8 = d; pj.B8 = L.proj_w8; pj.ldb8 = d; pj.b8_scale = L.proj_s8;
     }
@@ -279,13 +284,14 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     if (stop.hit(l, 6)) return copy_out(stop, R, (size_t)N * d * 4, st);
 
     LAUNCH("rownorm", 0, norm_bytes, false,
-           launch_rownorm(c.norm_kind, R, N, d, L.n2g, L.n2b, c.norm_eps, H, split, 1, st, rows_dev, H8));
+           launch_rownorm(c.norm_kind, R, N, d, L.n2g, L.n2b, c.norm_eps, H, split, 1, st, rows_dev, H8, f16));
     if (stop.hit(l, 7)) return copy_act(H, H8, N, d, 1);
 
     GemmArgs f1;
     f1.A = H; f1.lda = S * d; f1.B = L.fc1_w; f1.ldb = d; f1.a_group = split ? d : 0;
     f1.M = (int)N; f1.K = d; f1.bias = L.fc1_b; f1.out = F; f1.ldo = S * mp; f1.m_dev = rows_dev;
     f1.split_off = split ? mp : 0;
+    f1.f16 = f16; f1.acc_scale = L.fc1_sc;
     if (f8) {
       f1.A8 = H8; f1.lda8 = d; f1.B8 = L.fc1_w8; f1.ldb8 = d; f1.b8_scale = L.fc1_s8;
       f1.out8 = F8; f1.ldo8 = mp;
@@ -303,6 +309,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     GemmArgs f2;
     f2.A = F; f2.lda = S * mp; f2.B = L.fc2_w; f2.ldb = mp; f2.a_group = split ? mp : 0;
     f2.M = (int)N; f2.N = d; f2.K = mp; f2.bias = L.fc2_b; f2.out = R; f2.ldo = d; f2.m_dev = rows_dev;
+    f2.f16 = f16; f2.acc_scale = L.fc2_sc;
     if (f8) {
       f2.A8 = F8; f2.lda8 = mp; f2.B8 = L.fc2_w8; f2.ldb8 = mp; f2.b8_scale = L.fc2_s8;
     }
@@ -314,7 +321,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   // side by side as one row of 4 * S * d columns), then the MLP
   const int L = c.layers;
   LAUNCH("rownorm", 0, norm_bytes, false,
-         launch_rownorm(c.norm_kind, R, N, d, W.mq_g, W.mq_b, c.norm_eps, H, split, 4, st, rows_dev, H8));
+         launch_rownorm(c.norm_kind, R, N, d, W.mq_g, W.mq_b, c.norm_eps, H, split, 4, st, rows_dev, H8, f16));
   if (stop.hit(L, 1)) return copy_act(H, H8, N, d, 4);
   const int64_t U = pl->n_units;
   const double Ud = (double)U;
@@ -323,6 +330,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   m1.M = (int)U; m1.N = 4 * d; m1.K = 4 * d; m1.bias = W.m1_b; m1.out = F; m1.ldo = S * 4 * d;
   m1.m_dev = units_dev;
   m1.split_off = split ? 4 * d : 0;
+  m1.f16 = f16; m1.acc_scale = W.m1_sc;
   if (f8) {
     m1.A8 = H8; m1.lda8 = 4 * d; m1.B8 = W.m1_w8; m1.ldb8 = 4 * d; m1.b8_scale = W.m1_s8;
     m1.out8 = F8; m1.ldo8 = 4 * d;
@@ -334,6 +342,7 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
   m2.M = (int)U; m2.N = c.out_dim; m2.K = 4 * d; m2.bias = W.m2_b; m2.out = out; m2.ldo = c.out_dim;
   m2.m_dev = units_dev;
   m2.row_map = unitdst;
+  m2.f16 = f16; m2.acc_scale = W.m2_sc;
   if (f8) {
     m2.A8 = F8; m2.lda8 = 4 * d; m2.B8 = W.m2_w8; m2.ldb8 = 4 * d; m2.b8_scale = W.m2_s8;
   }
@@ -388,8 +397,8 @@ vit_status validate_config(const vit_config* c, int* head_dim) {
     return VIT_E_ARG;
   }
   if (c->activation_precision != VIT_ACT_BF16 && c->activation_precision != VIT_ACT_BF16X2 &&
-      c->activation_precision != VIT_ACT_BF16F8) {
-    set_error("activation_precision must be VIT_ACT_BF16, VIT_ACT_BF16X2 or VIT_ACT_BF16F8");
+      c->activation_precision != VIT_ACT_BF16F8 && c->activation_precision != VIT_ACT_F16) {
+    set_error("activation_precision must be VIT_ACT_F16, VIT_ACT_BF16, VIT_ACT_BF16X2 or VIT_ACT_BF16F8");
     return VIT_E_ARG;
   }
   if (c->n_full_attn_layers < 0 || c->n_full_attn_layers > VIT_MAX_FULL_LAYERS) {
@@ -481,6 +490,7 @@ vit_status vit_create(const vit_config* cfg, vit_ctx** out) {
   ctx->mlp_pad = (int)round_up(cfg->mlp_dim, 64);
   ctx->split = cfg->activation_precision == VIT_ACT_BF16X2 ? 2 : 1;
   ctx->f8 = cfg->activation_precision == VIT_ACT_BF16F8;
+  ctx->f16 = cfg->activation_precision == VIT_ACT_F16;
   build_lut(*cfg, ctx->lut);
   ctx->norm_affine = verify_affine(*cfg, ctx->lut, &ctx->affine);
   *out = ctx;

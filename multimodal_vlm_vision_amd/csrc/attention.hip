@@ -7,8 +7,9 @@
 // by the planner (section 3.3).  A tile never spans two segments: every work
 // unit names its segment and the kernel only reads that segment's keys.
 //
-// Formulation (v_mfma_f32_32x32x16_bf16 throughout): a wave owns 64 queries as
-// two 32-query tiles and walks the segment's keys 32 at a time.
+// Formulation (v_mfma_f32_32x32x16_f16 throughout with float16 operands, the
+// default; _bf16 with bfloat16 ones): a wave owns 64 queries as two 32-query
+// tiles and walks the segment's keys 32 at a time.
 //  * S^T = K Q^T: keys are MFMA rows, queries columns, head_dim the reduction
 //    (80 = 5 x 16, no padded chunk).  Each lane ends up with 16 keys
 //    (rows 8g + 4h + e, h = lane / 32) of one query (lane % 32), so the row
@@ -26,7 +27,7 @@
 // qkv epilogue applies it before q is rounded to bf16), and every score MFMA
 // chain starts from an accumulator tile holding -m (the query's running
 // offset), so the MFMAs return the exp2 argument s - m itself and the common
-// path spends no VALU op on it; P is rounded to bf16 for the MFMA.  The offset
+// path spends no VALU op on it; P is rounded to the operand type for the MFMA.  The offset
 // is only raised (and O rescaled) when a block's max exceeds it by more than
 // 2^8, which keeps the rescale off the common path without changing the math.
 // The two MFMA groups of a block run at raised wave priority (s_setprio): a
@@ -84,10 +85,33 @@ __device__ __forceinline__ float from_upper_half(float x) {
 
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 // two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// two floats -> packed float16 pair, round to nearest even (one v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
+// F16: q, k, V^T, P and the output are float16 (the default activation form); otherwise bfloat16.
+// Operand fragments travel as 16-byte vectors of either type (same bits, same layout).
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  if constexpr (F16) return pack_f16(a, b);
+  else return pack_bf16(a, b);
+}
+template <bool F16>
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // x - bf16(x): what the bf16 rounding of x leaves out
@@ -104,7 +128,7 @@ __device__ __forceinline__ uint32_t rest_e4m3x4(float a, float b, float c, float
 
 // DYN: the work-list length comes from device memory at run time (bucketed graphs); a separate
 // instantiation, so the plain path keeps it a launch constant.
-template <int HD, int NW, bool DYN>
+template <int HD, int NW, bool DYN, bool F16>
 __global__ void __launch_bounds__(NW * 64, 2)
 attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int32_t* __restrict__ n_work_dev) {
   constexpr int NCH = HD / 16;               // 16-wide reduction chunks of S^T = K Q^T
@@ -152,7 +176,8 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
 
   // constant V^T rows: HD = ones (softmax denominator), the rest zeros; never overwritten
   for (int i = tid; i < (VROWS - HD) * VDW; i += NW * 64) {
-    const uint32_t v = i < VDW ? 0x3f803f80u : 0u;   // bf16 1.0 pairs
+    const uint32_t one2 = F16 ? 0x3c003c00u : 0x3f803f80u;   // pairs of 1.0 (float16 or bfloat16)
+    const uint32_t v = i < VDW ? one2 : 0u;
     sV0[HD * VDW + i] = v;
     sV1[HD * VDW + i] = v;
   }
@@ -247,7 +272,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * c);
 #pragma unroll
         for (int t = 0; t < QT; ++t)
-          S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][c], c == 0 ? nm[t] : S[t], 0, 0, 0);
+          S[t] = mma<F16>(kf, qf[t][c], c == 0 ? nm[t] : S[t]);
       }
       __builtin_amdgcn_s_setprio(0);
       // ---- mask keys past the segment end (last step only); lane's keys are 8g + 4h + e
@@ -288,7 +313,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
         uint32_t pw[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          pw[i] = pack_bf16(__builtin_amdgcn_exp2f(S[t][2 * i]), __builtin_amdgcn_exp2f(S[t][2 * i + 1]));
+          pw[i] = pack16<F16>(__builtin_amdgcn_exp2f(S[t][2 * i]), __builtin_amdgcn_exp2f(S[t][2 * i + 1]));
         pb[t][0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
         pb[t][1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
       }
@@ -304,7 +329,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
           const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16 * c + 8);
           const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-          for (int t = 0; t < QT; ++t) O[t][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][c], O[t][dt], 0, 0, 0);
+          for (int t = 0; t < QT; ++t) O[t][dt] = mma<F16>(vf, pb[t][c], O[t][dt]);
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -344,7 +369,8 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
           const float y0 = o[4 * g] * inv, y1 = o[4 * g + 1] * inv, y2 = o[4 * g + 2] * inv,
                       y3 = o[4 * g + 3] * inv;
           *reinterpret_cast<uint2*>(a.o + kt_index(orow, ocol + d, ld)) =
-              make_uint2(pack_bf16(y0, y1), pack_bf16(y2, y3));
+              make_uint2(pack16<F16>(y0, y1), pack16<F16>(y2, y3));
+          if (F16) continue;   // float16 output needs no compensation
           if (a.o_split)
             *reinterpret_cast<uint2*>(a.o + kt_index(orow, hid + ocol + d, ld)) =
                 make_uint2(pack_bf16(bf16_rest(y0), bf16_rest(y1)), pack_bf16(bf16_rest(y2), bf16_rest(y3)));
@@ -355,20 +381,20 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
   }
 }
 
-template <int HD>
+template <int HD, bool F16>
 hipError_t run_hd(const AttnArgs& a, hipStream_t st) {
   if (a.n_long > 0 && a.n_long_dev)
-    hipLaunchKernelGGL((attn_kernel<HD, 4, true>), dim3(a.n_long * a.heads), dim3(256), 0, st, a, a.work_long,
-                       a.n_long, a.n_long_dev);
+    hipLaunchKernelGGL((attn_kernel<HD, 4, true, F16>), dim3(a.n_long * a.heads), dim3(256), 0, st, a,
+                       a.work_long, a.n_long, a.n_long_dev);
   else if (a.n_long > 0)
-    hipLaunchKernelGGL((attn_kernel<HD, 4, false>), dim3(a.n_long * a.heads), dim3(256), 0, st, a, a.work_long,
-                       a.n_long, nullptr);
+    hipLaunchKernelGGL((attn_kernel<HD, 4, false, F16>), dim3(a.n_long * a.heads), dim3(256), 0, st, a,
+                       a.work_long, a.n_long, nullptr);
   if (a.n_short > 0 && a.n_short_dev)
-    hipLaunchKernelGGL((attn_kernel<HD, 1, true>), dim3(a.n_short * a.heads), dim3(64), 0, st, a, a.work_short,
-                       a.n_short, a.n_short_dev);
+    hipLaunchKernelGGL((attn_kernel<HD, 1, true, F16>), dim3(a.n_short * a.heads), dim3(64), 0, st, a,
+                       a.work_short, a.n_short, a.n_short_dev);
   else if (a.n_short > 0)
-    hipLaunchKernelGGL((attn_kernel<HD, 1, false>), dim3(a.n_short * a.heads), dim3(64), 0, st, a, a.work_short,
-                       a.n_short, nullptr);
+    hipLaunchKernelGGL((attn_kernel<HD, 1, false, F16>), dim3(a.n_short * a.heads), dim3(64), 0, st, a,
+                       a.work_short, a.n_short, nullptr);
   return hipGetLastError();
 }
 
@@ -411,10 +437,14 @@ vit_status launch_attention(const AttnArgs& a, void* stream) {
     return VIT_E_ARG;
   }
   hipError_t e;
+  if (a.f16 && (a.o_split || a.o8)) {
+    set_error("attention: float16 output takes no compensation");
+    return VIT_E_ARG;
+  }
   switch (a.head_dim) {
-    case 32: e = run_hd<32>(a, st); break;
-    case 64: e = run_hd<64>(a, st); break;
-    case 80: e = run_hd<80>(a, st); break;
+    case 32: e = a.f16 ? run_hd<32, true>(a, st) : run_hd<32, false>(a, st); break;
+    case 64: e = a.f16 ? run_hd<64, true>(a, st) : run_hd<64, false>(a, st); break;
+    case 80: e = a.f16 ? run_hd<80, true>(a, st) : run_hd<80, false>(a, st); break;
     default:
       set_error("attention: head_dim %d not supported (32, 64, 80)", a.head_dim);
       return VIT_E_ARG;

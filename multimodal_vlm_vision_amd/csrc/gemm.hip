@@ -97,6 +97,21 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 __device__ __forceinline__ uint2 pack4(float4 v) { return make_uint2(pack2(v.x, v.y), pack2(v.z, v.w)); }
 
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
+// activation pairs in the operand type of activation mode AM: float16 for AM 3 (one
+// v_cvt_pk_f16_f32, round to nearest even), bfloat16 otherwise
+template <int AM>
+__device__ __forceinline__ uint32_t pack2a(float a, float b) {
+  if constexpr (AM == 3) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+  else return pack2(a, b);
+}
+template <int AM>
+__device__ __forceinline__ uint2 pack4a(float4 v) {
+  return make_uint2(pack2a<AM>(v.x, v.y), pack2a<AM>(v.z, v.w));
+}
+
 // erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26
 // (|error| <= 1.5e-7, far below the bf16 rounding of the GELU output).
 __device__ __forceinline__ float erf_as(float x) {
@@ -138,9 +153,11 @@ __device__ __forceinline__ void store_act8(const GemmArgs& p, int m, int n, cons
   uint16_t* o = static_cast<uint16_t*>(p.out);
   uint32_t hi[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hi[i] = pack2(y[2 * i], y[2 * i + 1]);
+  for (int i = 0; i < 4; ++i) hi[i] = pack2a<AM>(y[2 * i], y[2 * i + 1]);
   *reinterpret_cast<uint4*>(o + kt_index(m, n, p.ldo)) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  if constexpr (AM == 2) {
+  if constexpr (AM == 3) {
+    return;   // float16 activations carry no second part
+  } else if constexpr (AM == 2) {
     uint32_t l8[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -159,7 +176,8 @@ __device__ __forceinline__ void store_act8(const GemmArgs& p, int m, int n, cons
   }
 }
 
-// AM (activation mode): 0 single bf16, 1 hi+lo bf16 pairs, 2 bf16 + e4m3 residual
+// AM (activation mode): 0 single bf16, 1 hi+lo bf16 pairs, 2 bf16 + e4m3 residual, 3 float16
+// activations against float16 weights (loaded exactly like mode 0, multiplied on the f16 MFMA)
 template <int BM, int BN, int WM, int WN, int AM, int OCC = 1>
 struct Geo {
   static constexpr bool SPLIT = AM == 1, F8 = AM == 2;
@@ -339,10 +357,10 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const f
         const float4 a = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 4 * hf), ba[hf]);
         const float4 b = f4add(*reinterpret_cast<const float4*>(sc + r * SST + cl + 32 + 4 * hf), bb[hf]);
         const float4 c = cs[q][hf], s = sn[q][hf];
-        const uint2 u1 = pack4(make_float4((a.x * c.x - b.x * s.x) * qs, (a.y * c.y - b.y * s.y) * qs,
-                                           (a.z * c.z - b.z * s.z) * qs, (a.w * c.w - b.w * s.w) * qs));
-        const uint2 u2 = pack4(make_float4((b.x * c.x + a.x * s.x) * qs, (b.y * c.y + a.y * s.y) * qs,
-                                           (b.z * c.z + a.z * s.z) * qs, (b.w * c.w + a.w * s.w) * qs));
+        const uint2 u1 = pack4a<AM>(make_float4((a.x * c.x - b.x * s.x) * qs, (a.y * c.y - b.y * s.y) * qs,
+                                                (a.z * c.z - b.z * s.z) * qs, (a.w * c.w - b.w * s.w) * qs));
+        const uint2 u2 = pack4a<AM>(make_float4((b.x * c.x + a.x * s.x) * qs, (b.y * c.y + a.y * s.y) * qs,
+                                                (b.z * c.z + a.z * s.z) * qs, (b.w * c.w + a.w * s.w) * qs));
         w1[2 * hf] = u1.x; w1[2 * hf + 1] = u1.y;
         w2[2 * hf] = u2.x; w2[2 * hf + 1] = u2.y;
       }
@@ -371,9 +389,9 @@ __device__ __forceinline__ void epilogue_slice(const GemmArgs& p, int M, const f
                                     sc[(8 * rg + 6) * SST + c] + b, sc[(8 * rg + 7) * SST + c] + b);
       const int nn = n - 2 * d, head = nn / hd, dd = nn % hd;
       uint16_t* o = p.vt + ((int64_t)head * hd + dd) * p.vt_ld + m;
-      const uint2 u0 = pack4(v0);
+      const uint2 u0 = pack4a<AM>(v0);
       if (m + 8 <= M) {
-        const uint2 u1 = pack4(v1);
+        const uint2 u1 = pack4a<AM>(v1);
         *reinterpret_cast<uint4*>(o) = make_uint4(u0.x, u0.y, u1.x, u1.y);
       } else {
         *reinterpret_cast<uint2*>(o) = u0;
@@ -524,8 +542,13 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (AM == 3)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, xa[i]),
+                                                             __builtin_bit_cast(f16x8, xb[j]), acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+      }
     if constexpr (SPLIT) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -665,12 +688,15 @@ gemm_kernel(GemmArgs p) {
   // 8g + 4*(lane >> 5) + e of each 32x32 tile.
   float* sc = reinterpret_cast<float*>(smem) + wv * 32 * G::SST;
   const int lc = lane & 31, lr = (lane >> 5) * 4;
+  // AM 3: the float16 weights carry a power-of-two scale; undoing it is exact
+  const float osc = AM == 3 ? p.acc_scale : 1.0f;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc[(8 * (e / 4) + lr + (e % 4)) * G::SST + j * 32 + lc] = acc[i][j][e];
+      for (int e = 0; e < 16; ++e)
+        sc[(8 * (e / 4) + lr + (e % 4)) * G::SST + j * 32 + lc] = AM == 3 ? acc[i][j][e] * osc : acc[i][j][e];
     epilogue_slice<EPI, TN * 32, AM>(p, M, sc, m0 + wm * TM * 32 + i * 32, n0 + wn * TN * 32, lane);
   }
 }
@@ -776,8 +802,8 @@ int pick_cfg(int epi, const GemmArgs& a) {
 template <int AM>
 hipError_t dispatch(int epi, int cfg, const GemmArgs& a, hipStream_t st, bool* bad_epi) {
   switch (epi) {
-    case EPI_F32:   // (not built for compensated activations: no product of the tower has it)
-      if constexpr (AM == 2) break;
+    case EPI_F32:   // (patch embedding only, always bf16: not built for the other modes)
+      if constexpr (AM == 2 || AM == 3) break;
       else return run_cfg<AM, EPI_F32>(cfg, a, st);
     case EPI_RES: return run_cfg<AM, EPI_RES>(cfg, a, st);
     case EPI_GELU: return run_cfg<AM, EPI_GELU>(cfg, a, st);
@@ -793,7 +819,7 @@ hipError_t dispatch(int epi, int cfg, const GemmArgs& a, hipStream_t st, bool* b
 template <int AM>
 hipError_t allow_all() {
   hipError_t e = hipSuccess;
-  if constexpr (AM != 2) e = allow_smem_all<AM, EPI_F32>();
+  if constexpr (AM != 2 && AM != 3) e = allow_smem_all<AM, EPI_F32>();
   if (e == hipSuccess) e = allow_smem_all<AM, EPI_RES>();
   if (e == hipSuccess) e = allow_smem_all<AM, EPI_GELU>();
   if (e == hipSuccess) e = allow_smem_all<AM, EPI_SWIGLU>();
@@ -808,6 +834,7 @@ vit_status prepare_gemm_kernels() {
   hipError_t e = allow_all<0>();
   if (e == hipSuccess) e = allow_all<1>();
   if (e == hipSuccess) e = allow_all<2>();
+  if (e == hipSuccess) e = allow_all<3>();
   if (e != hipSuccess) {
     set_error("gemm LDS attribute: %s", hipGetErrorString(e));
     return VIT_E_HIP;
@@ -838,6 +865,10 @@ vit_status launch_gemm(int epi, const GemmArgs& in, void* stream) {
   }
   if (!f8 && a.out8) {
     set_error("gemm: an e4m3 residual output needs e4m3 residual inputs");
+    return VIT_E_ARG;
+  }
+  if (a.f16 && (f8 || split || a.split_off)) {
+    set_error("gemm: float16 operands take no compensation");
     return VIT_E_ARG;
   }
   // byte extents of the blocked operands (rows padded to 16), addressed with 32-bit buffer offsets
@@ -874,9 +905,10 @@ vit_status launch_gemm(int epi, const GemmArgs& in, void* stream) {
   a.group_m = (ci->occ == 1 && gn <= 8) ? std::max(1, 32 / gn) : 8;
   hipStream_t st = static_cast<hipStream_t>(stream);
   bool bad_epi = false;
-  const hipError_t e = f8      ? dispatch<2>(epi, cfg, a, st, &bad_epi)
-                      : split ? dispatch<1>(epi, cfg, a, st, &bad_epi)
-                              : dispatch<0>(epi, cfg, a, st, &bad_epi);
+  const hipError_t e = f8       ? dispatch<2>(epi, cfg, a, st, &bad_epi)
+                      : split  ? dispatch<1>(epi, cfg, a, st, &bad_epi)
+                      : a.f16  ? dispatch<3>(epi, cfg, a, st, &bad_epi)
+                               : dispatch<0>(epi, cfg, a, st, &bad_epi);
   if (bad_epi) {
     set_error("gemm: bad epilogue %d", epi);
     return VIT_E_ARG;

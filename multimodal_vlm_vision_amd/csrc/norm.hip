@@ -1,4 +1,4 @@
-// Row normalisation of the float32 residual stream into bfloat16 GEMM inputs.
+// Row normalisation of the float32 residual stream into 16-bit GEMM inputs.
 //
 // LayerNorm (Qwen2-VL tower) or RMSNorm (Qwen2.5-VL tower) over the hidden
 // width with eps 1e-6 (vLLM PR #55370 report, key code: the towers take a
@@ -6,9 +6,10 @@
 // performance optimisation", section 3.5 names RMSNorm among the fused ops).
 // One wave per row (two rows per wave at the tower's width 1280, so every store
 // writes whole lines); the row stays in registers, so the statistics are exact
-// two-pass sums in float32; output is rounded to nearest-even bfloat16 and
-// stored in the blocked layout the GEMMs load (kt_index), with the compensated
-// forms' second part (a bfloat16 lo half, or an e4m3 residual in kt8_index).
+// two-pass sums in float32; output is rounded to nearest-even float16 (the default
+// activation form) or bfloat16 and stored in the blocked layout the GEMMs load
+// (kt_index), with the compensated bf16 forms' second part (a bfloat16 lo half,
+// or an e4m3 residual in kt8_index).
 #include <hip/hip_runtime.h>
 
 #include "vit_internal.h"
@@ -34,6 +35,20 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+// two floats -> packed float16 pair, round to nearest even (one v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
+// AM 3 (float16 activations): float16 pairs; otherwise bfloat16 pairs
+template <int AM>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  if constexpr (AM == 3) return pack_f16(a, b);
+  else return pack_bf16(a, b);
+}
+
 __device__ __forceinline__ float bf16_lo(float x) {
   return x - (float)(__bf16)x;
 }
@@ -47,9 +62,9 @@ __device__ __forceinline__ uint32_t lo_e4m3x4(float4 y) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f(y.z), f(y.w), lo, true);
 }
 
-// VPL = float4 chunks per lane (d <= 256 * VPL).  AM 1: each output row is [hi | lo] with
-// hi = bf16(y) and lo = bf16(y - hi); AM 2: hi rows, and the e4m3 residuals (times
-// 2^kLoShift) at the same place of out8 (kt8_index).  Input row `row` lands in blocked row
+// VPL = float4 chunks per lane (d <= 256 * VPL).  AM 0: bf16 rows; AM 1: each output row is
+// [hi | lo] with hi = bf16(y) and lo = bf16(y - hi); AM 2: hi rows, and the e4m3 residuals
+// (times 2^kLoShift) at the same place of out8 (kt8_index); AM 3: float16 rows.  Input row `row` lands in blocked row
 // row / group at column offset (row % group) * S * d of a group * S * d wide matrix.
 template <int KIND, int VPL, int AM, bool DYN>
 __global__ void __launch_bounds__(kThreads)
@@ -105,7 +120,7 @@ rownorm_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __restr
         y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
       }
       *reinterpret_cast<uint2*>(out + kt_index(orow, ocol + 4 * c, ocols)) =
-          make_uint2(pack_bf16(y.x, y.y), pack_bf16(y.z, y.w));
+          make_uint2(pack16<AM>(y.x, y.y), pack16<AM>(y.z, y.w));
       if (SPLIT)
         *reinterpret_cast<uint2*>(out + kt_index(orow, ocol + d + 4 * c, ocols)) =
             make_uint2(pack_bf16(bf16_lo(y.x), bf16_lo(y.y)), pack_bf16(bf16_lo(y.z), bf16_lo(y.w)));
@@ -177,7 +192,7 @@ rownorm2_kernel(const float* __restrict__ r, int64_t rows, const int32_t* __rest
         y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
       }
       *reinterpret_cast<uint2*>(out + kt_index(row, 4 * c, w)) =
-          make_uint2(pack_bf16(y.x, y.y), pack_bf16(y.z, y.w));
+          make_uint2(pack16<AM>(y.x, y.y), pack16<AM>(y.z, y.w));
       if (SPLIT)
         *reinterpret_cast<uint2*>(out + kt_index(row, d + 4 * c, w)) =
             make_uint2(pack_bf16(bf16_lo(y.x), bf16_lo(y.y)), pack_bf16(bf16_lo(y.z), bf16_lo(y.w)));
@@ -297,18 +312,19 @@ vit_status launch_unblock(const uint16_t* src, int64_t rows, int cols, int group
 
 vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
                           const float* b, float eps, uint16_t* out, bool split, int group,
-                          void* stream, const int32_t* rows_dev, uint8_t* out8) {
+                          void* stream, const int32_t* rows_dev, uint8_t* out8, bool f16) {
   if (rows <= 0) return VIT_OK;
-  if (d % 32 || group < 1 || rows % group || (split && out8)) {
+  if (d % 32 || group < 1 || rows % group || ((int)split + (out8 != nullptr) + (int)f16 > 1)) {
     set_error("rownorm: hidden %d must be a multiple of 32 and rows %lld a multiple of the group %d "
-              "(and at most one of split / out8)", d, (long long)rows, group);
+              "(and at most one of split / out8 / f16)", d, (long long)rows, group);
     return VIT_E_ARG;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int am = out8 ? 2 : split ? 1 : 0;
+  const int am = f16 ? 3 : out8 ? 2 : split ? 1 : 0;
   vit_status s;
 #define VIT_NORM_AM(K)                                                                   \
-  (am == 2   ? launch_kind<K, 2>(r, rows, rows_dev, d, g, b, eps, group, out, out8, st) \
+  (am == 3   ? launch_kind<K, 3>(r, rows, rows_dev, d, g, b, eps, group, out, out8, st) \
+   : am == 2 ? launch_kind<K, 2>(r, rows, rows_dev, d, g, b, eps, group, out, out8, st) \
    : am == 1 ? launch_kind<K, 1>(r, rows, rows_dev, d, g, b, eps, group, out, out8, st) \
              : launch_kind<K, 0>(r, rows, rows_dev, d, g, b, eps, group, out, out8, st))
   s = kind == VIT_NORM_LAYER ? VIT_NORM_AM(VIT_NORM_LAYER) : VIT_NORM_AM(VIT_NORM_RMS);

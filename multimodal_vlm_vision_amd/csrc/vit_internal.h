@@ -64,6 +64,8 @@ constexpr int kLoShift = 9;
 uint16_t f32_to_bf16_bits(float f);
 // OCP E4M3 round-to-nearest-even of a float, saturating at +-448, as raw bits (host side).
 uint8_t f32_to_e4m3_bits(float f);
+// IEEE binary16 round-to-nearest-even of a float, as raw bits (host side).
+uint16_t f32_to_f16_bits(float f);
 
 // ---------------------------------------------------------------- device-side records
 
@@ -133,6 +135,9 @@ struct LayerW {
   const uint8_t* proj_w8 = nullptr; const uint8_t* proj_s8 = nullptr;
   const uint8_t* fc1_w8 = nullptr;  const uint8_t* fc1_s8 = nullptr;
   const uint8_t* fc2_w8 = nullptr;  const uint8_t* fc2_s8 = nullptr;
+  // VIT_ACT_F16: the matrices above are float16 copies times 2^e (one e per matrix); the GEMM
+  // multiplies its accumulators by these 2^-e
+  float qkv_sc = 1.0f, proj_sc = 1.0f, fc1_sc = 1.0f, fc2_sc = 1.0f;
 };
 
 struct DeviceWeights {
@@ -146,6 +151,7 @@ struct DeviceWeights {
   const uint16_t* m2_w = nullptr; const float* m2_b = nullptr;   // [out][4d]
   const uint8_t* m1_w8 = nullptr; const uint8_t* m1_s8 = nullptr;   // VIT_ACT_BF16F8 copies
   const uint8_t* m2_w8 = nullptr; const uint8_t* m2_s8 = nullptr;
+  float m1_sc = 1.0f, m2_sc = 1.0f;   // VIT_ACT_F16 weight scales (as in LayerW)
 };
 
 }  // namespace vitmi
@@ -156,6 +162,7 @@ struct vit_ctx {
   int mlp_pad = 0;       // mlp_dim rounded up to 64
   int split = 1;         // 2 with hi+lo activation pairs, else 1
   bool f8 = false;       // compensated activations as bf16 + e4m3 residual (VIT_ACT_BF16F8)
+  bool f16 = false;      // float16 activations and weight copies (VIT_ACT_F16)
   uint16_t lut[3][256];  // bf16 bits of ((x/255) - mean_c) / std_c, exactly rounded
   bool norm_affine = false;     // fma(x, a_c, b_c) verified equal to lut for every byte
   vitmi::NormAffine affine{};
@@ -263,6 +270,10 @@ struct GemmArgs {
   // GELU / SwiGLU with A8 mode outputs: the e4m3 residual of each stored activation, times
   // 2^kLoShift, into a kt8_index matrix of ldo8 columns
   uint8_t* out8 = nullptr; int64_t ldo8 = 0;
+  // float16 operands (A and B), the f16 MFMA, and float16 activations / q / k / V^T out; the
+  // weights carry a power-of-two scale that the accumulators are multiplied by (acc_scale)
+  bool f16 = false;
+  float acc_scale = 1.0f;
 };
 
 vit_status launch_gemm(int epi, const GemmArgs& a, void* stream);
@@ -281,10 +292,11 @@ vit_status launch_normrows_u8(const uint8_t* patches, int64_t n_rows, const uint
 // columns (the merger's view of 2x2 patch blocks).
 // rows_dev (optional): row count read at run time; rows is then the capacity.
 // out8 (instead of split): bf16 rows plus their e4m3 residuals (times 2^kLoShift) in a
-// kt8_index matrix of the same view.
+// kt8_index matrix of the same view.  f16 (instead of both): float16 rows.
 vit_status launch_rownorm(int kind, const float* r, int64_t rows, int d, const float* g,
                           const float* b, float eps, uint16_t* out, bool split, int group,
-                          void* stream, const int32_t* rows_dev = nullptr, uint8_t* out8 = nullptr);
+                          void* stream, const int32_t* rows_dev = nullptr, uint8_t* out8 = nullptr,
+                          bool f16 = false);
 // Blocked bf16 matrix -> row-major [rows][out_cols] (debug copies): row m of the result is
 // row m / group, columns (m % group) * cols + [0, out_cols) of a blocked matrix with
 // group * cols columns.
@@ -303,6 +315,7 @@ struct AttnArgs {
   uint16_t* o = nullptr;
   bool o_split = false;
   uint8_t* o8 = nullptr;
+  bool f16 = false;   // q, k, V^T and the output are float16 (else bfloat16)
   int64_t n_tok = 0;
   int64_t vt_ld = 0;   // V^T row pitch in tokens: a multiple of 8, pad columns finite (zero)
   int heads = 0, head_dim = 0;

@@ -49,6 +49,30 @@ uint8_t f32_to_e4m3_bits(float f) {
   return sign | (uint8_t)((Er + 7) << 3) | (uint8_t)mant;
 }
 
+// IEEE 754 binary16: sign, 5 exponent bits with bias 15, 10 fraction bits; subnormals on a
+// 2^-24 grid below 2^-14; largest finite value 65504.  Round to nearest even; magnitudes that
+// round past 65504 become infinity.
+uint16_t f32_to_f16_bits(float f) {
+  const uint16_t sign = std::signbit(f) ? 0x8000 : 0;
+  if (std::isnan(f)) return 0x7e00;
+  const double a = std::fabs((double)f);
+  if (std::isinf(f)) return sign | 0x7c00;
+  if (a < std::ldexp(1.0, -14)) {                           // subnormal range (or 0)
+    const double k = std::nearbyint(a / std::ldexp(1.0, -24));   // default mode: to nearest even
+    return sign | (uint16_t)k;   // k == 1024 encodes the smallest normal number, 2^-14
+  }
+  int e2;
+  (void)std::frexp(a, &e2);      // a in [2^(e2-1), 2^e2)
+  int E = e2 - 1;
+  double k = std::nearbyint((a / std::ldexp(1.0, E) - 1.0) * 1024.0);
+  if (k == 1024.0) {             // rounded up into the next binade
+    k = 0.0;
+    E += 1;
+  }
+  if (E > 15) return sign | 0x7c00;
+  return sign | (uint16_t)((E + 15) << 10) | (uint16_t)k;
+}
+
 static float bf16_bits_to_f32(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
   float f;
@@ -165,6 +189,33 @@ struct Packer {
     std::memcpy(blob.data() + scale_off, sc.data(), rows);
     return off;
   }
+  // float16 copy for the float16 activation form: the bf16-rounded value of (r, c) times 2^e,
+  // one e for the whole matrix, the largest power that keeps its largest magnitude below 2^15.
+  // The conversion is exact for every value above 2^-39 of that magnitude (smaller ones land
+  // on float16's subnormal grid, an error below 2^-40 of the largest weight).  acc_scale
+  // receives 2^-e, which the GEMM epilogue multiplies the accumulators by (exact).
+  template <class F>
+  size_t mat16(int64_t rows, int64_t cols, F src, float& acc_scale) {
+    double mx = 0;
+    for (int64_t r = 0; r < rows; ++r)
+      for (int64_t c = 0; c < cols; ++c)
+        mx = std::max(mx, (double)std::fabs(bf16_bits_to_f32(f32_to_bf16_bits(src(r, c)))));
+    int e = 0;
+    if (mx > 0) {
+      int e2;
+      (void)std::frexp(mx, &e2);   // mx < 2^e2
+      e = std::min(std::max(15 - e2, -100), 100);
+    }
+    acc_scale = (float)std::ldexp(1.0, -e);
+    size_t off = reserve((size_t)rows * cols * 2);
+    uint16_t* d = reinterpret_cast<uint16_t*>(blob.data() + off);
+    for (int64_t r = 0; r < rows; ++r)
+      for (int64_t c = 0; c < cols; ++c) {
+        const float w = bf16_bits_to_f32(f32_to_bf16_bits(src(r, c)));
+        d[kt_index(r, c, cols)] = f32_to_f16_bits((float)std::ldexp((double)w, e));
+      }
+    return off;
+  }
   template <class F>
   size_t vec(int64_t n, F src) {
     size_t off = reserve((size_t)n * 4);
@@ -190,8 +241,11 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
   struct LayerOff {
     size_t n1g, n1b, n2g, n2b, qkv_w, qkv_b, proj_w, proj_b, fc1_w, fc1_b, fc2_w, fc2_b;
     size_t qkv_w8 = 0, qkv_s8 = 0, proj_w8 = 0, proj_s8 = 0, fc1_w8 = 0, fc1_s8 = 0, fc2_w8 = 0, fc2_s8 = 0;
+    float qkv_sc = 1.0f, proj_sc = 1.0f, fc1_sc = 1.0f, fc2_sc = 1.0f;   // float16 weight scales
   };
   const bool f8 = ctx->f8;
+  const bool f16 = ctx->f16;
+  float m1sc = 1.0f, m2sc = 1.0f;   // merger float16 weight scales
   std::vector<LayerOff> lo(c.layers);
 
   size_t lut_off = P.reserve(3 * 256 * 2);
@@ -249,7 +303,7 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
       return part * d + head * hd + kk + (s < 32 ? 0 : r);
     };
     auto qkv_src = [&](int64_t j, int64_t k) { return wq[src_row(j) * d + k]; };
-    L.qkv_w = P.mat(3 * d, d, qkv_src);
+    L.qkv_w = f16 ? P.mat16(3 * d, d, qkv_src, L.qkv_sc) : P.mat(3 * d, d, qkv_src);
     if (f8) L.qkv_w8 = P.mat8(3 * d, d, qkv_src, L.qkv_s8);
     L.qkv_b = P.vec(3 * d, [&](int64_t j) { return bq[src_row(j)]; });
 
@@ -257,7 +311,7 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
     const HostTensor* pb = P.get(p + "proj.b", {d});
     if (!pw || !pb) goto fail;
     auto proj_src = [&](int64_t o, int64_t k) { return pw->data[o * d + k]; };
-    L.proj_w = P.mat(d, d, proj_src);
+    L.proj_w = f16 ? P.mat16(d, d, proj_src, L.proj_sc) : P.mat(d, d, proj_src);
     if (f8) L.proj_w8 = P.mat8(d, d, proj_src, L.proj_s8);
     L.proj_b = P.vec(d, [&](int64_t i) { return pb->data[i]; });
 
@@ -269,9 +323,9 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
       if (!w1 || !b1 || !w2 || !b2) goto fail;
       auto fc1_src = [&](int64_t o, int64_t k) { return o < mlp ? w1->data[o * d + k] : 0.f; };
       auto fc2_src = [&](int64_t o, int64_t k) { return k < mlp ? w2->data[o * mlp + k] : 0.f; };
-      L.fc1_w = P.mat(mp, d, fc1_src);
+      L.fc1_w = f16 ? P.mat16(mp, d, fc1_src, L.fc1_sc) : P.mat(mp, d, fc1_src);
       L.fc1_b = P.vec(mp, [&](int64_t o) { return o < mlp ? b1->data[o] : 0.f; });
-      L.fc2_w = P.mat(d, mp, fc2_src);
+      L.fc2_w = f16 ? P.mat16(d, mp, fc2_src, L.fc2_sc) : P.mat(d, mp, fc2_src);
       if (f8) {
         L.fc1_w8 = P.mat8(mp, d, fc1_src, L.fc1_s8);
         L.fc2_w8 = P.mat8(d, mp, fc2_src, L.fc2_s8);
@@ -298,14 +352,14 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
         return (up ? wu : wg)->data[o * d + k];
       };
       auto fc2_src = [&](int64_t o, int64_t k) { return k < mlp ? wd->data[o * mlp + k] : 0.f; };
-      L.fc1_w = P.mat(2 * mp, d, fc1_src);
+      L.fc1_w = f16 ? P.mat16(2 * mp, d, fc1_src, L.fc1_sc) : P.mat(2 * mp, d, fc1_src);
       L.fc1_b = P.vec(2 * mp, [&](int64_t j) {
         bool up;
         const int64_t o = gu(j, up);
         if (o >= mlp) return 0.f;
         return (up ? bu : bg)->data[o];
       });
-      L.fc2_w = P.mat(d, mp, fc2_src);
+      L.fc2_w = f16 ? P.mat16(d, mp, fc2_src, L.fc2_sc) : P.mat(d, mp, fc2_src);
       L.fc2_b = P.vec(d, [&](int64_t i) { return bd->data[i]; });
       if (f8) {
         L.fc1_w8 = P.mat8(2 * mp, d, fc1_src, L.fc1_s8);
@@ -336,9 +390,9 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
     m1w8 = m1s8 = m2w8 = m2s8 = 0;
     auto m1_src = [&](int64_t o, int64_t k) { return w1->data[o * md + k]; };
     auto m2_src = [&](int64_t o, int64_t k) { return w2->data[o * md + k]; };
-    m1w = P.mat(md, md, m1_src);
+    m1w = f16 ? P.mat16(md, md, m1_src, m1sc) : P.mat(md, md, m1_src);
     m1b = P.vec(md, [&](int64_t i) { return b1->data[i]; });
-    m2w = P.mat(od, md, m2_src);
+    m2w = f16 ? P.mat16(od, md, m2_src, m2sc) : P.mat(od, md, m2_src);
     if (f8) {
       m1w8 = P.mat8(md, md, m1_src, m1s8);
       m2w8 = P.mat8(od, md, m2_src, m2s8);
@@ -388,6 +442,7 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
       X.fc2_w = bf(L.fc2_w); X.fc2_b = fl(L.fc2_b);
       X.qkv_w8 = b8(L.qkv_w8); X.qkv_s8 = b8(L.qkv_s8);
       X.proj_w8 = b8(L.proj_w8); X.proj_s8 = b8(L.proj_s8);
+      X.qkv_sc = L.qkv_sc; X.proj_sc = L.proj_sc; X.fc1_sc = L.fc1_sc; X.fc2_sc = L.fc2_sc;
       X.fc1_w8 = b8(L.fc1_w8); X.fc1_s8 = b8(L.fc1_s8);
       X.fc2_w8 = b8(L.fc2_w8); X.fc2_s8 = b8(L.fc2_s8);
     }
@@ -396,6 +451,7 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
     W.m2_w = bf(m2w); W.m2_b = fl(m2b);
     W.m1_w8 = b8(m1w8); W.m1_s8 = b8(m1s8);
     W.m2_w8 = b8(m2w8); W.m2_s8 = b8(m2s8);
+    W.m1_sc = m1sc; W.m2_sc = m2sc;
   }
   ctx->host.clear();
   ctx->finalized = true;

@@ -18,7 +18,7 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 
 class GpuRun:
-    def __init__(self, wl, activation_precision: str = "bf16f8"):
+    def __init__(self, wl, activation_precision: str = "f16"):
         self.wl = wl
         self.prec = activation_precision
         cfg = wl.cfg
@@ -80,16 +80,17 @@ class GpuRun:
         c, n, S = self.cfg, self.n, self.S
         d, h, hd = c.hidden, c.heads, c.head_dim
         L = c.layers
+        a16 = torch.float16 if self.prec == "f16" else torch.bfloat16   # activations, q, k, v
         if layer == -1:
             shape, dt = ((n, 1176), torch.bfloat16) if step == 0 else ((n, d), torch.float32)
         elif layer == L:
-            shape, dt = {1: ((n, S * d), torch.bfloat16), 2: ((n // 4, S * 4 * d), torch.bfloat16),
+            shape, dt = {1: ((n, S * d), a16), 2: ((n // 4, S * 4 * d), a16),
                          3: ((n // 4, c.out_dim), torch.float32)}[step]
         else:
-            shape, dt = {1: ((n, S * d), torch.bfloat16), 2: ((h, n, hd), torch.bfloat16),
-                         3: ((h, n, hd), torch.bfloat16), 4: ((h, hd, n), torch.bfloat16),
-                         5: ((n, S * d), torch.bfloat16), 6: ((n, d), torch.float32),
-                         7: ((n, S * d), torch.bfloat16), 8: ((n, S * self.mlp_pad), torch.bfloat16),
+            shape, dt = {1: ((n, S * d), a16), 2: ((h, n, hd), a16),
+                         3: ((h, n, hd), a16), 4: ((h, hd, n), a16),
+                         5: ((n, S * d), a16), 6: ((n, d), torch.float32),
+                         7: ((n, S * d), a16), 8: ((n, S * self.mlp_pad), a16),
                          9: ((n, d), torch.float32)}[step]
         dst = torch.empty(shape, dtype=dt, device="cuda")
         self.tower.debug_stage(self.plan, self.pixels, self.ws, layer, step, dst)
@@ -151,8 +152,14 @@ def assert_encoder_tolerance(got: np.ndarray, ref: np.ndarray, max_abs=2e-2, mea
     assert ma <= max_abs and mr <= mean_rel, f"{what}: max_abs={ma:.3e} mean_rel={mr:.3e}"
 
 
+def unit(run) -> float:
+    """Relative rounding unit of the library's 16-bit activations: 2^-11 for float16, 2^-8 for
+    bfloat16 (one unit of the last place at the bottom of a binade)."""
+    return 2.0 ** -11 if run.prec == "f16" else 2.0 ** -8
+
+
 def assert_close_bf16(got: np.ndarray, ref: np.ndarray, rel=2.0 ** -7, abs_=1e-6, what="", extra=0.0):
-    """Element-wise |got - ref| <= abs + rel * |ref| + extra (bf16 output rounding plus fp32
+    """Element-wise |got - ref| <= abs + rel * |ref| + extra (16-bit output rounding plus fp32
     accumulation; extra: a per-element bound of a known approximation, e.g. the e4m3 residual
     products)."""
     err = np.abs(got - ref)

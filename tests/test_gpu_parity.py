@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_support import GpuRun, assert_close_bf16, assert_encoder_tolerance, f8_extra  # noqa: E402
+from gpu_support import GpuRun, assert_close_bf16, assert_encoder_tolerance, f8_extra, unit  # noqa: E402
 
 _RUNS = {}
 
@@ -39,11 +39,12 @@ def say(msg):
     sys.stdout.flush()
 
 
-# compensated activations: hi+lo bf16 pairs, or bf16 + e4m3 residual
-PRECS = ["bf16x2", "bf16f8"]
+# activation forms: float16 (the default), and the two compensated bf16 forms (hi+lo pairs,
+# bf16 + e4m3 residual)
+PRECS = ["f16", "bf16x2", "bf16f8"]
 
 
-def get_run(idx: int, layers=None, prec="bf16f8") -> GpuRun:
+def get_run(idx: int, layers=None, prec="f16") -> GpuRun:
     key = (idx, layers, prec)
     if key not in _RUNS:
         say(f"building workload {idx} layers={layers} activations={prec}")
@@ -126,7 +127,8 @@ def check_block(run, layer):
     r_in = run.stage(layer - 1, 9) if layer > 0 else run.stage(-1, 1)
     h1 = run.stage(layer, 1)
     ref = O.norm(r_in, run.wl.weights, p + ".n1", c.norm_kind, c.norm_eps)
-    assert_close_bf16(h1, ref, rel=2.0 ** -8, abs_=1e-5, what=f"L{layer} norm1")
+    un = unit(run)
+    assert_close_bf16(h1, ref, rel=un, abs_=1e-5, what=f"L{layer} norm1")
 
     # the library stores q times log2(e)/sqrt(head_dim) (the attention kernel's exp2 scale)
     qg = run.stage(layer, 2) / (np.log2(np.e) / np.sqrt(hd))
@@ -139,7 +141,7 @@ def check_block(run, layer):
     ex = (0.0, 0.0, 0.0) if np.isscalar(e) else \
         (rope_pairs(e[:, :d], H, hd), rope_pairs(e[:, d:2 * d], H, hd), e[:, 2 * d:].reshape(-1, H, hd))
     for (nm, got, want), x in zip((("q", qg, q), ("k", kg, k), ("v", vg, v)), ex):
-        assert_close_bf16(got, want, rel=2.0 ** -8, abs_=2e-4, what=f"L{layer} {nm}+rope", extra=x)
+        assert_close_bf16(got, want, rel=un, abs_=2e-4, what=f"L{layer} {nm}+rope", extra=x)
 
     og = run.stage(layer, 5)
     o = O.attention(qg, kg, vg, segs, rows=rows).reshape(-1, d)
@@ -153,7 +155,7 @@ def check_block(run, layer):
 
     h2 = run.stage(layer, 7)
     assert_close_bf16(h2, O.norm(r1g, run.wl.weights, p + ".n2", c.norm_kind, c.norm_eps),
-                      rel=2.0 ** -8, abs_=1e-5, what=f"L{layer} norm2")
+                      rel=un, abs_=1e-5, what=f"L{layer} norm2")
 
     ag = run.stage(layer, 8)
     if c.mlp_kind == "gelu":
@@ -167,7 +169,7 @@ def check_block(run, layer):
         w2, b2 = W64(run, p + ".down.w"), W64(run, p + ".down.b")
         eg, eu = f8_extra(run, h2, W64(run, p + ".gate.w")), f8_extra(run, h2, W64(run, p + ".up.w"))
         ea = 1.1 * np.abs(u) * eg + np.abs(O.silu(g)) * eu + eg * eu   # |silu'| <= 1.1
-    assert_close_bf16(ag, a, rel=2.0 ** -7, abs_=2e-4, what=f"L{layer} mlp activation", extra=ea)
+    assert_close_bf16(ag, a, rel=2 * un, abs_=2e-4, what=f"L{layer} mlp activation", extra=ea)
 
     r2g = run.stage(layer, 9)
     assert_close_bf16(r2g, r1g + ag @ w2.T + b2, rel=1e-5, abs_=2e-4, what=f"L{layer} mlp out+residual",
@@ -195,11 +197,11 @@ def test_patch_embed_and_merger_layer_local(idx, prec):
     rl = run.stage(c.layers - 1, 9)
     u = run.stage(c.layers, 1)
     assert_close_bf16(u, O.norm(rl, run.wl.weights, "mrg.nq", c.norm_kind, c.norm_eps),
-                      rel=2.0 ** -8, abs_=1e-5, what="merger norm")
+                      rel=unit(run), abs_=1e-5, what="merger norm")
     z1 = run.stage(c.layers, 2)
     u4 = u.reshape(-1, 4 * c.hidden)
     ref1 = O.gelu(u4 @ W64(run, "mrg.fc1.w").T + W64(run, "mrg.fc1.b"))
-    assert_close_bf16(z1, ref1, rel=2.0 ** -7, abs_=2e-4, what="merger fc1+gelu",
+    assert_close_bf16(z1, ref1, rel=2 * unit(run), abs_=2e-4, what="merger fc1+gelu",
                       extra=1.13 * f8_extra(run, u4, W64(run, "mrg.fc1.w")))
     out = run.encode()
     ref2 = z1 @ W64(run, "mrg.fc2.w").T + W64(run, "mrg.fc2.b")
@@ -285,7 +287,7 @@ def test_e4m3_residual_saturation():
     wl.weights["blk0.fc1.w"] = wl.weights["blk0.fc1.w"] * np.float32(128.0)
     ref = O.forward_workload(wl)
     errs = {}
-    for prec in ("bf16", "bf16x2", "bf16f8"):
+    for prec in ("bf16", "bf16x2", "bf16f8", "f16"):
         run = GpuRun(wl, activation_precision=prec)
         if prec == "bf16f8":
             a = run.stage(0, 8)
@@ -296,7 +298,7 @@ def test_e4m3_residual_saturation():
         assert np.all(np.isfinite(got)), f"{prec}: non-finite output"
         errs[prec] = float(np.abs(got - ref).sum() / np.abs(ref).sum())
         say(f"saturation {prec}: mean_rel={errs[prec]:.3e}")
-    assert errs["bf16f8"] < errs["bf16"] and errs["bf16x2"] < errs["bf16"], errs
+    assert errs["bf16f8"] < errs["bf16"] and errs["bf16x2"] < errs["bf16"] and errs["f16"] < errs["bf16"], errs
 
 
 def test_edge_items_end_to_end():

@@ -47,10 +47,10 @@ def test_config_validation(lib):
         assert _status(lambda: B.VisionTower(b, lib)) == B.VIT_E_ARG, b
     assert lib.vit_create(None, ctypes.byref(B._P())) == B.VIT_E_ARG
     assert b"NULL" in lib.vit_last_error()
-    for prec in ("bf16", "bf16x2", "bf16f8"):
+    for prec in ("f16", "bf16", "bf16x2", "bf16f8"):
         assert _status(lambda: B.VisionTower(cfg, lib, activation_precision=prec)) == B.VIT_OK, prec
     c = B.make_config(cfg)
-    c.activation_precision = 3
+    c.activation_precision = 4
     assert lib.vit_create(ctypes.byref(c), ctypes.byref(B._P())) == B.VIT_E_ARG
     assert b"activation_precision" in lib.vit_last_error()
 

@@ -63,15 +63,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen2vl-8img-mixed-32
 def kernel_sources_digest():
     """sha256 over the HIP kernel sources and the header they share (its layout helpers are
     kernel code): counter figures taken with other kernels are stale."""
-    import glob
-    import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "multimodal_vlm_vision_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from multimodal_vlm_vision_amd.rocprof_summary import kernel_sources_digest as digest
+    return digest()
 
 
 def measured_traffic(kernel):

@@ -35,10 +35,11 @@
 // delaying it.
 //
 // K tiles (32 keys x head_dim, row stride head_dim + 8 so 16-byte fragment
-// reads of 16 consecutive rows hit distinct banks) and V^T tiles (head_dim
-// rows x the 40 keys from the 8-aligned token at or below the block's first
-// key, so every load is a whole 16-byte chunk of a 16-byte aligned V^T row)
-// move global -> LDS with gfx950's 16-byte buffer loads into LDS, into a
+// reads of 16 consecutive rows hit distinct banks; keys in the row order of
+// key_at, which makes each lane's probabilities 8 consecutive keys) and V^T
+// tiles (head_dim rows x the block's 32 keys, 16-byte chunks rotated by row
+// bits 2-3, so a P.V fragment is one conflict-free 16-byte read) move
+// global -> LDS with gfx950's 16-byte buffer loads into LDS, into a
 // double-buffered ring.  Work units are laid out so each XCD
 // (workgroups are dispatched round-robin over 8 XCDs) runs contiguous
 // (head, segment) ranges and shares their K/V in its L2.  Long segments use
@@ -126,6 +127,15 @@ __device__ __forceinline__ uint32_t rest_e4m3x4(float a, float b, float c, float
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f(c), f(d), lo, true);
 }
 
+// Key of row p of a block's K tile.  S^T = K Q^T leaves lane (query, h) with rows
+// 8g + 4h + e (g, e < 4) of the 32-row score tile; loading key 16c + 8h + 4b + e into row
+// 16c + 8b + 4h + e makes the lane's probabilities of reduction chunk c (g = 2c, 2c + 1) the
+// eight consecutive keys 16c + 8h + 0..7 -- in the order the P.V MFMA pairs them with one
+// 16-byte V^T chunk.  Rows past 32 (the padding loads) keep their index.
+__device__ __forceinline__ int key_at(int p) {
+  return p < 32 ? (p & 0x13) | ((p & 4) << 1) | ((p & 8) >> 1) : p;
+}
+
 // DYN: the work-list length comes from device memory at run time (bucketed graphs); a separate
 // instantiation, so the plain path keeps it a launch constant.
 template <int HD, int NW, bool DYN, bool F16>
@@ -136,10 +146,10 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
   constexpr int KS = HD + 8;                 // K tile row stride (elements)
   constexpr int KCH = KS / 8;                // 16-byte chunks per K row (the last is padding)
   constexpr int KLOADS = (KB * KCH + 63) / 64;      // 1 KB direct loads per K tile
-  // V^T tile: each row holds the 40 keys from the 8-aligned token at or below the block's first
-  // key (16-byte loads need 16-byte aligned rows; segments start at multiples of 4 tokens), so
-  // the block's keys sit at DELTA = seg_start % 8 within the row.
-  constexpr int VP = KB + 8;                 // keys per V^T tile row (80 bytes, 5 chunks)
+  // V^T tile: each row holds the block's 32 keys (4 chunks of 8 keys), its chunks rotated by
+  // bits 2-3 of the row (chunk q at q ^ ((row >> 2) & 3)), so that a fragment read -- one 16-byte
+  // chunk of 32 consecutive rows -- touches every bank once per 16 lanes.
+  constexpr int VP = KB;                     // keys per V^T tile row (64 bytes, 4 chunks)
   constexpr int VCH = VP / 8;                // 16-byte chunks per V^T row
   constexpr int VDW = VP / 2;                // dwords per V^T row
   constexpr int VROWS = DT * 32;             // rows HD.. are constant (ones, then zeros)
@@ -172,7 +182,6 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
   const uint16_t* Qh = a.q + (int64_t)head * a.n_tok * HD;
   const uint16_t* Kh = a.k + (int64_t)head * a.n_tok * HD;
   const uint16_t* Vh = a.vt + (int64_t)head * HD * a.vt_ld;
-  const int delta = seg0 & 7;
 
   // constant V^T rows: HD = ones (softmax denominator), the rest zeros; never overwritten
   for (int i = tid; i < (VROWS - HD) * VDW; i += NW * 64) {
@@ -217,7 +226,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
   // so reads past a segment's end are kept in bounds by the layout instead: K rows past the
   // end are the next segment's (or, for the last head, the V^T region that follows K), and
   // their scores are masked to -inf; a V^T row has at least 40 zeroed columns past the last
-  // token (the planner's pitch), which covers the farthest read (39 tokens past a segment),
+  // token (the planner's pitch), which covers the farthest read (31 tokens past a segment),
   // so the keys that get P = 0 multiply finite zeros, never stale memory.
   constexpr int KLW = (KLOADS + NW - 1) / NW, VLW = (VLOADS + NW - 1) / NW;
   const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kh), (short)0,
@@ -231,11 +240,12 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
 #pragma unroll
   for (int j = 0; j < KLW; ++j) {
     const int id = (wv + j * NW) * 64 + lane, r = id / KCH, c = id % KCH;
-    koff[j] = (uint32_t)(r * HD + (c < HD / 8 ? c * 8 : 0)) * 2;
+    koff[j] = (uint32_t)(key_at(r) * HD + (c < HD / 8 ? c * 8 : 0)) * 2;
   }
 #pragma unroll
   for (int j = 0; j < VLW; ++j) {
-    const int id = (wv + j * NW) * 64 + lane, dd = id / VCH, c = id % VCH;
+    const int id = (wv + j * NW) * 64 + lane, dd = id / VCH, q = id % VCH;
+    const int c = q ^ ((dd >> 2) & 3);   // the global chunk that lands in slot q of row dd
     voff[j] = dd < HD ? (uint32_t)(dd * a.vt_ld + 8 * c) * 2 : 0u;
   }
   auto dload = [&](int kb, uint16_t* dK, uint32_t* dV) {
@@ -253,7 +263,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
       if (i >= VLOADS) break;
       if (i * 64 + lane < HD * VCH)   // lanes past the real rows must not touch the constant rows
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dV + i * 64 * 4), 16,
-                                                 voff[j], (key0 - delta) * 2, 0, 0);
+                                                 voff[j], key0 * 2, 0, 0);
     }
   };
 
@@ -280,7 +290,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
       if (key_base + KB > n) {
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (key_base + 8 * (e / 4) + 4 * h + (e % 4) >= n)
+          if (key_base + key_at(8 * (e / 4) + 4 * h + (e % 4)) >= n)
 #pragma unroll
             for (int t = 0; t < QT; ++t) S[t][e] = -INFINITY;
       }
@@ -317,17 +327,17 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
         pb[t][0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
         pb[t][1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
       }
-      // ---- O^T += V^T P^T over the 32 keys; V^T fragment of chunk c lists keys
-      //      16c + 4h + 0..3, 16c + 8 + 4h + 0..3 (the order of the lane's probabilities)
+      // ---- O^T += V^T P^T over the 32 keys; the lane's probabilities of chunk c are the keys
+      //      16c + 8h + 0..7 (K rows are loaded in key_at order), i.e. one whole 16-byte chunk
+      //      2c + h of a V^T row
       __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vr = Vt + (32 * dt + l32) * VP + delta + 4 * h;
+        const int row = 32 * dt + l32;
+        const uint16_t* vr = Vt + row * VP;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + 16 * c);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16 * c + 8);
-          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vr + 8 * ((2 * c + h) ^ ((row >> 2) & 3)));
 #pragma unroll
           for (int t = 0; t < QT; ++t) O[t][dt] = mma<F16>(vf, pb[t][c], O[t][dt]);
         }
@@ -399,7 +409,7 @@ hipError_t run_hd(const AttnArgs& a, hipStream_t st) {
 }
 
 // Zeroes V^T columns [n, n + 64) (clipped to the pitch) of every row: the attention's tile
-// loads read at most 39 keys past the last token, and the pitch leaves at least 40 columns.  n is the token count, read at run time
+// loads read at most 31 keys past the last token, and the pitch leaves at least 40 columns.  n is the token count, read at run time
 // when n_tok_dev is set (bucketed graph).
 __global__ void vt_pad_zero_kernel(uint16_t* vt, int rows, int64_t n_tok, const int32_t* n_tok_dev, int64_t vt_ld) {
   const int64_t n = n_tok_dev ? (int64_t)*n_tok_dev : n_tok;

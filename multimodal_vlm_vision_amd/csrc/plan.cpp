@@ -252,10 +252,10 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   p->off_h = take((size_t)std::max(Np * S * d, Up * 4 * S * d) * 2);
   p->off_q = take((size_t)N * d * 2);
   p->off_k = take((size_t)N * d * 2);
-  // V^T rows: 16-byte aligned for the attention's whole-chunk tile loads, with at least 40
-  // columns past the last token that are zeroed every forward.  A key block's load reaches up
-  // to 39 tokens past a segment's last key (keys that get probability 0); those columns must
-  // hold finite values, since 0 * NaN is NaN inside the MFMA, and must stay inside the row.
+  // V^T rows: a pitch that is a multiple of 8 tokens, with at least 40 columns past the last
+  // token that are zeroed every forward.  A key block's load reaches up to 31 tokens past a
+  // segment's last key (keys that get probability 0); those columns must hold finite values,
+  // since 0 * NaN is NaN inside the MFMA, and must stay inside the row.
   p->vt_ld = round_up(N, 8) + 40;
   p->off_vt = take((size_t)p->vt_ld * d * 2);
   p->off_o = take((size_t)Np * S * d * 2);

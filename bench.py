@@ -85,7 +85,7 @@ def measured_traffic(kernel):
     return row["fetch_bytes"] + row["write_bytes"], os.path.relpath(TRAFFIC_FILE, ROOT)
 
 
-def normpatch_stream(n_images=48, side=1344, reps=5):
+def normpatch_stream(n_images=48, side=1344, reps=20):
     """normpatch alone on a >= 1 GB streaming batch (48 images of 1344 x 1344): the
     per-forward traffic of the bench batch (~52 MB) fits in the 256 MB last-level cache,
     so HBM bandwidth is measured on a batch several times larger than that cache.

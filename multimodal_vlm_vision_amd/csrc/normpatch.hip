@@ -11,21 +11,27 @@
 // host that one float32 fma per byte rounds to the same 768 values, the
 // kernel evaluates that fma instead of the table (fewer LDS lookups).
 //
-// HBM-bound streaming kernel.  One workgroup handles kUnitsPerBlock merge
-// units that are consecutive in row order, so both sides stream:
+// HBM-bound streaming kernel.  One workgroup of 512 threads handles
+// kUnitsPerBlock = 4 merge units that are consecutive in row order, so both
+// sides stream:
 //  * input: each unit's 28 pixel rows x 84 bytes per temporal slot are staged
 //    in LDS with 12-byte loads ordered (slot, pixel row, unit, piece), so
 //    adjacent lanes read adjacent bytes of one image row, all issued before
-//    the first LDS store; an image's single frame is read once and serves
-//    both temporal slots;
-//  * output: the block's 4 * kUnitsPerBlock = 32 rows of 1184 bf16 (columns
-//    1176..1183 zero, so the patch-embed GEMM needs no K tail) are two whole
-//    16-row groups of the blocked GEMM layout (kt_index), i.e. one contiguous
+//    the first LDS store, and the block's tables are built while they are in
+//    flight; an image's single frame is read once and serves both temporal
+//    slots;
+//  * output: the block's 4 * kUnitsPerBlock = 16 rows of 1184 bf16 (columns
+//    1176..1183 zero, so the patch-embed GEMM needs no K tail) are one whole
+//    16-row group of the blocked GEMM layout (kt_index), i.e. one contiguous
 //    run, written as 16-byte nontemporal stores by consecutive lanes in
 //    memory order.
-// A per-block table maps each output feature to its staged byte (offset,
-// channel, temporal slot), so a 16-byte output chunk costs one table read and
-// 8 pairs of LDS lookups instead of per-element index division.
+// (On the 1.3 GB streaming batch, 4 units per 512-thread workgroup with the
+// loads issued first measured 224-228 us against 236-238 us for 8 units with
+// the tables built first; 16 units, or 128- and 1024-thread workgroups, were
+// slower.)
+// Two tables built at compile time (video units, image units) map each output
+// feature to its staged byte, so a 16-byte output chunk costs one table read
+// and 8 byte lookups, with no per-element index arithmetic.
 #include <hip/hip_runtime.h>
 
 #include "vit_internal.h"
@@ -35,7 +41,7 @@ namespace vitmi {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kUnitsPerBlock = 8;
+constexpr int kUnitsPerBlock = 4;
 constexpr int kRowBytes = kUnitPx * 3;                        // 84 bytes of one unit pixel row
 constexpr int kRowDwords = kRowBytes / 4;                     // 21
 constexpr int kSlotBytes = kUnitPx * kRowBytes;               // 2352 bytes of one temporal slot
@@ -45,7 +51,6 @@ constexpr int kChunksPerRow = kFeatPad / 8;                   // 148
 constexpr int kChunksPerUnit = 4 * kChunksPerRow;             // 592
 constexpr int kColBlocks = kFeatPad / 32;                     // 37 blocks of 32 features
 static_assert(4 * kUnitsPerBlock % 16 == 0, "a block's rows are whole 16-row groups");
-constexpr uint16_t kPadFeature = 0x8000;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 constexpr int kRowPieces = kRowBytes / 12;                    // 7 pieces of 12 bytes per unit row
 constexpr int kPieceIds = kUnitsPerBlock * kTemporal * kUnitPx * kRowPieces;
@@ -66,16 +71,28 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// feature f = ((c * 2 + tau) * 14 + i) * 14 + j of the unit's top-left patch ->
-// staged byte (tau * 28 + i) * 84 + 3 * j + c, packed as offset | c << 12 | tau << 14.
-__device__ __forceinline__ uint16_t feature_entry(int f) {
-  if (f >= kFeat) return kPadFeature;
-  const int c = f / 392, r1 = f - c * 392;
-  const int tau = r1 / 196, r2 = r1 - tau * 196;
-  const int i = r2 / 14, j = r2 - i * 14;
-  const int off = (tau * kUnitPx + i) * kRowBytes + 3 * j + c;
-  return (uint16_t)(off | (c << 12) | (tau << 14));
-}
+// Staged byte of every output feature, one table per kind of unit: feature
+// f = ((c * 2 + tau) * 14 + i) * 14 + j of the unit's top-left patch is byte
+// (tau * 28 + i) * 84 + 3 * j + c of a video unit's two staged frames, and byte
+// i * 84 + 3 * j + c of an image unit's one frame (both temporal slots are that
+// frame).  Pad features (>= 1176) are whole chunks and never read.  Built at
+// compile time; each workgroup copies both tables into LDS.
+struct FeatureTables {
+  uint16_t off[2][kFeatPad];   // [0] video unit, [1] image unit
+  constexpr FeatureTables() : off() {
+    for (int f = 0; f < kFeatPad; ++f) {
+      if (f >= kFeat) continue;
+      const int c = f / 392, r1 = f - c * 392;
+      const int tau = r1 / 196, r2 = r1 - tau * 196;
+      const int i = r2 / 14, j = r2 - i * 14;
+      off[0][f] = (uint16_t)((tau * kUnitPx + i) * kRowBytes + 3 * j + c);
+      off[1][f] = (uint16_t)(i * kRowBytes + 3 * j + c);
+    }
+  }
+};
+__constant__ __attribute__((aligned(16))) FeatureTables g_feat = FeatureTables();
+constexpr int kPadChunk = kFeat / 8;   // first chunk of pad features (147)
+constexpr int kChanChunks = 392 / 8;   // chunks per channel (49)
 
 template <bool AFFINE>
 __global__ void __launch_bounds__(kThreads)
@@ -83,7 +100,7 @@ normpatch_kernel(const uint8_t* __restrict__ pixels, const UnitDesc* __restrict_
                  int64_t n_units, const int32_t* __restrict__ n_units_dev, const uint16_t* __restrict__ lut_g,
                  NormAffine na, uint16_t* __restrict__ x) {
   __shared__ uint32_t stage[kUnitsPerBlock * kUnitDwords];
-  __shared__ __attribute__((aligned(16))) uint16_t tab[kFeatPad];
+  __shared__ __attribute__((aligned(16))) uint16_t tab[2 * kFeatPad];
   __shared__ uint16_t lut[3 * 256];
   __shared__ UnitDesc sud[kUnitsPerBlock];
   const int tid = threadIdx.x;
@@ -91,15 +108,12 @@ normpatch_kernel(const uint8_t* __restrict__ pixels, const UnitDesc* __restrict_
   const int64_t n_all = n_units_dev ? (int64_t)*n_units_dev : n_units;   // run-time count (bucketed graph)
   if (u0 >= n_all) return;
   const int nu = (int)min<int64_t>(kUnitsPerBlock, n_all - u0);
-  if (!AFFINE)
-    for (int i = tid; i < 3 * 256; i += kThreads) lut[i] = lut_g[i];
-  for (int f = tid; f < kFeatPad; f += kThreads) tab[f] = feature_entry(f);
   if (tid < nu) sud[tid] = units[u0 + tid];
   __syncthreads();
 
   // stage: piece id -> (slot, pixel row, unit, 12-byte piece of the row); images skip slot 1.
-  // Every load of the block is issued before the first LDS store, so a thread waits for
-  // one memory latency, not one per load.
+  // Every load of the block is issued before the first LDS store, and the block's tables are
+  // built while those loads are in flight, so a thread waits for one memory latency.
   Piece v[kLoadsPerThread];
   int dst[kLoadsPerThread];
 #pragma unroll
@@ -116,6 +130,10 @@ normpatch_kernel(const uint8_t* __restrict__ pixels, const UnitDesc* __restrict_
       dst[k] = u * kUnitDwords + (slot * kUnitPx + row) * kRowDwords + 3 * pc;
     }
   }
+  if (!AFFINE)
+    for (int i = tid; i < 3 * 256; i += kThreads) lut[i] = lut_g[i];
+  for (int i = tid; i < 2 * kFeatPad / 8; i += kThreads)
+    reinterpret_cast<uint4*>(tab)[i] = reinterpret_cast<const uint4*>(&g_feat.off[0][0])[i];
 #pragma unroll
   for (int k = 0; k < kLoadsPerThread; ++k)
     if (dst[k] >= 0) {
@@ -137,45 +155,25 @@ normpatch_kernel(const uint8_t* __restrict__ pixels, const UnitDesc* __restrict_
     if (u >= nu) continue;
     const int k8 = kb * 4 + kt_chunk(u0 * 4 + br, pos);   // feature chunk
     const int shift = (rr >> 1) * (kPatch * kRowBytes) + (rr & 1) * (kPatch * 3);
-    const bool image = sud[u].fstride == 0;
+    const int kind = sud[u].fstride == 0;   // 1: image (one frame for both slots)
     const uint8_t* ub = sb + u * kUnitBytes + shift;
-    const uint4 t4 = *reinterpret_cast<const uint4*>(tab + 8 * k8);
-    const uint32_t tw[4] = {t4.x, t4.y, t4.z, t4.w};
-    uint32_t packed[4];
-    if constexpr (AFFINE) {
-      // one channel per chunk (392 = 49 * 8); pad chunks (features >= 1176) are all pad
-      const int ch = (t4.x >> 12) & 3;
-      const float a = ch == 0 ? na.a[0] : ch == 1 ? na.a[1] : na.a[2];
-      const float b = ch == 0 ? na.b[0] : ch == 1 ? na.b[1] : na.b[2];
-      const bool pad = t4.x & kPadFeature;
+    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+    if (k8 < kPadChunk) {   // a chunk lies in one channel; pad chunks stay zero
+      const int ch = k8 >= 2 * kChanChunks ? 2 : k8 >= kChanChunks ? 1 : 0;
+      const uint4 t4 = *reinterpret_cast<const uint4*>(tab + kind * kFeatPad + 8 * k8);
+      const uint32_t tw[4] = {t4.x, t4.y, t4.z, t4.w};
+      if constexpr (AFFINE) {
+        const float a = ch == 0 ? na.a[0] : ch == 1 ? na.a[1] : na.a[2];
+        const float b = ch == 0 ? na.b[0] : ch == 1 ? na.b[1] : na.b[2];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        float y[2];
+        for (int h = 0; h < 4; ++h)
+          packed[h] = pack_bf16(__builtin_fmaf((float)ub[tw[h] & 0xffffu], a, b),
+                                __builtin_fmaf((float)ub[tw[h] >> 16], a, b));
+      } else {
+        const uint16_t* L = lut + ch * 256;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint32_t t = (tw[h] >> (16 * s)) & 0xffffu;
-          const int tau = (t >> 14) & 1;
-          const int off = (int)(t & 0xfff) - (image && tau ? kSlotBytes : 0);
-          y[s] = pad ? 0.f : __builtin_fmaf((float)ub[off], a, b);
-        }
-        packed[h] = pack_bf16(y[0], y[1]);
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        uint32_t pair = 0;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint32_t t = (tw[h] >> (16 * s)) & 0xffffu;
-          uint32_t v = 0;
-          if (!(t & kPadFeature)) {
-            const int tau = (t >> 14) & 1;
-            const int off = (int)(t & 0xfff) - (image && tau ? kSlotBytes : 0);
-            v = lut[((t >> 12) & 3) * 256 + ub[off]];
-          }
-          pair |= v << (16 * s);
-        }
-        packed[h] = pair;
+        for (int h = 0; h < 4; ++h)
+          packed[h] = (uint32_t)L[ub[tw[h] & 0xffffu]] | ((uint32_t)L[ub[tw[h] >> 16]] << 16);
       }
     }
     // streaming output: nontemporal stores (the rows are read once, by the next kernel)

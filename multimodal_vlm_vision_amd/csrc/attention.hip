@@ -39,8 +39,10 @@
 // key_at, which makes each lane's probabilities 8 consecutive keys) and V^T
 // tiles (head_dim rows x the block's 32 keys, 16-byte chunks rotated by row
 // bits 2-3, so a P.V fragment is one conflict-free 16-byte read) move
-// global -> LDS with gfx950's 16-byte buffer loads into LDS, into a
-// double-buffered ring.  Work units are laid out so each XCD
+// global -> LDS with gfx950's 16-byte buffer loads into LDS, into a ring of
+// two stages (of two key blocks per stage and one workgroup barrier per stage
+// for the 4-wave workgroups, one block per stage for the 1-wave ones).  Work
+// units are laid out so each XCD
 // (workgroups are dispatched round-robin over 8 XCDs) runs contiguous
 // (head, segment) ranges and shares their K/V in its L2.  Long segments use
 // 4-wave workgroups (256 queries share each K/V tile); short segments
@@ -158,11 +160,16 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
   constexpr int LIDX = 4 * (LROW / 8) + (LROW % 4), LHALF = (LROW % 8) / 4;
   static_assert(HD % 16 == 0 && KCH % 2 == 1, "head_dim must be a multiple of 16");
 
-  // two ring slots as separate objects: every access below names its slot statically, so
-  // the compiler can tell the prefetch into one slot from the reads of the other and does
-  // not make those reads wait for the prefetch
+  // Ring slots as separate objects: every access below names its slot statically, so the
+  // compiler can tell the prefetch into one slot from the reads of another and does not make
+  // those reads wait for the prefetch.  4-wave workgroups use four slots: two stages of two
+  // key blocks each, one barrier per two blocks, the next pair prefetched while the current
+  // one is computed (the 1-wave workgroups keep two slots: their LDS bounds occupancy).
+  constexpr int XS = NW == 4 ? 1 : 0;   // slots 2 and 3 exist
   __shared__ __attribute__((aligned(16))) uint16_t sK0[KLOADS * 64 * 8], sK1[KLOADS * 64 * 8];
   __shared__ __attribute__((aligned(16))) uint32_t sV0[VROWS * VDW], sV1[VROWS * VDW];
+  __shared__ __attribute__((aligned(16))) uint16_t sK2[XS * KLOADS * 64 * 8 + 8], sK3[XS * KLOADS * 64 * 8 + 8];
+  __shared__ __attribute__((aligned(16))) uint32_t sV2[XS * VROWS * VDW + 4], sV3[XS * VROWS * VDW + 4];
 
   // ---- work unit: XCD-contiguous ranges of (head, unit), units of a segment adjacent
   if (DYN) n_work = *n_work_dev;
@@ -189,6 +196,10 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
     const uint32_t v = i < VDW ? one2 : 0u;
     sV0[HD * VDW + i] = v;
     sV1[HD * VDW + i] = v;
+    if (XS) {
+      sV2[HD * VDW + i] = v;
+      sV3[HD * VDW + i] = v;
+    }
   }
 
   // ---- this wave's query fragments (B operand of S^T = K Q^T): query 32t + l32, dims 16c + 8h
@@ -267,9 +278,10 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
     }
   };
 
-  // one key block: prefetch block kb + 1 into (nK, nV) while computing on (cK, cV)
-  auto block = [&](int kb, const uint16_t* cK, const uint32_t* cV, uint16_t* nK, uint32_t* nV) {
-    if (kb + 1 < nkb) dload(kb + 1, nK, nV);
+  // one key block computed on (cK, cV); with sync, block kb + 1 is first prefetched into
+  // (nK, nV) and the workgroup meets at a barrier after the block (the two-slot ring)
+  auto block = [&](int kb, const uint16_t* cK, const uint32_t* cV, uint16_t* nK, uint32_t* nV, bool sync = true) {
+    if (sync && kb + 1 < nkb) dload(kb + 1, nK, nV);
     if (qbase < n) {
       const uint16_t* Kt = cK;
       const uint16_t* Vt = reinterpret_cast<const uint16_t*>(cV);
@@ -344,14 +356,35 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
       }
       __builtin_amdgcn_s_setprio(0);
     }
-    __syncthreads();
+    if (sync) __syncthreads();
   };
 
-  dload(0, sK0, sV0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; kb += 2) {
-    block(kb, sK0, sV0, sK1, sV1);
-    if (kb + 1 < nkb) block(kb + 1, sK1, sV1, sK0, sV0);
+  if constexpr (XS) {
+    // two key blocks per barrier: slots (0, 2) hold one pair, (1, 3) the next; the barrier
+    // after a pair makes the prefetched pair visible and frees the pair just read
+    dload(0, sK0, sV0);
+    if (1 < nkb) dload(1, sK2, sV2);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; kb += 4) {
+      if (kb + 2 < nkb) dload(kb + 2, sK1, sV1);
+      if (kb + 3 < nkb) dload(kb + 3, sK3, sV3);
+      block(kb, sK0, sV0, nullptr, nullptr, false);
+      if (kb + 1 < nkb) block(kb + 1, sK2, sV2, nullptr, nullptr, false);
+      __syncthreads();
+      if (kb + 2 >= nkb) break;
+      if (kb + 4 < nkb) dload(kb + 4, sK0, sV0);
+      if (kb + 5 < nkb) dload(kb + 5, sK2, sV2);
+      block(kb + 2, sK1, sV1, nullptr, nullptr, false);
+      if (kb + 3 < nkb) block(kb + 3, sK3, sV3, nullptr, nullptr, false);
+      __syncthreads();
+    }
+  } else {
+    dload(0, sK0, sV0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; kb += 2) {
+      block(kb, sK0, sV0, sK1, sV1);
+      if (kb + 1 < nkb) block(kb + 1, sK1, sV1, sK0, sV0);
+    }
   }
 
   if (qbase >= n) return;

@@ -204,6 +204,24 @@ vit_status vit_plan_sizes(const vit_plan* plan, size_t* pixel_bytes, size_t* ws_
  * reorders rows).  dst may be NULL; otherwise it holds N int32 (host). */
 vit_status vit_plan_rows(const vit_plan* plan, int64_t* n_patches, int32_t* dst);
 
+/* The long attention work units of a plan (test and tuning aid; pure host).
+ * Segments are the block-diagonal attention's per-item (or per-window)
+ * sequences ("vLLM multimodal inference | ViT performance optimisation",
+ * section 3.4, cu_seqlens).  layer_kind 0 = item segments, 1 = windows.
+ * split 0: the plain list (one unit per block of 256 queries of a segment;
+ * what bucketed graphs run); split 1: the list the eager forward and
+ * whole-forward graphs run (the plain list, or key-split units when the
+ * planner split some units' key ranges to balance the launch's tail, in
+ * which case *n_merge > 0 query blocks are merged from *n_parts partial
+ * slots).  units, if not NULL, receives *n_units rows of 8 int32 (host):
+ * segment start row, segment length, first query of the unit (relative to
+ * the segment start), first and end key block (32 keys each), partial slot
+ * (-1: the unit covers all keys of its queries), 0, 0.  Call once with
+ * units = NULL to size the buffer.  Errors: VIT_E_ARG for a NULL plan or a
+ * layer_kind / split outside {0, 1}. */
+vit_status vit_plan_attention_units(const vit_plan* plan, int32_t layer_kind, int32_t split,
+                                    int32_t* units, int32_t* n_units, int32_t* n_merge, int32_t* n_parts);
+
 /* Enqueues the whole forward on `stream` and returns without synchronising.
  * Defined by: "vLLM multimodal inference | ViT performance optimisation",
  * section 2.2 (encoding steps 1-4: patchify, patch embedding, 2D RoPE,
@@ -283,7 +301,11 @@ void vit_graph_destroy(vit_graph* g);
  * read the batch sizes (patches, merge units, attention work-list lengths)
  * from device memory, so padded capacity is skipped by normalisation,
  * attention and the products rather than computed.  Launched plainly
- * (vit_graph_launch) it encodes `plan`.  Also allocates one pinned host
+ * (vit_graph_launch) it encodes `plan`.  Its attention runs the plain work
+ * lists (one unit per 256-query block, see vit_plan_attention_units), never
+ * key-split units, so for a plan whose eager forward splits key ranges the
+ * replay equals vit_encode's result to rounding (the same softmax summed in
+ * another order) rather than bit for bit.  Also allocates one pinned host
  * staging buffer of the plan's metadata size.  Same requirements as
  * vit_graph_capture. */
 vit_status vit_graph_capture_bucket(const vit_ctx* ctx, const vit_plan* plan, void* ws,

@@ -67,6 +67,9 @@ _SIGS = {
     "vit_plan_sizes": (ctypes.c_int32, [_P, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t),
                                         ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
     "vit_plan_rows": (ctypes.c_int32, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]),
+    "vit_plan_attention_units": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                                  ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                                  ctypes.POINTER(ctypes.c_int32)]),
     "vit_encode": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "vit_encode_patches_u8": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "vit_encode_noalloc": (ctypes.c_int32, [_P, _P, _P, _P, _P]),
@@ -195,6 +198,19 @@ class Plan:
         _check(self.lib, self.lib.vit_plan_rows(self.handle, ctypes.byref(n),
                                                 out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
         return out
+
+    def attention_units(self, windows: bool = False, split: bool = True):
+        """The long attention work units (rows of: segment start, segment length, first query,
+        first and end key block, partial slot or -1, 0, 0), the number of merged query blocks
+        and of partial slots; split=False gives the plain list."""
+        n, nm, npart = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(self.lib, self.lib.vit_plan_attention_units(self.handle, int(windows), int(split), None,
+                                                           ctypes.byref(n), ctypes.byref(nm), ctypes.byref(npart)))
+        out = np.zeros((n.value, 8), dtype=np.int32)
+        _check(self.lib, self.lib.vit_plan_attention_units(self.handle, int(windows), int(split),
+                                                           out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                                           ctypes.byref(n), ctypes.byref(nm), ctypes.byref(npart)))
+        return out, nm.value, npart.value
 
     def close(self):
         if self.handle:

@@ -255,11 +255,19 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
     at.q = Q; at.k = K; at.vt = VT; at.o = O; at.o_split = split; at.o8 = O8; at.f16 = f16;
     at.n_tok = N; at.vt_ld = pl->vt_ld;
     at.heads = c.heads; at.head_dim = hd;
-    at.work_long = reinterpret_cast<const AttnWork*>(ws + lists.off_long);
+    // key-split units with their merge (not in bucketed graphs, whose capacity checks and
+    // device-side counts are those of the plain lists)
+    const bool use_split = !dims && lists.n_merge > 0;
+    at.work_long = reinterpret_cast<const AttnWork*>(ws + (use_split ? lists.off_long_split : lists.off_long));
     at.work_short = reinterpret_cast<const AttnWork*>(ws + lists.off_short);
-    if (lists.n_long > 0) {
+    if (use_split) {
+      at.part = reinterpret_cast<float*>(ws + pl->off_part);
+      at.n_parts = lists.n_parts;
+    }
+    const int n_long = use_split ? lists.n_long_split : lists.n_long;
+    if (n_long > 0) {
       AttnArgs a1 = at;
-      a1.n_long = lists.n_long;
+      a1.n_long = n_long;
       if (dims) a1.n_long_dev = windowed ? &dims->win_long : &dims->full_long;
       LAUNCH("attention", 4.0 * dd * lists.sq_long, 0, true, launch_attention(a1, st));
     }
@@ -268,6 +276,12 @@ vit_status forward(const vit_ctx* ctx, const vit_plan* pl, const uint8_t* pixels
       a2.n_short = lists.n_short;
       if (dims) a2.n_short_dev = windowed ? &dims->win_short : &dims->full_short;
       LAUNCH("attention_short", 4.0 * dd * lists.sq_short, 0, true, launch_attention(a2, st));
+    }
+    if (use_split) {
+      const double part_bytes = (double)c.heads * lists.n_parts * (hd + 2) * 256 * 4;
+      LAUNCH("attention_merge", 0, part_bytes + (double)c.heads * lists.n_merge * 256 * hd * 2, false,
+             launch_attention_merge(at, reinterpret_cast<const AttnMerge*>(ws + lists.off_merge), lists.n_merge,
+                                    st));
     }
     if (stop.hit(l, 5)) return copy_act(O, O8, N, d, 1);
 
@@ -558,6 +572,23 @@ vit_status vit_plan_rows(const vit_plan* plan, int64_t* n_patches, int32_t* dst)
   if (n_patches) *n_patches = plan->n_rows;
   if (dst && !plan->row_order.empty())
     std::memcpy(dst, plan->row_order.data(), plan->row_order.size() * sizeof(int32_t));
+  return VIT_OK;
+}
+
+vit_status vit_plan_attention_units(const vit_plan* plan, int32_t layer_kind, int32_t split, int32_t* units,
+                                    int32_t* n_units, int32_t* n_merge, int32_t* n_parts) {
+  if (!plan || (layer_kind != 0 && layer_kind != 1) || (split != 0 && split != 1)) {
+    set_error("vit_plan_attention_units: plan must not be NULL and layer_kind, split must be 0 or 1");
+    return VIT_E_ARG;
+  }
+  const AttnLists& L = layer_kind ? plan->win : plan->full;
+  const bool s = split && L.n_merge > 0;
+  const int32_t n = s ? L.n_long_split : L.n_long;
+  if (n_units) *n_units = n;
+  if (n_merge) *n_merge = s ? L.n_merge : 0;
+  if (n_parts) *n_parts = s ? L.n_parts : 0;
+  if (units && n > 0)
+    std::memcpy(units, plan->meta.data() + (s ? L.off_long_split : L.off_long), (size_t)n * sizeof(AttnWork));
   return VIT_OK;
 }
 

@@ -138,9 +138,26 @@ __device__ __forceinline__ int key_at(int p) {
   return p < 32 ? (p & 0x13) | ((p & 4) << 1) | ((p & 8) >> 1) : p;
 }
 
+// Four consecutive output columns of one row, in the blocked GEMM layout (the out-projection's
+// A operand): the rounded values, plus what their bf16 rounding leaves out when the
+// out-projection compensates it (hi+lo rows or an e4m3 residual).  (The attention kernel's own
+// epilogue writes the same forms inline.)
+template <bool F16>
+__device__ __forceinline__ void store_o4(const AttnArgs& a, int64_t orow, int col, float y0, float y1, float y2,
+                                         float y3) {
+  const int hid = a.heads * a.head_dim;
+  const int ld = a.o_split ? 2 * hid : hid;
+  *reinterpret_cast<uint2*>(a.o + kt_index(orow, col, ld)) = make_uint2(pack16<F16>(y0, y1), pack16<F16>(y2, y3));
+  if (F16) return;   // float16 output needs no compensation
+  if (a.o_split)
+    *reinterpret_cast<uint2*>(a.o + kt_index(orow, hid + col, ld)) =
+        make_uint2(pack_bf16(bf16_rest(y0), bf16_rest(y1)), pack_bf16(bf16_rest(y2), bf16_rest(y3)));
+  if (a.o8) *reinterpret_cast<uint32_t*>(a.o8 + kt8_index(orow, col, hid)) = rest_e4m3x4(y0, y1, y2, y3);
+}
+
 // DYN: the work-list length comes from device memory at run time (bucketed graphs); a separate
 // instantiation, so the plain path keeps it a launch constant.
-template <int HD, int NW, bool DYN, bool F16>
+template <int HD, int NW, bool DYN, bool F16, bool PART>
 __global__ void __launch_bounds__(NW * 64, 2)
 attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int32_t* __restrict__ n_work_dev) {
   constexpr int NCH = HD / 16;               // 16-wide reduction chunks of S^T = K Q^T
@@ -229,7 +246,11 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
 #pragma unroll
       for (int e = 0; e < 16; ++e) O[t][dt][e] = 0.f;
   }
-  const int nkb = (n + KB - 1) / KB;
+  // keys of this unit: with PART, blocks [kb0, kb1) of the segment (rows kseg..), kn of them
+  // valid; the loop below runs over the unit's blocks 0.. either way
+  const int kseg = PART ? seg0 + wk.kb0 * KB : seg0;
+  const int kn = PART ? min(n, wk.kb1 * KB) - wk.kb0 * KB : n;
+  const int nkb = (kn + KB - 1) / KB;
 
   // Direct global -> LDS tile loads through buffer resources over this head's K and V^T:
   // each lane keeps one 32-bit offset per load and the block's key offset rides in the
@@ -260,7 +281,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
     voff[j] = dd < HD ? (uint32_t)(dd * a.vt_ld + 8 * c) * 2 : 0u;
   }
   auto dload = [&](int kb, uint16_t* dK, uint32_t* dV) {
-    const uint32_t key0 = (uint32_t)(seg0 + kb * KB);
+    const uint32_t key0 = (uint32_t)(kseg + kb * KB);
 #pragma unroll
     for (int j = 0; j < KLW; ++j) {
       const int i = wv + j * NW;
@@ -299,10 +320,10 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
       __builtin_amdgcn_s_setprio(0);
       // ---- mask keys past the segment end (last step only); lane's keys are 8g + 4h + e
       const int key_base = kb * KB;
-      if (key_base + KB > n) {
+      if (key_base + KB > kn) {
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (key_base + key_at(8 * (e / 4) + 4 * h + (e % 4)) >= n)
+          if (key_base + key_at(8 * (e / 4) + 4 * h + (e % 4)) >= kn)
 #pragma unroll
             for (int t = 0; t < QT; ++t) S[t][e] = -INFINITY;
       }
@@ -388,6 +409,27 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
   }
 
   if (qbase >= n) return;
+  if (PART && wk.part >= 0) {
+    // part of the query block's keys: the unnormalised output, the running offset and the
+    // denominator go to the partial slot (rows of 256 queries, coalesced over the lanes)
+    float* pb = a.part + ((int64_t)head * a.n_parts + wk.part) * (HD + 2) * 256;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int q = qbase + 32 * t + l32;
+      if (q >= n) continue;
+      const int qr = q - wk.q0;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int d = 32 * dt + 8 * (e / 4) + 4 * h + (e % 4);
+          if (d < HD) pb[d * 256 + qr] = O[t][dt][e];
+        }
+      if (h == LHALF) pb[(HD + 1) * 256 + qr] = O[t][DT - 1][LIDX];
+      if (h == 0) pb[HD * 256 + qr] = m[t];
+    }
+    return;
+  }
   const int hid = a.heads * HD;
   const int ld = a.o_split ? 2 * hid : hid;
 #pragma unroll
@@ -426,19 +468,58 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
 
 template <int HD, bool F16>
 hipError_t run_hd(const AttnArgs& a, hipStream_t st) {
+  // key-split lists (partial slots given) take the PART instantiation; bucketed graphs (DYN)
+  // run plain lists only
   if (a.n_long > 0 && a.n_long_dev)
-    hipLaunchKernelGGL((attn_kernel<HD, 4, true, F16>), dim3(a.n_long * a.heads), dim3(256), 0, st, a,
+    hipLaunchKernelGGL((attn_kernel<HD, 4, true, F16, false>), dim3(a.n_long * a.heads), dim3(256), 0, st, a,
                        a.work_long, a.n_long, a.n_long_dev);
+  else if (a.n_long > 0 && a.part)
+    hipLaunchKernelGGL((attn_kernel<HD, 4, false, F16, true>), dim3(a.n_long * a.heads), dim3(256), 0, st, a,
+                       a.work_long, a.n_long, nullptr);
   else if (a.n_long > 0)
-    hipLaunchKernelGGL((attn_kernel<HD, 4, false, F16>), dim3(a.n_long * a.heads), dim3(256), 0, st, a,
+    hipLaunchKernelGGL((attn_kernel<HD, 4, false, F16, false>), dim3(a.n_long * a.heads), dim3(256), 0, st, a,
                        a.work_long, a.n_long, nullptr);
   if (a.n_short > 0 && a.n_short_dev)
-    hipLaunchKernelGGL((attn_kernel<HD, 1, true, F16>), dim3(a.n_short * a.heads), dim3(64), 0, st, a,
+    hipLaunchKernelGGL((attn_kernel<HD, 1, true, F16, false>), dim3(a.n_short * a.heads), dim3(64), 0, st, a,
                        a.work_short, a.n_short, a.n_short_dev);
   else if (a.n_short > 0)
-    hipLaunchKernelGGL((attn_kernel<HD, 1, false, F16>), dim3(a.n_short * a.heads), dim3(64), 0, st, a,
+    hipLaunchKernelGGL((attn_kernel<HD, 1, false, F16, false>), dim3(a.n_short * a.heads), dim3(64), 0, st, a,
                        a.work_short, a.n_short, nullptr);
   return hipGetLastError();
+}
+
+// Merge of key-split units: workgroup = (merge, head, 16 head dims), thread = query of the
+// merge's 256-query block.  With the parts' running offsets m_p (log2 units) and M = max m_p,
+// the output is sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p -- the rescale the attention
+// kernel applies between key blocks, applied between parts.
+template <int HD, bool F16>
+__global__ void __launch_bounds__(256)
+attn_merge_kernel(AttnArgs a, const AttnMerge* __restrict__ merges) {
+  constexpr int DG = HD / 16;          // groups of 16 head dims
+  constexpr int PS = (HD + 2) * 256;   // floats per partial slot
+  const int dg = blockIdx.x % DG, head = (blockIdx.x / DG) % a.heads;
+  const AttnMerge mg = merges[blockIdx.x / DG / a.heads];
+  const int qr = threadIdx.x, q = mg.q0 + qr;
+  if (q >= mg.seg_len) return;
+  const float* pb = a.part + ((int64_t)head * a.n_parts + mg.part0) * PS + qr;
+  const int np = mg.n_parts;
+  float mx = -INFINITY;
+  for (int p = 0; p < np; ++p) mx = fmaxf(mx, pb[p * PS + HD * 256]);
+  float l = 0.f, y[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) y[j] = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float* pp = pb + p * PS;
+    const float w = __builtin_amdgcn_exp2f(pp[HD * 256] - mx);
+    l += w * pp[(HD + 1) * 256];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) y[j] += w * pp[(16 * dg + j) * 256];
+  }
+  const float inv = 1.0f / l;
+  const int64_t orow = mg.seg_start + q;
+#pragma unroll
+  for (int j = 0; j < 16; j += 4)
+    store_o4<F16>(a, orow, head * HD + 16 * dg + j, y[j] * inv, y[j + 1] * inv, y[j + 2] * inv, y[j + 3] * inv);
 }
 
 // Zeroes V^T columns [n, n + 64) (clipped to the pitch) of every row: the attention's tile
@@ -463,6 +544,43 @@ vit_status launch_vt_pad_zero(uint16_t* vt, int rows, int64_t n_tok, int64_t vt_
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("V^T pad clear: %s", hipGetErrorString(e));
+    return VIT_E_HIP;
+  }
+  return VIT_OK;
+}
+
+vit_status launch_attention_merge(const AttnArgs& a, const AttnMerge* merge, int n_merge, void* stream) {
+  if (n_merge <= 0) return VIT_OK;
+  if (!a.part || a.n_parts <= 0 || !merge) {
+    set_error("attention merge: no partial slots");
+    return VIT_E_ARG;
+  }
+  if (a.f16 && (a.o_split || a.o8)) {
+    set_error("attention merge: float16 output takes no compensation");
+    return VIT_E_ARG;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(n_merge * a.heads * (a.head_dim / 16)));
+  switch (a.head_dim) {
+    case 32:
+      if (a.f16) hipLaunchKernelGGL((attn_merge_kernel<32, true>), grid, dim3(256), 0, st, a, merge);
+      else hipLaunchKernelGGL((attn_merge_kernel<32, false>), grid, dim3(256), 0, st, a, merge);
+      break;
+    case 64:
+      if (a.f16) hipLaunchKernelGGL((attn_merge_kernel<64, true>), grid, dim3(256), 0, st, a, merge);
+      else hipLaunchKernelGGL((attn_merge_kernel<64, false>), grid, dim3(256), 0, st, a, merge);
+      break;
+    case 80:
+      if (a.f16) hipLaunchKernelGGL((attn_merge_kernel<80, true>), grid, dim3(256), 0, st, a, merge);
+      else hipLaunchKernelGGL((attn_merge_kernel<80, false>), grid, dim3(256), 0, st, a, merge);
+      break;
+    default:
+      set_error("attention merge: head_dim %d not supported (32, 64, 80)", a.head_dim);
+      return VIT_E_ARG;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("attention merge launch: %s", hipGetErrorString(e));
     return VIT_E_HIP;
   }
   return VIT_OK;

@@ -13,6 +13,7 @@
 //    and shared by every layer (section 3.4), as attention work lists.
 #include <algorithm>
 #include <climits>
+#include <functional>
 #include <cmath>
 #include <cstring>
 
@@ -34,10 +35,66 @@ struct Seg {
   int32_t start, len;
 };
 
+// ---- key splits of the long units.  The 4-wave attention workgroups run two per CU and are
+// dispatched in work order, each XCD (workgroups go round-robin over 8 XCDs) taking a
+// contiguous range of (head, unit) pairs, head-major.  A list-scheduling model of that
+// dispatch (a unit costs its key blocks plus a fixed overhead) finds the unit that finishes
+// last; while the modelled makespan exceeds the mean load per slot by more than 3%, that unit
+// is split into two halves of its key range (no part below kMinPartBlocks blocks), and the
+// list is kept largest-first.  The best list found is kept only if its makespan plus the
+// merge pass's modelled cost is at least 3% below the unsplit makespan.  (Units of time: one
+// key block of one 4-wave workgroup, ~1.4 us on MI355X with two workgroups per CU; the merge
+// moves (head_dim + 2) x 1 KB per partial slot and head, at a few TB/s, plus a launch.)
+constexpr int kAttnQB = 256;            // queries per long unit
+constexpr int kAttnKB = 32;             // keys per block
+constexpr int kMinPartBlocks = 16;
+constexpr double kUnitOverhead = 4.0;   // key blocks' worth of per-unit work (query load, output)
+constexpr double kPartOverhead = 2.0;   // extra for a part (its partial store)
+constexpr double kMergeFixed = 3.0;     // merge launch
+constexpr double kMergePerSlot = 0.015; // merge traffic per partial slot and head
+
+struct SimUnit {
+  AttnWork w;
+  bool part;
+};
+
+double unit_cost(const SimUnit& u) {
+  return (u.w.kb1 - u.w.kb0) + kUnitOverhead + (u.part ? kPartOverhead : 0.0);
+}
+
+// Modelled makespan and mean slot load of `L` (all heads); *last = the list entry whose
+// instance finishes last.
+void simulate(const std::vector<SimUnit>& L, int heads, int slots, double* makespan, double* mean, int* last) {
+  const int64_t n = (int64_t)L.size(), G = n * heads;
+  const int64_t per = G >> 3, rem = G & 7;
+  double total = 0.0;
+  *makespan = 0.0;
+  *last = -1;
+  std::vector<double> heap;
+  for (int64_t x = 0; x < 8; ++x) {
+    const int64_t start = x * per + std::min(x, rem), cnt = per + (x < rem ? 1 : 0);
+    heap.assign((size_t)slots, 0.0);
+    for (int64_t l = start; l < start + cnt; ++l) {
+      const int e = (int)(l % n);
+      const double c = unit_cost(L[e]);
+      std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
+      const double t = heap.back() + c;
+      heap.back() = t;
+      std::push_heap(heap.begin(), heap.end(), std::greater<double>());
+      total += c;
+      if (t > *makespan) {
+        *makespan = t;
+        *last = e;
+      }
+    }
+  }
+  *mean = total / (8.0 * slots);
+}
+
 // Long segments go to 4-wave workgroups of 256 queries, short ones to 1-wave
 // workgroups of 64 queries; long units are ordered largest segment first.
 void build_lists(const std::vector<Seg>& segs, std::vector<uint8_t>& blob, AttnLists& out,
-                 int32_t& max_len) {
+                 int32_t& max_len, int heads, int n_cu) {
   std::vector<AttnWork> lw, sw;
   out.sq_long = out.sq_short = 0.0;
   std::vector<Seg> order(segs);
@@ -46,11 +103,12 @@ void build_lists(const std::vector<Seg>& segs, std::vector<uint8_t>& blob, AttnL
   max_len = 0;
   for (const Seg& s : order) {
     max_len = std::max(max_len, s.len);
+    const int32_t nkb = (s.len + kAttnKB - 1) / kAttnKB;
     if (s.len > 128) {
-      for (int32_t q0 = 0; q0 < s.len; q0 += 256) lw.push_back({s.start, s.len, q0, 0});
+      for (int32_t q0 = 0; q0 < s.len; q0 += kAttnQB) lw.push_back({s.start, s.len, q0, 0, nkb, -1, {0, 0}});
       out.sq_long += (double)s.len * s.len;
     } else {
-      for (int32_t q0 = 0; q0 < s.len; q0 += 64) sw.push_back({s.start, s.len, q0, 0});
+      for (int32_t q0 = 0; q0 < s.len; q0 += 64) sw.push_back({s.start, s.len, q0, 0, nkb, -1, {0, 0}});
       out.sq_short += (double)s.len * s.len;
     }
   }
@@ -58,6 +116,69 @@ void build_lists(const std::vector<Seg>& segs, std::vector<uint8_t>& blob, AttnL
   out.n_short = (int32_t)sw.size();
   out.off_long = put(blob, lw);
   out.off_short = put(blob, sw);
+
+  // key splits
+  out.n_long_split = out.n_merge = out.n_parts = 0;
+  if (lw.empty() || heads <= 0) return;
+  const int slots = std::max(1, n_cu / 8) * 2;
+  std::vector<SimUnit> L;
+  for (const AttnWork& w : lw) L.push_back({w, false});
+  double ms0, mean, ms;
+  int last;
+  simulate(L, heads, slots, &ms0, &mean, &last);
+  auto merge_cost = [&](const std::vector<SimUnit>& v) {
+    int parts = 0;
+    for (const SimUnit& u : v) parts += u.part ? 1 : 0;
+    return parts ? kMergeFixed + kMergePerSlot * parts * heads : 0.0;
+  };
+  std::vector<SimUnit> best = L;
+  double best_t = ms0;
+  ms = ms0;
+  for (int it = 0; it < 128 && ms > 1.03 * mean && last >= 0; ++it) {
+    const SimUnit u = L[last];
+    const int32_t nb = u.w.kb1 - u.w.kb0;
+    if (nb < 2 * kMinPartBlocks) break;
+    int32_t parts_of_block = 0;   // parts this query block would have after the split
+    for (const SimUnit& v : L)
+      if (v.w.seg_start == u.w.seg_start && v.w.q0 == u.w.q0) ++parts_of_block;
+    if (parts_of_block + 1 > kAttnMaxParts) break;
+    const int32_t mid = u.w.kb0 + nb / 2;
+    SimUnit lo = u, hi = u;
+    lo.w.kb1 = mid;
+    hi.w.kb0 = mid;
+    lo.part = hi.part = true;
+    L.erase(L.begin() + last);
+    L.push_back(lo);
+    L.push_back(hi);
+    std::stable_sort(L.begin(), L.end(),
+                     [](const SimUnit& a, const SimUnit& b) { return unit_cost(a) > unit_cost(b); });
+    simulate(L, heads, slots, &ms, &mean, &last);
+    const double t = ms + merge_cost(L);
+    if (t < best_t) {
+      best_t = t;
+      best = L;
+    }
+  }
+  if (best_t > 0.97 * ms0) return;   // not worth a merge pass
+
+  // partial slots: the parts of one query block get consecutive slots, in key order
+  std::vector<AttnWork> split;
+  std::vector<AttnMerge> merges;
+  for (const SimUnit& u : best) split.push_back(u.w);
+  for (size_t i = 0; i < split.size(); ++i) {
+    AttnWork& w = split[i];
+    if (!best[i].part || w.part >= 0) continue;
+    std::vector<size_t> members;
+    for (size_t j = 0; j < split.size(); ++j)
+      if (best[j].part && split[j].seg_start == w.seg_start && split[j].q0 == w.q0) members.push_back(j);
+    std::sort(members.begin(), members.end(), [&](size_t a, size_t b) { return split[a].kb0 < split[b].kb0; });
+    merges.push_back({w.seg_start, w.seg_len, w.q0, out.n_parts, (int32_t)members.size(), {0, 0, 0}});
+    for (size_t j : members) split[j].part = out.n_parts++;
+  }
+  out.n_long_split = (int32_t)split.size();
+  out.n_merge = (int32_t)merges.size();
+  out.off_long_split = put(blob, split);
+  out.off_merge = put(blob, merges);
 }
 
 }  // namespace
@@ -223,8 +344,9 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   p->off_unitdst = put(blob, unitdst);
   p->off_cos = put(blob, cs);
   p->off_sin = put(blob, sn);
-  build_lists(item_segs, blob, p->full, p->max_seg_full);
-  if (wu > 0) build_lists(win_segs, blob, p->win, p->max_seg_win);
+  const int n_cu = ctx->n_cu > 0 ? ctx->n_cu : 256;
+  build_lists(item_segs, blob, p->full, p->max_seg_full, c.heads, n_cu);
+  if (wu > 0) build_lists(win_segs, blob, p->win, p->max_seg_win, c.heads, n_cu);
   blob.resize(round_up((int64_t)blob.size(), 256));
   RunDims dims{};
   dims.n_rows = (int32_t)n_rows;
@@ -266,6 +388,8 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
     p->off_f8 = take((size_t)std::max(N32 * p->mlp_pad, U32 * 4 * d));
     p->off_o8 = take((size_t)N32 * d);
   }
+  const int32_t n_parts = std::max(p->full.n_parts, p->win.n_parts);
+  p->off_part = n_parts > 0 ? take((size_t)c.heads * n_parts * (p->head_dim + 2) * kAttnQB * 4) : 0;
   p->off_pix = take(px);
   p->off_out = take((size_t)p->n_units * c.out_dim * 4);
   p->ws_bytes = off;

@@ -79,20 +79,44 @@ struct UnitDesc {
 static_assert(sizeof(UnitDesc) == 16, "UnitDesc layout");
 
 // One attention work unit: a block of queries of one segment (all heads via grid.y).
+// It runs its queries against key blocks [kb0, kb1) of the segment (32 keys per block).  With
+// part >= 0 the unit covers only part of the segment's keys and leaves its unnormalised
+// output, running offset and softmax denominator in partial slot `part`, for the merge
+// kernel; with part == -1 it covers all keys and writes the output itself.
 struct AttnWork {
   int32_t seg_start;  // first internal row of the segment
   int32_t seg_len;    // rows in the segment
   int32_t q0;         // first query (relative to seg_start) of this unit
-  int32_t pad;
+  int32_t kb0, kb1;   // key blocks of the unit
+  int32_t part;       // partial slot, or -1
+  int32_t pad[2];
 };
-static_assert(sizeof(AttnWork) == 16, "AttnWork layout");
+static_assert(sizeof(AttnWork) == 32, "AttnWork layout");
 
-// Work lists for one kind of attention layer (item segments or windows).
+// One merge of the partial units of a query block: partial slots [part0, part0 + n_parts).
+struct AttnMerge {
+  int32_t seg_start, seg_len, q0;
+  int32_t part0, n_parts;
+  int32_t pad[3];
+};
+static_assert(sizeof(AttnMerge) == 32, "AttnMerge layout");
+constexpr int kAttnMaxParts = 16;   // parts of one query block at most
+
+// Work lists for one kind of attention layer (item segments or windows).  The plain long list
+// has one unit per 256-query block; the split list (used when n_merge > 0, by the eager
+// forward and whole-forward graphs; bucketed graphs use the plain list) has the key-split
+// units the planner chose to balance the launch's tail, and n_merge merges over n_parts
+// partial slots.
 struct AttnLists {
   int64_t off_long = 0;   // byte offset in the metadata blob
   int32_t n_long = 0;     // units of 256 queries (4-wave workgroups)
   int64_t off_short = 0;
   int32_t n_short = 0;    // units of 64 queries (1-wave workgroups)
+  int64_t off_long_split = 0;
+  int32_t n_long_split = 0;
+  int64_t off_merge = 0;
+  int32_t n_merge = 0;
+  int32_t n_parts = 0;
   double sq_long = 0.0;   // sum of segment_length^2 over segments in each list
   double sq_short = 0.0;
 };
@@ -169,6 +193,7 @@ struct vit_ctx {
   std::map<std::string, vitmi::HostTensor> host;
   bool finalized = false;
   int device = -1;
+  int n_cu = 0;          // compute units of the device (set at finalize; the planner assumes 256 before)
   vitmi::DeviceWeights w;
   bool is_full_layer(int l) const;
 };
@@ -199,6 +224,7 @@ struct vit_plan {
   size_t off_x = 0, off_r = 0, off_h = 0, off_q = 0, off_k = 0, off_vt = 0, off_o = 0, off_f = 0;
   size_t off_h8 = 0, off_f8 = 0;  // e4m3 residuals of H and F (VIT_ACT_BF16F8)
   size_t off_o8 = 0;              // e4m3 residual of the attention output O (VIT_ACT_BF16F8)
+  size_t off_part = 0;            // partial slots of key-split attention units
   size_t off_pix = 0, off_out = 0, ws_bytes = 0;
   int64_t vt_ld = 0;              // V^T row pitch (tokens), N rounded up to 8
 };
@@ -323,8 +349,14 @@ struct AttnArgs {
   const AttnWork* work_short = nullptr; int n_short = 0;
   // if set: list lengths read at run time (n_long / n_short above are the capacities)
   const int32_t* n_long_dev = nullptr; const int32_t* n_short_dev = nullptr;
+  // partial slots of key-split units: [heads][n_parts][head_dim + 2][256] floats (rows: the
+  // unnormalised output dims, then the running offset m, then the denominator l; 256 queries)
+  float* part = nullptr; int n_parts = 0;
 };
 vit_status launch_attention(const AttnArgs& a, void* stream);
+// Combines the partial slots of each merge into the output (same layout and forms as the
+// attention output).
+vit_status launch_attention_merge(const AttnArgs& a, const AttnMerge* merge, int n_merge, void* stream);
 // Per-item partial sums of the pixel content key (pixel_hash.hip): items_dev[i] = {byte offset,
 // 64-bit word count}, sums_dev[2 i + j] = lane-j sum (zeroed here first).
 vit_status launch_pixel_hash(const uint8_t* pixels, const int64_t* items_dev, int n_items, int64_t max_words,

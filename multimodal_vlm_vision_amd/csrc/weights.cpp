@@ -406,6 +406,11 @@ vit_status finalize_weights(vit_ctx* ctx, void* stream) {
       set_error("hipGetDevice: %s", hipGetErrorString(e));
       return VIT_E_HIP;
     }
+    e = hipDeviceGetAttribute(&ctx->n_cu, hipDeviceAttributeMultiprocessorCount, ctx->device);
+    if (e != hipSuccess) {
+      set_error("hipDeviceGetAttribute(multiprocessor count): %s", hipGetErrorString(e));
+      return VIT_E_HIP;
+    }
     vit_status ps = prepare_gemm_kernels();
     if (ps != VIT_OK) return ps;
     void* arena = nullptr;

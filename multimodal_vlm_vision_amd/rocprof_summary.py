@@ -83,6 +83,8 @@ def classify(names):
             c = "normrows_u8"
         elif "rownorm" in nm:
             c = "rownorm"
+        elif "attn_merge_kernel" in nm:
+            c = "attention_merge"
         elif "attn_kernel" in nm:
             a = _targs(nm)
             c = "attention" if len(a) >= 2 and a[1] == "4" else "attention_short"

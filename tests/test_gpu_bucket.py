@@ -2,9 +2,11 @@
 capture for a capacity plan replays other batches of the same tower without
 re-capture.  Each replay is bit-identical to eager encoding of that batch
 (every kernel reads the batch sizes at run time; per-element arithmetic does
-not depend on the tile configuration, which the capacity fixes), and two of
-them -- one image and the video replayed alone -- are also compared with the
-oracle.  Also: a replay with leftovers of a larger batch in the workspace, a
+not depend on the tile configuration, which the capacity fixes) -- unless the
+eager forward of that batch runs key-split attention units (bucketed graphs run
+the plain unit lists), in which case the two are two summation orders of the
+same softmax and agree to the encoder tolerance.  Two of the replays -- one
+image and the video replayed alone -- are also compared with the oracle.  Also: a replay with leftovers of a larger batch in the workspace, a
 batch over capacity, and a plain graph that cannot take plans."""
 
 import numpy as np
@@ -71,7 +73,13 @@ def test_bucket_graph_replays_other_batches():
         plan, ref = _eager(tower, sub, out_dim)
         say(f"replay {name}: N={plan.n_patches}")
         got = replay(plan, sub)
-        assert np.array_equal(got, ref), f"{name}: bucket replay differs from eager"
+        split = any(plan.attention_units(win)[1] > 0 for win in (False, True))
+        if split:
+            say(f"  eager runs key-split units: max |replay - eager| = {np.abs(got - ref).max():.3e}")
+            assert_encoder_tolerance(got.astype(np.float64), ref.astype(np.float64),
+                                     what=f"bucket replay vs eager (key splits), {name}")
+        else:
+            assert np.array_equal(got, ref), f"{name}: bucket replay differs from eager"
         if name in oracle_items:
             want = O.forward_workload(wl, items=oracle_items[name])
             assert_encoder_tolerance(got.astype(np.float64), want, what=f"bucket replay, {name}")

@@ -160,6 +160,70 @@ def test_workspace_grows_with_batch(lib):
     assert sizes == sorted(sizes) and len(set(sizes)) == 4
 
 
+# ---- attention work units and the planner's key splits (pure host)
+
+def _check_units(plain, split, n_merge, n_parts):
+    """The split list covers exactly the plain list's query blocks: each block either as its
+    plain unit (partial slot -1) or as parts that tile its key blocks [0, nkb) in consecutive,
+    distinct partial slots, each part at least 16 key blocks."""
+    nkb = lambda L: (L + 31) // 32
+    blocks = {}
+    for u in plain:
+        assert u[3] == 0 and u[4] == nkb(u[1]) and u[5] == -1
+        blocks[(u[0], u[2])] = u
+    seen, slots, merged = set(), set(), 0
+    by_block = {}
+    for u in split:
+        key = (u[0], u[2])
+        assert key in blocks and u[1] == blocks[key][1]
+        by_block.setdefault(key, []).append(u)
+    assert set(by_block) == set(blocks)
+    for key, us in by_block.items():
+        if len(us) == 1 and us[0][5] == -1:
+            assert us[0][3] == 0 and us[0][4] == nkb(us[0][1])
+            continue
+        merged += 1
+        us = sorted(us, key=lambda u: u[3])
+        assert all(u[5] >= 0 for u in us)
+        assert us[0][3] == 0 and us[-1][4] == nkb(us[0][1])
+        assert all(a[4] == b[3] for a, b in zip(us, us[1:]))          # contiguous key ranges
+        assert all(u[4] - u[3] >= 16 for u in us)
+        sl = [u[5] for u in us]
+        assert sl == list(range(sl[0], sl[0] + len(sl)))               # consecutive slots in key order
+        assert not (set(sl) & slots) and all(0 <= x < n_parts for x in sl)
+        slots |= set(sl)
+    assert merged == n_merge and len(slots) == n_parts
+
+
+def test_attention_units_and_key_splits(lib):
+    # the 16-frame video (one 18,432-token segment): 72 query blocks per head, 2.25 rounds of
+    # the 512 two-per-CU slots -- the planner splits the tail's key ranges
+    t = B.VisionTower(tower_config(4), lib)
+    p = t.plan([[8, 36, 64]], [16])
+    plain, nm0, np0 = p.attention_units(split=False)
+    split, nm, npart = p.attention_units(split=True)
+    assert len(plain) == 72 and nm0 == 0 and np0 == 0
+    assert nm > 0 and len(split) > len(plain)
+    _check_units(plain, split, nm, npart)
+    # a single 8-block query block cannot be split (parts of at least 16 blocks)
+    small = t.plan([[1, 16, 16]], [1])
+    u, nm, npart = small.attention_units()
+    assert len(u) == 1 and nm == 0 and u[0][5] == -1
+    # the 8-image batch shape: whatever the planner chose is a valid cover
+    t3 = B.VisionTower(tower_config(3), lib)
+    g = np.array([[1, 82, 22], [1, 30, 34], [1, 30, 80], [1, 86, 62], [1, 18, 22], [1, 42, 50], [1, 66, 54],
+                  [1, 36, 28]], dtype=np.int32)
+    p3 = t3.plan(g, np.ones(8, dtype=np.int32))
+    _check_units(p3.attention_units(split=False)[0], *p3.attention_units(split=True))
+    # window layers (1-wave units) are never split
+    t5 = B.VisionTower(tower_config(5), lib)
+    p5 = t5.plan([[1, 48, 64], [4, 32, 32]], [1, 8])
+    w, nmw, _ = p5.attention_units(windows=True)
+    assert nmw == 0
+    with pytest.raises(B.VitError):
+        p5.attention_units(windows=2)
+
+
 # ---- premise of the two normalisation kernels (table vs one float32 fma per byte)
 
 def _round_fraction(q, mant_bits):

@@ -346,8 +346,8 @@ def measure_workload(index, steps, warmup, activations, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workload", type=int, default=WORKLOAD)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -358,7 +358,7 @@ def main():
     ap.add_argument("--no-cache", action="store_true", help="skip the embedding-cache measurement")
     ap.add_argument("--no-resize", action="store_true", help="skip the device-resize measurement")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the other workloads (448 px tower, 16-frame video, Qwen2.5-shaped batch)")
+                    help="skip the other workloads (tiny tower, 448 px tower, 16-frame video, Qwen2.5-shaped batch)")
     ap.add_argument("--cpu-items", default="all",
                     help="items of the batch the CPU oracle runs on: 'all' or a comma list of indices")
     ap.add_argument("--activations", default="f16", choices=["f16", "bf16f8", "bf16x2"],
@@ -483,7 +483,7 @@ def main():
         tower.close()
         torch.cuda.empty_cache()
         line["workloads"] = {}
-        for idx in (2, 4, 5):
+        for idx in (1, 2, 4, 5):
             line["workloads"][f"w{idx}"] = measure_workload(idx, args.steps, args.warmup, args.activations,
                                                             stream)
             torch.cuda.empty_cache()

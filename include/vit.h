@@ -343,8 +343,12 @@ void vit_cache_destroy(vit_cache* cache);
  * the device, copies the keys to the host and synchronises `stream` (the
  * hit/miss split is a host decision), copies cached items' rows from the
  * arena into `out`, encodes the remaining items as one batch (their pixels
- * gathered into the workspace), writes their rows into `out` (item order,
- * as vit_encode) and caches them.  Everything after the key read is
+ * gathered into the workspace; that batch runs no key-split attention units,
+ * so an item's cached rows do not depend on which items missed with it),
+ * writes their rows into `out` (item order, as vit_encode) and caches them.
+ * The rows equal vit_encode's for the same batch bit for bit when that
+ * batch's plan runs no key-split units (vit_plan_attention_units), and to
+ * rounding otherwise.  Everything after the key read is
  * asynchronous on `stream`; the arena must not be touched by other work
  * until it completes.  *n_hits (optional) receives the number of items
  * served from the cache.  pixels_u8 must be 16-byte aligned.  Errors as

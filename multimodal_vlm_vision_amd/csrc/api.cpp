@@ -472,6 +472,27 @@ vit_status check_plan_ws(const vit_ctx* ctx, const vit_plan* plan, const void* w
   return check_common(ctx, plan, ws, ws_bytes);
 }
 
+vit_status create_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t* n_frames, int32_t n_items,
+                       bool key_splits, vit_plan** out) {
+  if (!ctx || !out) {
+    set_error("ctx and out must not be NULL");
+    return VIT_E_ARG;
+  }
+  *out = nullptr;
+  vit_plan* p = new (std::nothrow) vit_plan();
+  if (!p) {
+    set_error("out of host memory");
+    return VIT_E_ARG;
+  }
+  vit_status s = build_plan(ctx, grid_thw, n_frames, n_items, p, key_splits);
+  if (s != VIT_OK) {
+    delete p;
+    return s;
+  }
+  *out = p;
+  return VIT_OK;
+}
+
 }  // namespace vitmi
 
 using namespace vitmi;
@@ -530,24 +551,9 @@ vit_status vit_finalize_weights(vit_ctx* ctx, void* stream) {
 
 vit_status vit_plan_create(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t* n_frames,
                            int32_t n_items, vit_plan** out) {
-  if (!ctx || !out) {
-    set_error("ctx and out must not be NULL");
-    return VIT_E_ARG;
-  }
-  *out = nullptr;
-  vit_plan* p = new (std::nothrow) vit_plan();
-  if (!p) {
-    set_error("out of host memory");
-    return VIT_E_ARG;
-  }
-  vit_status s = build_plan(ctx, grid_thw, n_frames, n_items, p);
-  if (s != VIT_OK) {
-    delete p;
-    return s;
-  }
-  *out = p;
-  return VIT_OK;
+  return create_plan(ctx, grid_thw, n_frames, n_items, true, out);
 }
+
 
 void vit_plan_destroy(vit_plan* plan) { delete plan; }
 

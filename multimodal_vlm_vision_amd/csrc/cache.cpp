@@ -249,9 +249,11 @@ vit_status vit_encode_cached(const vit_ctx* ctx, vit_cache* cache, const vit_pla
   if (n_hits) *n_hits = n - (int32_t)miss.size();
   if (miss.empty()) return VIT_OK;
 
-  // misses: one plan for them alone, pixels gathered into that plan's pixel region of ws
+  // misses: one plan for them alone, pixels gathered into that plan's pixel region of ws.  That
+  // plan runs no key-split attention units, so a cached item's rows do not depend on which
+  // other items missed with it, and every workspace region of the plan is at most the batch's.
   vit_plan* sub = nullptr;
-  VIT_TRY(vit_plan_create(ctx, mgrid.data(), mframes.data(), (int32_t)miss.size(), &sub));
+  VIT_TRY(vitmi::create_plan(ctx, mgrid.data(), mframes.data(), (int32_t)miss.size(), false, &sub));
   struct PlanGuard {
     vit_plan* p;
     ~PlanGuard() { vit_plan_destroy(p); }

@@ -184,7 +184,7 @@ void build_lists(const std::vector<Seg>& segs, std::vector<uint8_t>& blob, AttnL
 }  // namespace
 
 vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t* n_frames,
-                      int32_t n_items, vit_plan* p) {
+                      int32_t n_items, vit_plan* p, bool key_splits) {
   const vit_config& c = ctx->cfg;
   p->cfg = c;
   p->head_dim = ctx->head_dim;
@@ -345,8 +345,9 @@ vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t
   p->off_cos = put(blob, cs);
   p->off_sin = put(blob, sn);
   const int n_cu = ctx->n_cu > 0 ? ctx->n_cu : 256;
-  build_lists(item_segs, blob, p->full, p->max_seg_full, c.heads, n_cu);
-  if (wu > 0) build_lists(win_segs, blob, p->win, p->max_seg_win, c.heads, n_cu);
+  const int split_heads = key_splits ? c.heads : 0;   // 0: no key splits
+  build_lists(item_segs, blob, p->full, p->max_seg_full, split_heads, n_cu);
+  if (wu > 0) build_lists(win_segs, blob, p->win, p->max_seg_win, split_heads, n_cu);
   blob.resize(round_up((int64_t)blob.size(), 256));
   RunDims dims{};
   dims.n_rows = (int32_t)n_rows;

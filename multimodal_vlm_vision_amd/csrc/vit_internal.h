@@ -243,8 +243,13 @@ struct vit_graph {
 namespace vitmi {
 
 // Builds plan metadata and layout (pure host).  Returns VIT_OK or an error.
+// key_splits = false: the attention lists keep one unit per query block (no partial slots);
+// used for plans whose results are combined with other plans' (the embedding cache's misses).
 vit_status build_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t* n_frames,
-                      int32_t n_items, vit_plan* p);
+                      int32_t n_items, vit_plan* p, bool key_splits = true);
+// vit_plan_create with the key_splits choice above.
+vit_status create_plan(const vit_ctx* ctx, const int32_t* grid_thw, const int32_t* n_frames, int32_t n_items,
+                       bool key_splits, vit_plan** out);
 
 // Weight packing + upload (weights.cpp)
 vit_status finalize_weights(vit_ctx* ctx, void* stream);

@@ -89,7 +89,11 @@ def test_bucket_graph_replays_other_batches():
     torch.cuda.synchronize()
     n = cap.out_rows
     got = gws[out_off:out_off + n * out_dim * 4].view(torch.float32).reshape(n, out_dim).cpu().numpy()
-    assert np.array_equal(got, run.encode())
+    if any(cap.attention_units(win)[1] > 0 for win in (False, True)):
+        assert_encoder_tolerance(got.astype(np.float64), run.encode().astype(np.float64),
+                                 what="plain launch vs eager (key splits)")
+    else:
+        assert np.array_equal(got, run.encode())
 
     # over capacity: more patches than captured
     big = tower.plan(*_grid(items + items[:1]))

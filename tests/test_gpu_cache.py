@@ -3,7 +3,9 @@
 * the device pixel content keys equal the CPU oracle's (bit-exact);
 * a batch encoded through the cache equals plain encoding, bit for bit, on a
   cold cache (all misses), a warm one (all hits) and mixes of cached, changed
-  and repeated items;
+  and repeated items -- when the batch's plain encoding runs no key-split
+  attention units (the cache encodes its misses without them); otherwise the
+  two agree to the encoder tolerance (the same softmax summed in another order);
 * a small arena evicts first-in first-out and stays correct.
 """
 
@@ -19,7 +21,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_support import GpuRun  # noqa: E402
+from gpu_support import GpuRun, assert_encoder_tolerance  # noqa: E402
 from multimodal_vlm_vision_amd import EmbeddingCache  # noqa: E402
 
 
@@ -52,6 +54,15 @@ class Batch:
         return hits, self.out.cpu().numpy().copy()
 
 
+def same(got, ref, batch, what):
+    """Bit-identical unless the batch's plain encoding runs key-split units."""
+    if any(batch.plan.attention_units(w)[1] > 0 for w in (False, True)):
+        say(f"{what}: plain encoding runs key-split units, max diff {np.abs(got - ref).max():.3e}")
+        assert_encoder_tolerance(got.astype(np.float64), ref.astype(np.float64), what=what)
+    else:
+        assert np.array_equal(got, ref), what
+
+
 @pytest.fixture(scope="module")
 def run():
     return GpuRun(make_workload(3, layers=2))   # 8 images of mixed sizes, 2 layers
@@ -78,11 +89,13 @@ def test_cached_encode_equals_plain(run):
     ref = full.plain(t)
     say("cold cache")
     hits, got = full.cached(t, cache)
-    assert hits == 0 and np.array_equal(got, ref)
+    assert hits == 0
+    same(got, ref, full, "cold cache")
     assert cache.stats()[0] == len(items)
     say("warm cache")
     hits, got = full.cached(t, cache)
-    assert hits == len(items) and np.array_equal(got, ref)
+    assert hits == len(items)
+    same(got, ref, full, "warm cache")
 
     # cached items, one changed pixel (a different key), a repeat inside the batch
     changed = type(items[3])(items[3].frames.copy(), items[3].grid_thw)
@@ -92,7 +105,8 @@ def test_cached_encode_equals_plain(run):
     ref_mix = mb.plain(t)
     say("mixed batch")
     hits, got = mb.cached(t, cache)
-    assert hits == 4 and np.array_equal(got, ref_mix)
+    assert hits == 4
+    same(got, ref_mix, mb, "mixed batch")
     cache.close()
 
 
@@ -107,13 +121,14 @@ def test_small_arena_evicts_fifo(run):
     cache = EmbeddingCache(t, arena)
     say(f"small arena {arena_bytes} bytes")
     hits, got = full.cached(t, cache)
-    assert hits == 0 and np.array_equal(got, ref)
+    assert hits == 0
+    same(got, ref, full, "small arena, cold")
     n, used = cache.stats()
     assert 1 <= n < len(items) and used <= arena_bytes
     hits, got = full.cached(t, cache)
-    assert np.array_equal(got, ref)
+    same(got, ref, full, "small arena, again")
     # the last item inserted is still there
     last = Batch(t, items[-1:], od)
     h1, g1 = last.cached(t, cache)
-    assert np.array_equal(g1, last.plain(t))
+    same(g1, last.plain(t), last, "last item")
     cache.close()

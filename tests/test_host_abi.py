@@ -224,6 +224,30 @@ def test_attention_units_and_key_splits(lib):
         p5.attention_units(windows=2)
 
 
+def test_key_split_cover_on_random_batches(lib):
+    # random mixes of images and videos (seeded): every split list is an exact cover
+    rng = np.random.default_rng(11)
+    t = B.VisionTower(tower_config(4), lib)
+    splits = 0
+    for _ in range(60):
+        n = int(rng.integers(1, 9))
+        grid, frames = [], []
+        for _ in range(n):
+            if rng.random() < 0.3:
+                tt = int(rng.integers(1, 9))
+                grid.append([tt, 2 * int(rng.integers(4, 40)), 2 * int(rng.integers(4, 40))])
+                frames.append(2 * tt)
+            else:
+                grid.append([1, 2 * int(rng.integers(4, 60)), 2 * int(rng.integers(4, 60))])
+                frames.append(1)
+        p = t.plan(np.array(grid, dtype=np.int32), np.array(frames, dtype=np.int32))
+        plain = p.attention_units(split=False)[0]
+        split, nm, npart = p.attention_units(split=True)
+        _check_units(plain, split, nm, npart)
+        splits += nm > 0
+    assert splits > 0   # the planner split some of them
+
+
 # ---- premise of the two normalisation kernels (table vs one float32 fma per byte)
 
 def _round_fraction(q, mant_bits):

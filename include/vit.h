@@ -394,7 +394,7 @@ void vit_destroy(vit_ctx* ctx);
 typedef struct vit_kernel_stat {
   char    name[32];
   int32_t launches;
-  int32_t mfma_bound;   /* 1: judged against MFMA peak, 0: against HBM bandwidth */
+  int32_t mfma_bound;   /* 1: rated against the MFMA peak, 0: against HBM bandwidth */
   double  total_ms;     /* sum of hipEvent-measured launch durations */
   double  flops;
   double  bytes;

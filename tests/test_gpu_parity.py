@@ -363,6 +363,21 @@ def test_determinism_and_graph_replay_match_eager():
     g.close()
 
 
+def test_key_split_video_graph_replays_match_eager():
+    """The 16-frame video at 2 layers runs key-split attention units (parts of up to a quarter
+    of the segment's keys) and the merge pass: eager, repeated eager and three graph replays
+    (eager work between them) give the same bytes."""
+    wl = make_workload(4, layers=2)
+    run = GpuRun(wl)
+    _, n_merge, n_parts = run.plan.attention_units()
+    say(f"key-split video: {n_merge} merged query blocks over {n_parts} partial slots")
+    assert n_merge > 0
+    a = run.encode()
+    assert np.array_equal(run.encode(), a)
+    got = run.graph_encode(replays=3)
+    assert np.array_equal(got, a), "graph replay differs from eager"
+
+
 def test_graph_replay_matches_oracle_448px():
     """The captured whole-encoder graph (normalisation inside it, pixels written into its uint8
     input region) against the oracle, whole output of the 448 px 4-layer tower."""

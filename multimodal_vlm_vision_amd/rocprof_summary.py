@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 runs of bench.py, as the short markdown files kept under profiles/.
 
-    python -m multimodal_vlm_vision_amd.rocprof_summary trace   <dir> <out.md> "<command>"
+    python -m multimodal_vlm_vision_amd.rocprof_summary trace   <dir> <out.md> "<command>" [workload index]
     python -m multimodal_vlm_vision_amd.rocprof_summary traffic <fetch dir> <write dir> <out.md> "<commands>"
     python -m multimodal_vlm_vision_amd.rocprof_summary mfma    <dir> <out.md> "<command>"
 
@@ -9,7 +9,7 @@ recursively.  Every dispatch is assigned to a launch class of the forward from i
 template arguments and its position in the forward (the out-projection and fc2 share one
 kernel: the first residual product after a qkv launch is the out-projection); the class names
 are the ones bench.py and vit_encode_profiled use.  Algorithmic figures are those of the
-8-image headline batch (workloads.make_workload(3)).
+workload given (default: the 8-image headline batch, workloads.make_workload(3)).
 """
 
 from __future__ import annotations
@@ -119,20 +119,51 @@ def _dispatches(rows):
     return out
 
 
-def headline_algorithmic():
-    """Algorithmic MFMA FLOPs and HBM bytes per launch of each class on the headline batch."""
+def _window_lengths(items, window_units):
+    """Patch counts of the attention windows: per frame, square windows of window_units x
+    window_units merge units tiled from the top-left, truncated at the edges."""
+    out = []
+    for it in items:
+        t, h, w = it.grid_thw
+        uh, uw = h // 2, w // 2
+        for _ in range(t):
+            for wy in range(0, uh, window_units):
+                for wx in range(0, uw, window_units):
+                    out.append(4 * min(window_units, uh - wy) * min(window_units, uw - wx))
+    return out
+
+
+def headline_algorithmic(index: int = 3):
+    """Algorithmic MFMA FLOPs and HBM bytes per launch of each class on workload `index`
+    (3, the 8-image headline batch, by default).  Attention classes average over their
+    launches: 'attention' runs the long units (segments above 128 patches) of the item-segment
+    layers, 'attention_short' the short ones and, in windowed towers, the window layers."""
     sys.path.insert(0, ROOT)
     from workloads import make_workload
-    wl = make_workload(3, with_weights=False)
+    wl = make_workload(index, with_weights=False)
     c = wl.cfg
     N = wl.n_patches
     d, mlp, out, K = c.hidden, c.mlp_dim, c.out_dim, 1176
     U = N // 4
-    sq = float(sum(n * n for n in wl.seg_lengths))
+    segs = wl.seg_lengths
+    sq = float(sum(n * n for n in segs))
+    sq_long = float(sum(n * n for n in segs if n > 128))
+    sq_short = float(sum(n * n for n in segs if n <= 128))
+    if c.window_px:
+        n_full = len(c.full_attn_layers)
+        n_win = c.layers - n_full
+        sq_win = float(sum(n * n for n in _window_lengths(wl.items, c.window_px // 28)))
+        short_launches = n_win + (n_full if sq_short else 0)
+        attn_short = 4.0 * d * (n_win * sq_win + n_full * sq_short) / max(short_launches, 1)
+    else:
+        attn_short = 4.0 * d * sq_short
     b = 2   # float16 / bfloat16 operands
+    mlp_mult = 2 if c.mlp_kind == "swiglu" else 1
     flops = {"gemm_patch_embed": 2.0 * N * d * K, "gemm_qkv_rope": 2.0 * N * 3 * d * d,
-             "attention": 4.0 * d * sq, "gemm_proj_residual": 2.0 * N * d * d,
-             "gemm_fc1_gelu": 2.0 * N * d * mlp, "gemm_fc2_residual": 2.0 * N * mlp * d,
+             "attention": 4.0 * d * sq_long, "attention_short": attn_short,
+             "gemm_proj_residual": 2.0 * N * d * d,
+             "gemm_fc1_gelu": 2.0 * N * d * mlp, "gemm_gateup_swiglu": 2.0 * N * d * mlp * mlp_mult,
+             "gemm_fc2_residual": 2.0 * N * mlp * d,
              "gemm_merger_fc1_gelu": 2.0 * U * 16 * d * d, "gemm_merger_fc2": 2.0 * U * 4 * d * out}
     px = sum(it.frames.size for it in wl.items)
     # bytes: every operand read once, every output written once (residual products read and
@@ -160,7 +191,7 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def cmd_trace(directory, out_md, command):
+def cmd_trace(directory, out_md, command, index=3):
     disp = _dispatches(_rows(directory, "kernel_trace.csv"))
     classes = classify([d[1] for d in disp])
     by_name = defaultdict(list)
@@ -171,7 +202,7 @@ def cmd_trace(directory, out_md, command):
         by_class[c].append((e - s) / 1e3)
         cls_of_name[short_name(nm)].add(c)
     total = sum(sum(v) for v in by_name.values())
-    wl, flops, _, _ = headline_algorithmic()
+    wl, flops, _, _ = headline_algorithmic(index)
     lines = [f"# rocprofv3 kernel statistics -- vision tower forward, {wl.cfg.name}", "",
              f"Workload: {wl.cfg.name} (N = {wl.n_patches} patches, hidden {wl.cfg.hidden}, {wl.cfg.heads} heads of "
              f"{wl.cfg.head_dim}, MLP {wl.cfg.mlp_dim}, out {wl.cfg.out_dim}), float16 activations (bf16 patch "
@@ -315,7 +346,7 @@ def cmd_mfma(directory, out_md, command):
 
 def main(argv):
     if len(argv) >= 4 and argv[0] == "trace":
-        cmd_trace(argv[1], argv[2], argv[3])
+        cmd_trace(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) >= 5 else 3)
     elif len(argv) >= 5 and argv[0] == "traffic":
         cmd_traffic(argv[1], argv[2], argv[3], argv[4])
     elif len(argv) >= 4 and argv[0] == "mfma":

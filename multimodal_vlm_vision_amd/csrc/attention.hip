@@ -16,15 +16,15 @@
 //    max is 15 in-lane maxima and one permlane32 swap with the lane holding
 //    the other 16 keys.
 //  * O^T = V^T P^T: the lane's 16 probabilities are directly its B operands
-//    for the two 16-key reduction chunks (chunk c takes rows g = 2c, 2c + 1),
-//    provided V^T fragments list keys in the same order, which the V^T reads
-//    do (keys 16c + 4h + 0..3 and 16c + 8 + 4h + 0..3).  P never leaves
+//    for the two 16-key reduction chunks (chunk c takes rows g = 2c, 2c + 1);
+//    with K rows loaded in key_at order those are keys 16c + 8h + 0..7, so
+//    each V^T fragment is one 16-byte chunk of a V^T row.  P never leaves
 //    registers.
 //  * The softmax denominator comes from the padding of the last O^T row tile:
 //    row head_dim of the V^T tile holds ones (and the rows after it zeros), so
 //    O^T row head_dim accumulates sum_k P.
 // Online softmax in fp32 with exp2: q arrives scaled by log2(e)/sqrt(d) (the
-// qkv epilogue applies it before q is rounded to bf16), and every score MFMA
+// qkv epilogue applies it before q is rounded to 16 bits), and every score MFMA
 // chain starts from an accumulator tile holding -m (the query's running
 // offset), so the MFMAs return the exp2 argument s - m itself and the common
 // path spends no VALU op on it; P is rounded to the operand type for the MFMA.  The offset
@@ -48,7 +48,10 @@
 // 4-wave workgroups (256 queries share each K/V tile); short segments
 // (windows) use 1-wave workgroups of 64 queries.  The DYN instantiations read
 // the work-list length from device memory (bucketed graphs: the grid covers the
-// capacity and surplus workgroups leave at once).
+// capacity and surplus workgroups leave at once).  The PART instantiation runs
+// the planner's key-split lists: a unit may cover only a range of its query
+// block's key blocks, leaving its unnormalised output, running offset and
+// denominator in a partial slot that attn_merge_kernel combines.
 #include <hip/hip_runtime.h>
 
 #include <cmath>

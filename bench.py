@@ -127,6 +127,26 @@ def normpatch_stream(n_images=48, side=1344, reps=20):
     return res
 
 
+def pixels_upload(pixels_host, steps):
+    """Host -> device copy of the batch's uint8 pixels from pinned memory, the step before the
+    forward when frames arrive in host memory (reported beside the forward, never in it)."""
+    import torch
+    src = torch.from_numpy(pixels_host).pin_memory()
+    dst = torch.empty(src.numel(), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        dst.copy_(src, non_blocking=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"bytes": int(src.numel()), "ms": ms, "gbs": src.numel() / (ms * 1e-3) / 1e9}
+
+
 def resize_measure(wl, steps):
     """Device resize of the batch's images, each made off-grid by a seeded offset of up to 13
     pixels per side, back to the 28-pixel grid: one launch per image, all on one stream, timed
@@ -447,6 +467,9 @@ def main():
     }
     graph.close()
     roof["traffic"], roof["traffic_source"] = measured_traffic(dom)
+    line["pixels_h2d"] = pixels_upload(pack_pixels(wl.items), args.steps)
+    log(f"pixel upload (pinned host -> device): {line['pixels_h2d']['bytes'] / 1e6:.1f} MB, "
+        f"{line['pixels_h2d']['ms']:.3f} ms, {line['pixels_h2d']['gbs']:.1f} GB/s")
     if not args.no_resize:
         line["resize"] = resize_measure(wl, args.steps)
         r = line["resize"]

@@ -10,6 +10,7 @@ identical seeded inputs.
   workloads are compared whole, through the graph, in
   test_gpu_whole_output.py; here only the hi+lo form's smallest item);
 * a workspace full of stale NaN bytes never reaches the output;
+* key-split attention units on segments that end inside a key block, against the oracle;
 * isolation between items, run-to-run determinism, graph replay == eager,
   the uint8 flatten_patches entry point, and degenerate batches.
 """
@@ -376,6 +377,30 @@ def test_key_split_video_graph_replays_match_eager():
     assert np.array_equal(run.encode(), a)
     got = run.graph_encode(replays=3)
     assert np.array_equal(got, a), "graph replay differs from eager"
+
+
+def test_key_split_ragged_segments_match_oracle():
+    """Key-split units whose segments end inside a key block and inside a query block: one
+    1,804-patch image (57 key blocks, the last holding 12 keys; its last query block 12
+    queries) and a 2,100-patch image beside a 396-patch one, at 2 layers of the 1280-wide
+    tower.  The planner splits their query blocks' key ranges (few units for 512 slots), so
+    the partial units' masked last blocks and the merge pass run on ragged lengths; eager and
+    graph outputs against the oracle."""
+    cfg = tower_config(2).with_layers(2)
+    for sizes, seed in (([(1, 82 * 14, 22 * 14)], 53), ([(1, 42 * 14, 50 * 14), (1, 18 * 14, 22 * 14)], 59)):
+        wl = make_custom_workload(cfg, sizes, seed=seed)
+        run = GpuRun(wl)
+        units, n_merge, n_parts = run.plan.attention_units()
+        ragged = {int(u[1]) for u in units if u[5] >= 0 and u[1] % 32}
+        say(f"ragged key splits: segments {wl.seg_lengths}, {len(units)} units, {n_merge} merges, "
+            f"{n_parts} partial slots, ragged split segments {sorted(ragged)}")
+        assert n_merge > 0 and ragged, "the planner no longer splits these segments"
+        ref = O.forward_workload(wl)
+        assert_encoder_tolerance(run.encode(), ref, what=f"ragged key splits {wl.seg_lengths} (eager)")
+        assert_encoder_tolerance(run.graph_encode(replays=2), ref,
+                                 what=f"ragged key splits {wl.seg_lengths} (graph)")
+        del run
+        torch.cuda.empty_cache()
 
 
 def test_graph_replay_matches_oracle_448px():

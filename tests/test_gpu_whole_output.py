@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_support import GpuRun, assert_encoder_tolerance, per_item_errors, progress_log  # noqa: E402
+from gpu_support import GpuRun, assert_encoder_tolerance, per_item_errors, progress_log, rel_err  # noqa: E402
 
 
 def say(msg):
@@ -52,4 +52,6 @@ def test_whole_output_through_graph_matches_oracle(idx):
     say(f"workload {idx}: oracle (float32, {O._threads()} threads) {time.time() - t0:.1f} s")
     for i, (ma, mr) in enumerate(per_item_errors(got, ref, wl.items)):
         say(f"workload {idx} item {i} grid {wl.items[i].grid_thw}: max_abs={ma:.3e} mean_rel={mr:.3e}")
+    say(f"workload {idx} whole output: max_abs={float(np.abs(got - ref).max()):.3e} "
+        f"mean_rel={rel_err(got, ref):.3e}")
     assert_encoder_tolerance(got, ref, what=f"workload {idx} whole output (graph)")

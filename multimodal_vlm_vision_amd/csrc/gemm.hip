@@ -664,15 +664,29 @@ gemm_kernel(GemmArgs p) {
     lfrag((kt + 1) % S, 0, fa[0], fl[0], fb[0]);
     issue(kt + S, buf);
     mfma_step(fa[1], fl[1], fb[1]);
+    // Three fragment reads per MFMA, then one load per MFMA: the loads into LDS must follow
+    // every fragment read (see above), and spreading them one per MFMA keeps the vector memory
+    // queue from filling behind a burst, which would hold up the wave's next MFMAs.  Tiles with
+    // too few MFMAs for that take the reads and the loads each in one group.
+    {
+      constexpr int ND3 = (NDS + 2) / 3;
+      if constexpr (ND3 + G::LPW <= NMF) {
 #pragma unroll
-    for (int i = 0; i < NDS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+        for (int i = 0; i < ND3; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS read
+        }
 #pragma unroll
-    for (int i = 0; i < G::LPW; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (buffer load -> LDS)
+        for (int i = 0; i < G::LPW; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (buffer load -> LDS)
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, G::LPW, 0);
+      }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
     __builtin_amdgcn_sched_barrier(0);

@@ -3,6 +3,7 @@
     python -m multimodal_vlm_vision_amd.rocprof_summary trace   <dir> <out.md> "<command>" [workload index]
     python -m multimodal_vlm_vision_amd.rocprof_summary traffic <fetch dir> <write dir> <out.md> "<commands>"
     python -m multimodal_vlm_vision_amd.rocprof_summary mfma    <dir> <out.md> "<command>"
+    python -m multimodal_vlm_vision_amd.rocprof_summary counters <out.md> "<command>" <dir> [<dir> ...]
 
 <dir> is a rocprofv3 output directory (``--output-format csv``); the csv files are found
 recursively.  Every dispatch is assigned to a launch class of the forward from its kernel's
@@ -344,6 +345,91 @@ def cmd_mfma(directory, out_md, command):
         fh.write("\n".join(lines) + "\n")
 
 
+# (counter, divisor kind, column title): "simd" divides by the cycles x 1024 SIMDs, "cu" by the
+# cycles x 256 CUs, "cyc" by the cycles (an average over instances), "lds" by SQ_LDS_IDX_ACTIVE
+_PATH_COLUMNS = [
+    ("SQ_VALU_MFMA_BUSY_CYCLES", "simd", "MFMA busy"),
+    ("SQ_VALU_MFMA_COEXEC_CYCLES", "simd", "VALU beside MFMA"),
+    ("SQ_LDS_IDX_ACTIVE", "cu", "LDS active"),
+    ("SQ_LDS_BANK_CONFLICT", "lds", "LDS bank conflicts (of LDS active)"),
+    ("TA_BUSY_avr", "cyc", "TA busy"),
+    ("TD_TD_BUSY_sum", "cu", "TD busy"),
+    ("TCP_PENDING_STALL_CYCLES_sum", "cu", "L1 stalled on pending misses"),
+]
+
+
+def cmd_counters(out_md, command, dirs):
+    """Memory-path and issue counters per launch class, from one or more counter passes (each
+    pass carrying GRBM_GUI_ACTIVE for its clock), as fractions of the kernel's cycles."""
+    per = defaultdict(dict)      # (pass, dispatch) -> counter -> value
+    meta = {}
+    order = []
+    for i, d in enumerate(dirs):
+        rows = _rows(d, "counter_collection.csv")
+        m = {}
+        for r in rows:
+            did = int(_col(r, "Dispatch_Id", "Dispatch_ID"))
+            per[(i, did)][_col(r, "Counter_Name")] = float(_col(r, "Counter_Value"))
+            m[did] = (_col(r, "Kernel_Name"), int(_col(r, "Start_Timestamp")), int(_col(r, "End_Timestamp")))
+        dids = sorted(m, key=lambda x: (m[x][1], x))
+        for did, c in zip(dids, classify([m[x][0] for x in dids])):
+            meta[(i, did)] = (c, m[did][2] - m[did][1])
+            order.append((i, did))
+    classes = ["gemm_qkv_rope", "attention", "gemm_proj_residual", "gemm_fc1_gelu", "gemm_fc2_residual",
+               "rownorm"]
+
+    def avg(c, name):
+        vals, cyc, dur = [], [], []
+        for key in order:
+            if meta[key][0] != c or name not in per[key]:
+                continue
+            vals.append(per[key][name])
+            cyc.append(per[key].get("GRBM_GUI_ACTIVE", 0.0) / 8)
+            dur.append(meta[key][1])
+        if not vals:
+            return None
+        return sum(vals) / len(vals), sum(cyc) / len(cyc), sum(dur) / len(dur)
+
+    head = ["Launch class", "Duration (us)", "Clock (GHz)"] + [t for _, _, t in _PATH_COLUMNS] + \
+           ["L2 read latency (cycles)", "L1 <- L2 read bytes per CU and cycle"]
+    lines = ["# Issue and memory-path counters per launch class -- vision tower forward, qwen2vl-8img-mixed-32L", "",
+             "Counter passes over the bench's forwards, one rocprofv3 run per pass "
+             f"(kernel sources digest {kernel_sources_digest()}).  Commands (from the repository root on the "
+             "GPU host; <counters> is each pass's list below):", "", "```", command, "```", ""]
+    for i, d in enumerate(dirs):
+        names = sorted({n for k, v in per.items() if k[0] == i for n in v})
+        lines.append(f"* pass {i + 1}: {' '.join(names)}")
+    lines += ["", "Cycles are GRBM_GUI_ACTIVE / 8 (it reads as the sum over the 8 XCDs).  MFMA busy and VALU "
+              "beside MFMA are per SIMD (1024 SIMDs), LDS active, TD busy and the L1 stall per CU (256), TA busy "
+              "is already an average over the TA instances; the L2 read latency is TCP_TCC_READ_REQ_LATENCY_sum "
+              "/ TCP_TCC_READ_REQ_sum, and the read bytes count 128 bytes per L1 -> L2 read request.", "",
+              "| " + " | ".join(head) + " |", "|---|" + "---:|" * (len(head) - 1)]
+    for c in classes:
+        g = avg(c, "GRBM_GUI_ACTIVE")
+        if g is None:
+            continue
+        _, cyc, dur = g
+        cells = [c, f"{dur / 1e3:.1f}", f"{cyc / dur:.2f}"]
+        for name, kind, _ in _PATH_COLUMNS:
+            a = avg(c, name)
+            if a is None:
+                cells.append("--")
+                continue
+            v, cy, _ = a
+            if kind == "lds":
+                b = avg(c, "SQ_LDS_IDX_ACTIVE")
+                cells.append(f"{100 * v / b[0]:.0f}%" if b and b[0] else "--")
+            else:
+                div = {"simd": cy * 1024, "cu": cy * 256, "cyc": cy}[kind]
+                cells.append(f"{100 * v / div:.0f}%" if div else "--")
+        lat, req = avg(c, "TCP_TCC_READ_REQ_LATENCY_sum"), avg(c, "TCP_TCC_READ_REQ_sum")
+        cells.append(f"{lat[0] / req[0]:.0f}" if lat and req and req[0] else "--")
+        cells.append(f"{req[0] * 128 / (req[1] * 256):.1f}" if req and req[1] else "--")
+        lines.append("| " + " | ".join(cells) + " |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main(argv):
     if len(argv) >= 4 and argv[0] == "trace":
         cmd_trace(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) >= 5 else 3)
@@ -351,6 +437,8 @@ def main(argv):
         cmd_traffic(argv[1], argv[2], argv[3], argv[4])
     elif len(argv) >= 4 and argv[0] == "mfma":
         cmd_mfma(argv[1], argv[2], argv[3])
+    elif len(argv) >= 4 and argv[0] == "counters":
+        cmd_counters(argv[1], argv[2], argv[3:])
     else:
         print(__doc__)
         return 2

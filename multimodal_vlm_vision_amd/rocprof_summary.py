@@ -375,8 +375,9 @@ def cmd_counters(out_md, command, dirs):
         for did, c in zip(dids, classify([m[x][0] for x in dids])):
             meta[(i, did)] = (c, m[did][2] - m[did][1])
             order.append((i, did))
-    classes = ["gemm_qkv_rope", "attention", "gemm_proj_residual", "gemm_fc1_gelu", "gemm_fc2_residual",
-               "rownorm"]
+    # (the ~23 us row norm is left out: for launches that short GRBM_GUI_ACTIVE also counts the
+    # dispatch around the kernel and reads above the clock)
+    classes = ["gemm_qkv_rope", "attention", "gemm_proj_residual", "gemm_fc1_gelu", "gemm_fc2_residual"]
 
     def avg(c, name):
         vals, cyc, dur = [], [], []

@@ -227,7 +227,7 @@ def test_encoder_full_workload(idx, prec):
 @pytest.mark.parametrize("idx", [3, 5])
 def test_encoder_full_depth_sampled_items(idx, prec):
     """32-layer tower on the whole batch with hi+lo activation pairs; the oracle recomputes the
-    smallest item alone (the default bf16 + e4m3 form is compared on every item of these
+    smallest item alone (the default float16 form is compared on every item of these
     workloads, through the graph, in test_gpu_whole_output.py)."""
     run = get_run(idx, prec=prec)
     say(f"encoder workload {idx} N={run.n} (32 layers), oracle on the smallest item, activations {prec}")

@@ -4,6 +4,7 @@
     python -m multimodal_vlm_vision_amd.rocprof_summary traffic <fetch dir> <write dir> <out.md> "<commands>"
     python -m multimodal_vlm_vision_amd.rocprof_summary mfma    <dir> <out.md> "<command>"
     python -m multimodal_vlm_vision_amd.rocprof_summary counters <out.md> "<command>" <dir> [<dir> ...]
+    python -m multimodal_vlm_vision_amd.rocprof_summary stream  <trace dir> <fetch dir> <write dir> <out.md> "<commands>"
 
 <dir> is a rocprofv3 output directory (``--output-format csv``); the csv files are found
 recursively.  Every dispatch is assigned to a launch class of the forward from its kernel's
@@ -431,6 +432,64 @@ def cmd_counters(out_md, command, dirs):
         fh.write("\n".join(lines) + "\n")
 
 
+def cmd_stream(trace_dir, fetch_dir, write_dir, out_md, command, n_images=48, side=1344):
+    """normpatch on bench.py's streaming batch (n_images images of side x side pixels, one
+    frame each): the launches with the largest grid among the normpatch dispatches.  Achieved
+    bandwidth = algorithmic bytes (the uint8 pixels read once, the bf16 patch rows written
+    once) / average duration; traffic from FETCH_SIZE / WRITE_SIZE scaled by the 512 MiB
+    calibration copies."""
+    g = side // 14
+    n_patch = n_images * g * g
+    alg_read = n_images * side * side * 3
+    alg_write = n_patch * 1176 * 2
+
+    def stream_rows(rows, name_col="Kernel_Name"):
+        np_rows = [r for r in rows if "normpatch_kernel" in _col(r, name_col)]
+        if not np_rows:
+            raise RuntimeError("no normpatch dispatches")
+        big = max(int(_col(r, "Grid_Size", "Grid_Size_X")) for r in np_rows)
+        return [r for r in np_rows if int(_col(r, "Grid_Size", "Grid_Size_X")) == big], big
+
+    tr, grid = stream_rows(_rows(trace_dir, "kernel_trace.csv"))
+    durs = sorted(int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp")) for r in tr)
+    avg = sum(durs) / len(durs)
+    copy_bytes = 512 << 20
+
+    def counter_bytes(directory, counter):
+        rows = [r for r in _rows(directory, "counter_collection.csv") if _col(r, "Counter_Name") == counter]
+        cp = sorted((r for r in rows if "copy" in _col(r, "Kernel_Name").lower()),
+                    key=lambda r: (int(_col(r, "Start_Timestamp")), int(_col(r, "Dispatch_Id", "Dispatch_ID"))))[-3:]
+        if len(cp) < 3:
+            raise RuntimeError("no calibration copies found (run bench.py with --calibrate-copy)")
+        kib = sorted(float(_col(r, "Counter_Value")) for r in cp)[1]
+        fac = copy_bytes / (kib * 1024.0)
+        sr, _ = stream_rows(rows)
+        return sum(float(_col(r, "Counter_Value")) for r in sr) / len(sr) * 1024.0 * fac, fac, len(sr)
+
+    fb, ffac, nf = counter_bytes(fetch_dir, "FETCH_SIZE")
+    wb, wfac, nw = counter_bytes(write_dir, "WRITE_SIZE")
+    alg = alg_read + alg_write
+    gbs = alg / (avg * 1e-9) / 1e9
+    lines = [f"# normpatch on a streaming batch -- {n_images} images of {side} x {side} pixels", "",
+             f"The uint8 -> normalised bf16 patch-row kernel alone on bench.py's streaming batch ({n_patch} image "
+             f"patches, {alg / 1e9:.2f} GB of algorithmic traffic per launch, several times the 256 MB last-level "
+             "cache), inside the bench's normpatch_stream measurement (a zero-layer tower).  Commands (from the "
+             "repository root on the GPU host):", "", "```", command, "```", "",
+             f"Launches of the streaming batch: the {len(tr)} normpatch dispatches with the largest grid "
+             f"({grid} work-items) in the trace, {nf} and {nw} in the counter passes.  Algorithmic bytes per "
+             f"launch: {alg_read / 1e6:.1f} MB of pixels read (an image's one frame serves both temporal "
+             f"slots) + {alg_write / 1e6:.1f} MB of bf16 rows written (588 + 2352 bytes per image patch).", "",
+             "| Avg (us) | Min (us) | Max (us) | Achieved (GB/s) | Fraction of 8 TB/s | Fetched (MB) | Written (MB) "
+             "| Counter bytes / algorithmic |",
+             "|---:|---:|---:|---:|---:|---:|---:|---:|",
+             f"| {avg / 1e3:.1f} | {durs[0] / 1e3:.1f} | {durs[-1] / 1e3:.1f} | {gbs:.0f} | {gbs / 8000:.3f} | "
+             f"{fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / alg:.3f} |", "",
+             f"Counter calibration: FETCH_SIZE factor {ffac:.4f}, WRITE_SIZE factor {wfac:.4f} (512 MiB copy).  "
+             f"Kernel sources digest {kernel_sources_digest()}."]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main(argv):
     if len(argv) >= 4 and argv[0] == "trace":
         cmd_trace(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) >= 5 else 3)
@@ -440,6 +499,8 @@ def main(argv):
         cmd_mfma(argv[1], argv[2], argv[3])
     elif len(argv) >= 4 and argv[0] == "counters":
         cmd_counters(argv[1], argv[2], argv[3:])
+    elif len(argv) >= 6 and argv[0] == "stream":
+        cmd_stream(argv[1], argv[2], argv[3], argv[4], argv[5])
     else:
         print(__doc__)
         return 2

@@ -1,10 +1,8 @@
 """The rocprofv3 summarizer behind profiles/ (CPU only): launch classes from kernel names in
-dispatch order, and the derived columns of the counter tables on a small synthetic csv."""
+dispatch order, and the derived columns of the counter and streaming tables on small
+synthetic csv files."""
 
 import csv
-import os
-
-import pytest
 
 from multimodal_vlm_vision_amd import rocprof_summary as R
 
@@ -102,3 +100,44 @@ def test_kernel_digest_tracks_the_sources():
     d = R.kernel_sources_digest()
     assert len(d) == 16 and int(d, 16) >= 0
     assert R.kernel_sources_digest() == d
+
+
+def test_stream_table(tmp_path):
+    """normpatch streaming summary: the launches with the largest grid, bandwidth from the
+    algorithmic bytes, counter bytes scaled by the 512 MiB calibration copies."""
+    np_name = "void vitmi::(anonymous namespace)::normpatch_kernel<true>(vitmi::NormpatchArgs)"
+    cp_name = "__amd_rocclr_copyBuffer"
+    trace = tmp_path / "trace"
+    trace.mkdir()
+    cols = ["Dispatch_Id", "Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"]
+    with open(trace / "p_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(cols)
+        w.writerow([1, np_name, 4096, 0, 13_000])              # the forward's small launch: ignored
+        w.writerow([2, np_name, 1 << 20, 20_000, 220_000])     # 200 us
+        w.writerow([3, np_name, 1 << 20, 300_000, 520_000])    # 220 us
+    alg = 48 * 1344 * 1344 * 3 + 48 * 96 * 96 * 1176 * 2
+
+    def pmc(name, counter, kib_copy, kib_np):
+        d = tmp_path / name
+        d.mkdir()
+        rows = [(i, cp_name, "Grid_Size", counter, kib_copy, 10 * i, 10 * i + 5) for i in range(3)]
+        rows += [(9, np_name, "Grid_Size", counter, kib_np, 100, 200)]
+        with open(d / "p_counter_collection.csv", "w", newline="") as fh:
+            w = csv.writer(fh)
+            w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value",
+                        "Start_Timestamp", "End_Timestamp"])
+            for r in rows:
+                w.writerow([r[0], r[1], 1 << 20, r[3], r[4], r[5], r[6]])
+        return str(d)
+
+    f = pmc("fetch", "FETCH_SIZE", 262144, 150_000)   # factor 2
+    wr = pmc("write", "WRITE_SIZE", 524288, 1_000_000)  # factor 1
+    out = tmp_path / "s.md"
+    R.cmd_stream(str(trace), f, wr, str(out), "rocprofv3 ...")
+    row = [l for l in out.read_text().splitlines() if l.startswith("| 210.0 |")]
+    assert len(row) == 1
+    cells = [c.strip() for c in row[0].strip("|").split("|")]
+    assert cells[1] == "200.0" and cells[2] == "220.0"
+    assert cells[3] == f"{alg / 210e-6 / 1e9:.0f}"
+    assert cells[5] == f"{150_000 * 1024 * 2 / 1e6:.1f}" and cells[6] == f"{1_000_000 * 1024 / 1e6:.1f}"

@@ -11,6 +11,7 @@ identical seeded inputs.
   test_gpu_whole_output.py; here only the hi+lo form's smallest item);
 * a workspace full of stale NaN bytes never reaches the output;
 * key-split attention units on segments that end inside a key block, against the oracle;
+* a batch within 3% of the 2 GiB operand limit: its last items equal themselves encoded alone;
 * isolation between items, run-to-run determinism, graph replay == eager,
   the uint8 flatten_patches entry point, and degenerate batches.
 """
@@ -340,6 +341,41 @@ def test_isolation_between_items():
     u0, u1 = wl.items[0].n_patches // 4, wl.items[1].n_patches // 4
     assert np.array_equal(a[:u0], b[:u0]) and np.array_equal(a[u0 + u1:], b[u0 + u1:])
     assert not np.allclose(a[u0:u0 + u1], b[u0:u0 + u1])
+
+
+def test_batch_near_the_operand_limit_matches_its_items_alone():
+    """A batch whose largest operand (the MLP activation, N x 5120 float16) is within 3% of the
+    2 GiB that the kernels' 32-bit buffer offsets address: 50 images of 64 x 64 patches (204,800
+    patches), one layer of the 1280-wide tower.  Its last two items, encoded alone, give the same
+    bytes as their rows of the big batch (neither plan splits key ranges, and without splits an
+    item's output does not depend on its batch), so the addressing holds up to the largest
+    offsets a plan may reach; the last item alone is also checked against the oracle."""
+    cfg = tower_config(2).with_layers(1)
+    wl = make_custom_workload(cfg, [(1, 896, 896)] * 50, seed=67)
+    act = wl.n_patches * 5120 * 2
+    assert 0.97 * (1 << 31) < act < (1 << 31)
+    run = GpuRun(wl)
+    assert run.plan.attention_units()[1] == 0, "the big batch's plan splits key ranges"
+    say(f"near-limit batch: N={run.n}, MLP activation {act / 2**30:.3f} GiB")
+    run.tower.encode(run.plan, run.pixels, run.ws, run.out)
+    torch.cuda.synchronize()
+    last = wl.items[48:]
+    grid = np.asarray([it.grid_thw for it in last], dtype=np.int32)
+    frames = np.asarray([it.n_frames for it in last], dtype=np.int32)
+    plan2 = run.tower.plan(grid, frames)
+    assert plan2.attention_units()[1] == 0
+    px0 = sum(it.frames.size for it in wl.items[:48])
+    px2 = run.pixels[px0:].contiguous()
+    ws2 = torch.empty(plan2.ws_bytes, dtype=torch.uint8, device="cuda")
+    out2 = torch.empty(plan2.out_rows, cfg.out_dim, dtype=torch.float32, device="cuda")
+    run.tower.encode(plan2, px2, ws2, out2)
+    torch.cuda.synchronize()
+    r0 = sum(it.n_patches for it in wl.items[:48]) // 4
+    assert torch.equal(run.out[r0:r0 + plan2.out_rows], out2), "items differ between the big batch and alone"
+    ref = O.forward_workload(wl, items=[49], dtype=np.float32)
+    u = last[0].n_patches // 4
+    assert_encoder_tolerance(out2[u:].cpu().numpy().astype(np.float64), ref.astype(np.float64),
+                             what="near-limit batch, last item")
 
 
 def test_determinism_and_graph_replay_match_eager():

@@ -12,6 +12,7 @@ identical seeded inputs.
 * a workspace full of stale NaN bytes never reaches the output;
 * key-split attention units on segments that end inside a key block, against the oracle;
 * a batch within 3% of the 2 GiB operand limit: its last items equal themselves encoded alone;
+* segments on both sides of the 128-patch boundary between one- and four-wave attention units;
 * isolation between items, run-to-run determinism, graph replay == eager,
   the uint8 flatten_patches entry point, and degenerate batches.
 """
@@ -475,6 +476,23 @@ def test_stale_workspace_never_reaches_the_output(case):
     got = run.encode()
     assert np.all(np.isfinite(got)), f"{case}: non-finite output from a 0xFF workspace"
     assert_encoder_tolerance(got, O.forward_workload(wl), what=f"{case}, 0xFF workspace")
+
+
+def test_segments_around_the_short_long_threshold():
+    """Segments of up to 128 patches run on one-wave workgroups of 64 queries, longer ones on
+    four-wave workgroups of 256: items of 124, 128, 132, 252, 256 and 260 patches (and a 2-frame
+    clip of 2 x 64) on both sides of either boundary, 2 layers of the 1280-wide tower, against
+    the oracle."""
+    cfg = tower_config(2).with_layers(2)
+    sizes = [(1, 28, 868), (1, 112, 224), (1, 28, 924), (1, 196, 252), (1, 224, 224), (1, 28, 1820),
+             (4, 112, 112)]
+    wl = make_custom_workload(cfg, sizes, seed=73)
+    assert sorted(wl.seg_lengths) == [124, 128, 128, 132, 252, 256, 260]
+    run = GpuRun(wl)
+    units = run.plan.attention_units()[0]
+    say(f"short/long threshold: segments {wl.seg_lengths}, {len(units)} long units")
+    assert sorted({int(u[1]) for u in units}) == [132, 252, 256, 260]
+    assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="segments around 128 and 256")
 
 
 def test_patches_u8_entry_matches_frames_entry():

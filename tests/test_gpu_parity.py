@@ -13,6 +13,7 @@ identical seeded inputs.
 * key-split attention units on segments that end inside a key block, against the oracle;
 * a batch within 3% of the 2 GiB operand limit: its last items equal themselves encoded alone;
 * segments on both sides of the 128-patch boundary between one- and four-wave attention units;
+* extreme aspect ratios (2 x 2048 and 1024 x 4 patches);
 * isolation between items, run-to-run determinism, graph replay == eager,
   the uint8 flatten_patches entry point, and degenerate batches.
 """
@@ -493,6 +494,17 @@ def test_segments_around_the_short_long_threshold():
     say(f"short/long threshold: segments {wl.seg_lengths}, {len(units)} long units")
     assert sorted({int(u[1]) for u in units}) == [132, 252, 256, 260]
     assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="segments around 128 and 256")
+
+
+def test_extreme_aspect_ratios():
+    """A 28 x 28672-pixel strip (2 x 2048 patches) and a 14336 x 56-pixel one (1024 x 4): rotary
+    positions up to 2047 on one axis, an 86 KB pixel pitch, merge units along one row or one
+    column; 2 layers of the 1280-wide tower against the oracle."""
+    cfg = tower_config(2).with_layers(2)
+    wl = make_custom_workload(cfg, [(1, 28, 28672), (1, 14336, 56)], seed=79)
+    run = GpuRun(wl)
+    say(f"extreme aspect ratios: grids {[it.grid_thw for it in wl.items]}, N={run.n}")
+    assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="extreme aspect ratios")
 
 
 def test_patches_u8_entry_matches_frames_entry():

@@ -209,7 +209,7 @@ def cmd_trace(directory, out_md, command, index=3):
              f"Workload: {wl.cfg.name} (N = {wl.n_patches} patches, hidden {wl.cfg.hidden}, {wl.cfg.heads} heads of "
              f"{wl.cfg.head_dim}, MLP {wl.cfg.mlp_dim}, out {wl.cfg.out_dim}), float16 activations (bf16 patch "
              "embedding), whole forward replayed as a HIP graph plus eager and profiled eager forwards.", "",
-             "Command (from the repository root on the GPU host):", "", "```", command, "```", "",
+             "Command (from the repository root on an MI355X machine; <out> is any output directory):", "", "```", command, "```", "",
              "Per kernel (durations from the kernel trace):", "",
              "| Kernel | Launch class | Calls | Avg (µs) | Min (µs) | Max (µs) | % time |",
              "|---|---|---:|---:|---:|---:|---:|"]
@@ -270,7 +270,7 @@ def cmd_traffic(fetch_dir, write_dir, out_md, command):
     per_launch = {}
     lines = [f"# HBM traffic per launch -- vision tower forward, {wl.cfg.name}", "",
              "Two counter passes over the bench, each with a 512 MiB device-to-device copy (3 times, "
-             "`--calibrate-copy`) as the known-size reference.  Commands (from the repository root on the GPU host):",
+             "`--calibrate-copy`) as the known-size reference.  Commands (from the repository root on an MI355X machine; <out> is any output directory):",
              "", "```", command, "```", "",
              f"Calibration: the 512 MiB copy reads as FETCH_SIZE {f_kib:.0f} KiB (factor {f_fac:.4f}) and WRITE_SIZE "
              f"{w_kib:.0f} KiB (factor {w_fac:.4f}); every figure below is the counter's KiB per dispatch x 1024 x its "
@@ -316,7 +316,7 @@ def cmd_mfma(directory, out_md, command):
         acc[c].append(d)
     wl, flops, _, _ = headline_algorithmic()
     lines = [f"# MFMA hardware counters per launch class -- vision tower forward, {wl.cfg.name}", "",
-             "One counter pass over the bench's forwards.  Command (from the repository root on the GPU host):", "",
+             "One counter pass over the bench's forwards.  Command (from the repository root on an MI355X machine; <out> is any output directory):", "",
              "```", command, "```", "",
              "GRBM_GUI_ACTIVE reads as the sum over the 8 XCDs, so the clock column is GRBM_GUI_ACTIVE / 8 / duration "
              "and MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs) / (GRBM_GUI_ACTIVE / 8 x 1024).  "
@@ -396,8 +396,8 @@ def cmd_counters(out_md, command, dirs):
            ["L2 read latency (cycles)", "L1 <- L2 read bytes per CU and cycle"]
     lines = ["# Issue and memory-path counters per launch class -- vision tower forward, qwen2vl-8img-mixed-32L", "",
              "Counter passes over the bench's forwards, one rocprofv3 run per pass "
-             f"(kernel sources digest {kernel_sources_digest()}).  Commands (from the repository root on the "
-             "GPU host; <counters> is each pass's list below):", "", "```", command, "```", ""]
+             f"(kernel sources digest {kernel_sources_digest()}).  Commands (from the repository root on an MI355X machine; <out> is any output directory; "
+             "<counters> is each pass's list below):", "", "```", command, "```", ""]
     for i, d in enumerate(dirs):
         names = sorted({n for k, v in per.items() if k[0] == i for n in v})
         lines.append(f"* pass {i + 1}: {' '.join(names)}")
@@ -474,7 +474,7 @@ def cmd_stream(trace_dir, fetch_dir, write_dir, out_md, command, n_images=48, si
              f"The uint8 -> normalised bf16 patch-row kernel alone on bench.py's streaming batch ({n_patch} image "
              f"patches, {alg / 1e9:.2f} GB of algorithmic traffic per launch, several times the 256 MB last-level "
              "cache), inside the bench's normpatch_stream measurement (a zero-layer tower).  Commands (from the "
-             "repository root on the GPU host):", "", "```", command, "```", "",
+             "repository root on an MI355X machine; <out> is any output directory):", "", "```", command, "```", "",
              f"Launches of the streaming batch: the {len(tr)} normpatch dispatches with the largest grid "
              f"({grid} work-items) in the trace, {nf} and {nw} in the counter passes.  Algorithmic bytes per "
              f"launch: {alg_read / 1e6:.1f} MB of pixels read (an image's one frame serves both temporal "

@@ -17,7 +17,7 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy().astype(np.float64)
 
 
-class GpuRun:
+class TowerRun:
     def __init__(self, wl, activation_precision: str = "f16"):
         self.wl = wl
         self.prec = activation_precision
@@ -117,15 +117,20 @@ class GpuRun:
 
 
 def progress_log(msg: str):
-    """Appends a progress line of a long test step to gpurun_out/gpu_tests_progress.log (test
-    output is captured until a test ends; this file shows a long oracle run advancing)."""
+    """A progress line of a long test step (test output is captured until a test ends): written
+    to the process's own stderr, past pytest's capture, and appended to the file named by the
+    VIT_TEST_PROGRESS environment variable when that is set."""
     import os
+    import sys
     import time
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    d = os.path.join(root, "gpurun_out")
-    os.makedirs(d, exist_ok=True)
-    with open(os.path.join(d, "gpu_tests_progress.log"), "a") as f:
-        f.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
+    line = f"{time.strftime('%H:%M:%S')} {msg}\n"
+    sys.__stderr__.write(line)
+    sys.__stderr__.flush()
+    path = os.environ.get("VIT_TEST_PROGRESS")
+    if path:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "a") as f:
+            f.write(line)
 
 
 def per_item_errors(got: np.ndarray, ref: np.ndarray, items) -> list:

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_support import GpuRun, assert_encoder_tolerance  # noqa: E402
+from gpu_support import TowerRun, assert_encoder_tolerance  # noqa: E402
 from oracle import vit_oracle as O  # noqa: E402
 from multimodal_vlm_vision_amd.binding import VitError  # noqa: E402
 
@@ -48,7 +48,7 @@ def _eager(tower, items, out_dim):
 def test_bucket_graph_replays_other_batches():
     # windowed and full-attention layers, RMSNorm, SwiGLU: every count the kernels read
     wl = make_workload(5, layers=8)
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     tower, cap, out_dim = run.tower, run.plan, wl.cfg.out_dim
     say(f"bucket capacity N={cap.n_patches}, {len(wl.items)} items")
     gws = torch.empty(cap.ws_bytes, dtype=torch.uint8, device="cuda")
@@ -111,7 +111,7 @@ def test_bucket_graph_replays_other_batches():
 
 
 def test_plain_graph_rejects_plans():
-    run = GpuRun(make_workload(1))
+    run = TowerRun(make_workload(1))
     gws = torch.empty(run.plan.ws_bytes, dtype=torch.uint8, device="cuda")
     g = run.tower.capture(run.plan, gws)
     with pytest.raises(VitError, match="capture_bucket"):

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_support import GpuRun, assert_encoder_tolerance  # noqa: E402
+from gpu_support import TowerRun, assert_encoder_tolerance  # noqa: E402
 from multimodal_vlm_vision_amd import EmbeddingCache  # noqa: E402
 
 
@@ -65,7 +65,7 @@ def same(got, ref, batch, what):
 
 @pytest.fixture(scope="module")
 def run():
-    return GpuRun(make_workload(3, layers=2))   # 8 images of mixed sizes, 2 layers
+    return TowerRun(make_workload(3, layers=2))   # 8 images of mixed sizes, 2 layers
 
 
 def test_device_pixel_keys_match_oracle(run):

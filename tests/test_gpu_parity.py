@@ -33,7 +33,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_support import GpuRun, assert_close_bf16, assert_encoder_tolerance, f8_extra, unit  # noqa: E402
+from gpu_support import TowerRun, assert_close_bf16, assert_encoder_tolerance, f8_extra, unit  # noqa: E402
 
 _RUNS = {}
 
@@ -48,13 +48,13 @@ def say(msg):
 PRECS = ["f16", "bf16x2", "bf16f8"]
 
 
-def get_run(idx: int, layers=None, prec="f16") -> GpuRun:
+def get_run(idx: int, layers=None, prec="f16") -> TowerRun:
     key = (idx, layers, prec)
     if key not in _RUNS:
         say(f"building workload {idx} layers={layers} activations={prec}")
         _RUNS.clear()
         torch.cuda.empty_cache()
-        _RUNS[key] = GpuRun(make_workload(idx, layers=layers), activation_precision=prec)
+        _RUNS[key] = TowerRun(make_workload(idx, layers=layers), activation_precision=prec)
     return _RUNS[key]
 
 
@@ -99,7 +99,7 @@ TABLE_PATH_MEAN, TABLE_PATH_STD = (0.1, 0.2, 0.3), (0.11, 0.13, 0.17)
 def test_normpatch_bit_exact_table_path():
     cfg = dataclasses.replace(tower_config(1).with_layers(1), mean=TABLE_PATH_MEAN, std=TABLE_PATH_STD)
     wl = make_custom_workload(cfg, [(1, 84, 140), (4, 56, 112), (1, 224, 168)], seed=61)
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     say(f"normpatch table path N={run.n}")
     got = run.stage(-1, 0)
     table = O.normalize_table(cfg.mean, cfg.std)
@@ -257,7 +257,7 @@ def test_video_workload_last_block_and_merger():
 def test_video_shaped_short_clip_end_to_end():
     cfg = tower_config(4).with_layers(2)
     wl = make_custom_workload(cfg, [(4, 504, 896)], seed=41)
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     say(f"short video clip N={run.n}")
     assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="video 4 frames, 2 layers")
 
@@ -274,7 +274,7 @@ def test_tile_configs_across_batch_sizes(side, prec):
     oracle (computed once per size)."""
     cfg = tower_config(2).with_layers(1)
     wl = make_custom_workload(cfg, [(1, side, side)], seed=71)
-    run = GpuRun(wl, activation_precision=prec)
+    run = TowerRun(wl, activation_precision=prec)
     say(f"tile configs: {side}x{side} image N={run.n} activations {prec}")
     if side not in _TILE_REFS:
         _TILE_REFS[side] = O.forward_workload(wl)
@@ -292,7 +292,7 @@ def test_e4m3_residual_saturation():
     ref = O.forward_workload(wl)
     errs = {}
     for prec in ("bf16", "bf16x2", "bf16f8", "f16"):
-        run = GpuRun(wl, activation_precision=prec)
+        run = TowerRun(wl, activation_precision=prec)
         if prec == "bf16f8":
             a = run.stage(0, 8)
             say(f"saturation: largest MLP activation {np.abs(a).max():.1f}, "
@@ -310,7 +310,7 @@ def test_edge_items_end_to_end():
     cfg = tower_config(2).with_layers(2)
     sizes = [(1, 28, 28), (1, 56, 28), (2, 28, 84), (1, 28, 28 * 19), (1, 196, 140)]
     wl = make_custom_workload(cfg, sizes, seed=43)
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     say(f"edge items N={run.n} segments={wl.seg_lengths}")
     assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="edge items")
 
@@ -319,7 +319,7 @@ def test_qwen25_windows_small_end_to_end():
     cfg = dataclasses.replace(tower_config(5).with_layers(3), full_attn_layers=(1,))
     sizes = [(1, 28 * 9, 28 * 5), (1, 56, 28 * 7), (4, 28 * 6, 28 * 5)]
     wl = make_custom_workload(cfg, sizes, seed=47)
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     say(f"window tower N={run.n}")
     assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="windows + full layer")
 
@@ -331,7 +331,7 @@ def test_isolation_between_items():
     cfg = tower_config(3).with_layers(2)
     sizes = [(1, 56, 84), (1, 112, 56), (1, 84, 84)]
     wl = make_custom_workload(cfg, sizes, seed=53)
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     say("isolation")
     a = run.encode()
     px = pack_pixels(wl.items)
@@ -356,7 +356,7 @@ def test_batch_near_the_operand_limit_matches_its_items_alone():
     wl = make_custom_workload(cfg, [(1, 896, 896)] * 50, seed=67)
     act = wl.n_patches * 5120 * 2
     assert 0.97 * (1 << 31) < act < (1 << 31)
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     assert run.plan.attention_units()[1] == 0, "the big batch's plan splits key ranges"
     say(f"near-limit batch: N={run.n}, MLP activation {act / 2**30:.3f} GiB")
     run.tower.encode(run.plan, run.pixels, run.ws, run.out)
@@ -407,7 +407,7 @@ def test_key_split_video_graph_replays_match_eager():
     of the segment's keys) and the merge pass: eager, repeated eager and three graph replays
     (eager work between them) give the same bytes."""
     wl = make_workload(4, layers=2)
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     _, n_merge, n_parts = run.plan.attention_units()
     say(f"key-split video: {n_merge} merged query blocks over {n_parts} partial slots")
     assert n_merge > 0
@@ -427,7 +427,7 @@ def test_key_split_ragged_segments_match_oracle():
     cfg = tower_config(2).with_layers(2)
     for sizes, seed in (([(1, 82 * 14, 22 * 14)], 53), ([(1, 42 * 14, 50 * 14), (1, 18 * 14, 22 * 14)], 59)):
         wl = make_custom_workload(cfg, sizes, seed=seed)
-        run = GpuRun(wl)
+        run = TowerRun(wl)
         units, n_merge, n_parts = run.plan.attention_units()
         ragged = {int(u[1]) for u in units if u[5] >= 0 and u[1] % 32}
         say(f"ragged key splits: segments {wl.seg_lengths}, {len(units)} units, {n_merge} merges, "
@@ -470,7 +470,7 @@ _STALE_CASES = {
 @pytest.mark.parametrize("case", list(_STALE_CASES))
 def test_stale_workspace_never_reaches_the_output(case):
     wl = _STALE_CASES[case]()
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     say(f"0xFF-filled workspace, {case}: N={run.n}, segments {wl.seg_lengths}")
     run.ws.fill_(0xFF)
     run.out.fill_(float("nan"))
@@ -489,7 +489,7 @@ def test_segments_around_the_short_long_threshold():
              (4, 112, 112)]
     wl = make_custom_workload(cfg, sizes, seed=73)
     assert sorted(wl.seg_lengths) == [124, 128, 128, 132, 252, 256, 260]
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     units = run.plan.attention_units()[0]
     say(f"short/long threshold: segments {wl.seg_lengths}, {len(units)} long units")
     assert sorted({int(u[1]) for u in units}) == [132, 252, 256, 260]
@@ -502,7 +502,7 @@ def test_extreme_aspect_ratios():
     column; 2 layers of the 1280-wide tower against the oracle."""
     cfg = tower_config(2).with_layers(2)
     wl = make_custom_workload(cfg, [(1, 28, 28672), (1, 14336, 56)], seed=79)
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     say(f"extreme aspect ratios: grids {[it.grid_thw for it in wl.items]}, N={run.n}")
     assert_encoder_tolerance(run.encode(), O.forward_workload(wl), what="extreme aspect ratios")
 

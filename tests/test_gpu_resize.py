@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_support import GpuRun, assert_encoder_tolerance  # noqa: E402
+from gpu_support import TowerRun, assert_encoder_tolerance  # noqa: E402
 from multimodal_vlm_vision_amd import resize_side, resize_u8  # noqa: E402
 
 
@@ -56,7 +56,7 @@ def test_resized_image_through_the_tower():
     say(f"resized {raw.shape[1:3]} -> {frames.shape[1:3]}, encoding")
     item = Item(frames, (1, frames.shape[1] // 14, frames.shape[2] // 14))
     wl = Workload(1, cfg, [item], make_weights(1, cfg))
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     got = run.encode()
     ref = O.forward_workload(wl)
     assert_encoder_tolerance(got, ref, what="resized image")

@@ -12,7 +12,7 @@ float32 on the same seeded inputs:
 
 Bar: max |g - r| <= 2e-2 and sum |g - r| / sum |r| <= 5e-3 over the whole output.  Each
 item's own figures are printed as well.  The oracle's long runs report each finished layer
-in gpurun_out/gpu_tests_progress.log.
+on stderr (and in the file VIT_TEST_PROGRESS names, when set).
 """
 
 import time
@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_support import GpuRun, assert_encoder_tolerance, per_item_errors, progress_log, rel_err  # noqa: E402
+from gpu_support import TowerRun, assert_encoder_tolerance, per_item_errors, progress_log, rel_err  # noqa: E402
 
 
 def say(msg):
@@ -40,7 +40,7 @@ def say(msg):
 @pytest.mark.parametrize("idx", [3, 4, 5])
 def test_whole_output_through_graph_matches_oracle(idx):
     wl = make_workload(idx)
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     say(f"workload {idx} ({wl.cfg.name}): N={run.n}, {len(wl.items)} items, graph replay")
     got = run.graph_encode(replays=2)
     del run

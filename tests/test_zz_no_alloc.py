@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU too; every test here needs the GPU
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_support import GpuRun  # noqa: E402
+from gpu_support import TowerRun  # noqa: E402
 from multimodal_vlm_vision_amd.binding import VIT_E_WORKSPACE, VitError  # noqa: E402
 
 
@@ -31,7 +31,7 @@ def _noalloc(tower, plan, pixels, out_dim):
 
 def test_noalloc_matches_encode_on_two_calls_second_smaller():
     wl = make_workload(2)                       # 448 x 448 image, 1024 patches, 4 layers
-    run = GpuRun(wl)
+    run = TowerRun(wl)
     tower, cfg = run.tower, wl.cfg
     say(f"no-alloc encode: N={run.n}, workspace {run.plan.ws_bytes / 2**20:.1f} MiB")
     want = run.encode().astype(np.float32)

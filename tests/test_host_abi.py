@@ -2,7 +2,8 @@
 symbol the header declares; configuration, weight and batch validation fail
 with the documented status before anything is enqueued; the planner's sizes,
 row order and window permutation agree with index sets derived independently
-(from the oracle's window partition).  No GPU call is made."""
+(from the oracle's window partition); the header compiles as C99 and a C program linked
+with the library runs the host-side calls.  No GPU call is made."""
 
 import ctypes
 
@@ -295,3 +296,62 @@ def test_normalisation_fma_path_premise():
     assert _fma_path_mismatches(cfg.mean, cfg.std) == 0
     # the table-path GPU test's mean/std: one byte differs, so the library keeps the table
     assert _fma_path_mismatches((0.1, 0.2, 0.3), (0.11, 0.13, 0.17)) >= 1
+
+
+# ---- the header as a plain C interface: a C99 program compiled against include/vit.h and
+# linked with the library runs the host-side calls (no GPU call is made)
+
+_C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "vit.h"
+
+int main(void) {
+  vit_config c;
+  memset(&c, 0, sizeof c);
+  c.hidden = 64; c.heads = 2; c.layers = 1; c.mlp_dim = 256;
+  c.mlp_kind = VIT_MLP_GELU; c.norm_kind = VIT_NORM_LAYER; c.norm_eps = 1e-6f;
+  c.patch = 14; c.temporal_patch = 2; c.merge = 2; c.out_dim = 128; c.rope_theta = 10000.f;
+  for (int i = 0; i < 3; ++i) { c.mean[i] = 0.5f; c.std[i] = 0.25f; }
+  c.activation_precision = VIT_ACT_F16;
+  vit_ctx* ctx = NULL;
+  if (vit_create(&c, &ctx) != VIT_OK) { printf("create: %s\n", vit_last_error()); return 1; }
+  const int32_t grid[6] = {1, 4, 6, 2, 2, 2};   /* a 56 x 84 image and a 4-frame 28 x 28 clip */
+  const int32_t frames[2] = {1, 4};
+  vit_plan* plan = NULL;
+  if (vit_plan_create(ctx, grid, frames, 2, &plan) != VIT_OK) { printf("plan: %s\n", vit_last_error()); return 1; }
+  size_t px = 0, ws = 0;
+  int64_t rows = 0, cols = 0, n = 0;
+  if (vit_plan_sizes(plan, &px, &ws, &rows, &cols) != VIT_OK || vit_plan_rows(plan, &n, NULL) != VIT_OK) return 1;
+  printf("pixels %zu rows %lld cols %lld patches %lld ws %d\n", px, (long long)rows, (long long)cols,
+         (long long)n, ws > 0);
+  vit_config bad = c;
+  bad.heads = 3;   /* 64 / 3 is no head size */
+  vit_ctx* ctx2 = NULL;
+  const vit_status s = vit_create(&bad, &ctx2);
+  printf("bad config %d %d %d\n", (int)s, ctx2 == NULL, (int)(strlen(vit_last_error()) > 0));
+  vit_plan_destroy(plan);
+  vit_destroy(ctx);
+  return 0;
+}
+"""
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use_vit.c"
+    src.write_text(_C_PROGRAM)
+    exe = tmp_path / "use_vit"
+    lib = os.path.abspath(B.LIB_PATH)
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(B.__file__))), "include")
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", inc, str(src), "-o", str(exe), lib,
+                    f"-Wl,-rpath,{os.path.dirname(lib)}"], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, timeout=60).stdout.split("\n")
+    # 56 x 84 px image: 4 x 6 patches; 4-frame 28 x 28 clip: 2 temporal x 2 x 2 patches
+    assert out[0] == f"pixels {56 * 84 * 3 + 4 * 28 * 28 * 3} rows {(24 + 8) // 4} cols 128 patches 32 ws 1"
+    assert out[1] == f"bad config {B.VIT_E_ARG} 1 1"

@@ -30,9 +30,10 @@
 // path spends no VALU op on it; P is rounded to the operand type for the MFMA.  The offset
 // is only raised (and O rescaled) when a block's max exceeds it by more than
 // 2^8, which keeps the rescale off the common path without changing the math.
-// The two MFMA groups of a block run at raised wave priority (s_setprio): a
-// co-resident wave in its softmax then fills the matrix pipe's gaps instead of
-// delaying it.
+// A block's score MFMAs run at raised wave priority (s_setprio): a co-resident
+// wave in its softmax then fills the matrix pipe's gaps instead of delaying the
+// scores that the wave's own softmax waits for (raising the P.V MFMAs as well
+// measured slower on long segments).
 //
 // K tiles (32 keys x head_dim, row stride head_dim + 8 so 16-byte fragment
 // reads of 16 consecutive rows hit distinct banks; keys in the row order of
@@ -366,7 +367,6 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
       // ---- O^T += V^T P^T over the 32 keys; the lane's probabilities of chunk c are the keys
       //      16c + 8h + 0..7 (K rows are loaded in key_at order), i.e. one whole 16-byte chunk
       //      2c + h of a V^T row
-      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int row = 32 * dt + l32;
@@ -378,7 +378,6 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
           for (int t = 0; t < QT; ++t) O[t][dt] = mma<F16>(vf, pb[t][c], O[t][dt]);
         }
       }
-      __builtin_amdgcn_s_setprio(0);
     }
     if (sync) __syncthreads();
   };

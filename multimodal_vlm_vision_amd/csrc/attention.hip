@@ -30,10 +30,11 @@
 // path spends no VALU op on it; P is rounded to the operand type for the MFMA.  The offset
 // is only raised (and O rescaled) when a block's max exceeds it by more than
 // 2^8, which keeps the rescale off the common path without changing the math.
-// A block's score MFMAs run at raised wave priority (s_setprio): a co-resident
-// wave in its softmax then fills the matrix pipe's gaps instead of delaying the
-// scores that the wave's own softmax waits for (raising the P.V MFMAs as well
-// measured slower on long segments).
+// A block's score MFMAs, and its softmax up to the last tile's exponentials, run
+// at raised wave priority (s_setprio): a co-resident wave then fills the matrix
+// pipe's gaps instead of delaying the chain from the scores to the probabilities
+// (raising the P.V MFMAs as well measured slower on long segments).  The score
+// MFMAs' K fragments are read three ahead of their MFMAs.
 //
 // K tiles (32 keys x head_dim, row stride head_dim + 8 so 16-byte fragment
 // reads of 16 consecutive rows hit distinct banks; keys in the row order of
@@ -313,15 +314,26 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
       // ---- S^T = K Q^T for both query tiles: rows = 32 keys, columns = 32 queries
       f32x16 S[QT];
       const uint16_t* kr = Kt + l32 * KS + 8 * h;
+      // K fragments three reads ahead of their MFMAs (the compiler's own order keeps two in
+      // flight, so each pair of MFMAs would wait for its read)
+      constexpr int KAH = NCH < 3 ? NCH : 3;
+      bf16x8 kf[NCH];
+#pragma unroll
+      for (int c = 0; c < KAH; ++c) kf[c] = *reinterpret_cast<const bf16x8*>(kr + 16 * c);
       __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * c);
 #pragma unroll
         for (int t = 0; t < QT; ++t)
-          S[t] = mma<F16>(kf, qf[t][c], c == 0 ? nm[t] : S[t]);
+          S[t] = mma<F16>(kf[c], qf[t][c], c == 0 ? nm[t] : S[t]);
+        if (c + KAH < NCH) kf[c + KAH] = *reinterpret_cast<const bf16x8*>(kr + 16 * (c + KAH));
       }
-      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_group_barrier(0x100, KAH, 1);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QT, 1);
+        if (c + KAH < NCH) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
       // ---- mask keys past the segment end (last step only); lane's keys are 8g + 4h + e
       const int key_base = kb * KB;
       if (key_base + KB > kn) {
@@ -357,6 +369,7 @@ attn_kernel(AttnArgs a, const AttnWork* __restrict__ work, int n_work, const int
             S[t][e] -= dm;
           }
         }
+        if (t == QT - 1) __builtin_amdgcn_s_setprio(0);   // raised since the score MFMAs
         uint32_t pw[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)

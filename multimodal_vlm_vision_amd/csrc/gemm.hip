@@ -560,6 +560,12 @@ gemm_kernel(GemmArgs p) {
   constexpr int NMF = TM * TN * (SPLIT ? 2 : 1);   // MFMAs per 16-wide K step
   constexpr int NDS = TM * (SPLIT ? 2 : 1) + TN;    // fragment reads per K step
 
+  // Products whose epilogue carries VALU work (GELU, SwiGLU, RoPE) run their main loop at raised
+  // wave priority and the epilogue at the normal one, so a co-resident workgroup's epilogue
+  // yields issue slots to this one's matrix work (the residual products, whose epilogue is
+  // mostly memory traffic, measured no better with it).
+  constexpr bool kPrio = EPI == EPI_GELU || EPI == EPI_SWIGLU || EPI == EPI_QKV;
+  if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
   // ---- prologue: every stage in flight, stage 0 landed everywhere
 #pragma unroll
   for (int s = 0; s < S; ++s) issue(s, s);
@@ -692,6 +698,7 @@ gemm_kernel(GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   }
   }
+  if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
   // drain the (redundant) trailing loads before the ring is reused for the epilogue
   wait_vm<0>();
   __syncthreads();

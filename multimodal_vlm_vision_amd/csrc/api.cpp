@@ -97,10 +97,19 @@ vit_status check_common(const vit_ctx* ctx, const vit_plan* plan, const void* ws
     set_error("weights not finalized");
     return VIT_E_STATE;
   }
-  if (plan->cfg.hidden != ctx->cfg.hidden || plan->cfg.layers != ctx->cfg.layers ||
-      plan->cfg.window_px != ctx->cfg.window_px || plan->head_dim != ctx->head_dim ||
-      plan->split != ctx->split || plan->f8 != ctx->f8 ||
-      plan->cfg.activation_precision != ctx->cfg.activation_precision) {
+  // the plan's workspace layout, work lists and rotary tables follow the configuration of the
+  // tower it was built for: every field they depend on must match this tower's
+  const vit_config& pc = plan->cfg;
+  const vit_config& cc = ctx->cfg;
+  bool same = pc.hidden == cc.hidden && pc.heads == cc.heads && pc.layers == cc.layers &&
+              pc.mlp_dim == cc.mlp_dim && pc.mlp_kind == cc.mlp_kind && pc.out_dim == cc.out_dim &&
+              pc.rope_theta == cc.rope_theta && pc.window_px == cc.window_px &&
+              pc.n_full_attn_layers == cc.n_full_attn_layers &&
+              pc.activation_precision == cc.activation_precision && plan->head_dim == ctx->head_dim &&
+              plan->mlp_pad == ctx->mlp_pad && plan->split == ctx->split && plan->f8 == ctx->f8;
+  for (int i = 0; same && i < cc.n_full_attn_layers && i < VIT_MAX_FULL_LAYERS; ++i)
+    same = pc.full_attn_layers[i] == cc.full_attn_layers[i];
+  if (!same) {
     set_error("plan was built for a different tower configuration");
     return VIT_E_ARG;
   }

@@ -524,3 +524,26 @@ def test_empty_batch_enqueues_nothing():
     p = run.tower.plan(np.zeros((0, 3), np.int32), np.zeros(0, np.int32))
     run.tower.encode(p, None, None, None)
     torch.cuda.synchronize()
+
+
+def test_plan_of_another_tower_is_refused_before_any_work():
+    """A plan carries the workspace layout, work lists and rotary tables of the tower it was
+    built for: encoding it with a tower whose MLP width, output width or rotary base differs is
+    refused (VIT_E_ARG) before anything is enqueued, and the tower encodes its own plans as
+    before."""
+    from multimodal_vlm_vision_amd.binding import VIT_E_ARG, VitError
+    base = tower_config(1)
+    wl = make_custom_workload(base, [(1, 56, 84)], seed=107)
+    run = TowerRun(wl)
+    ref = run.encode()
+    for field, value in (("mlp_dim", 2 * base.mlp_dim), ("out_dim", 2 * base.out_dim),
+                         ("rope_theta", 2 * base.rope_theta)):
+        other = TowerRun(make_custom_workload(dataclasses.replace(base, **{field: value}), [(1, 56, 84)], seed=107))
+        say(f"foreign plan: {field} {getattr(base, field)} vs {value}")
+        with pytest.raises(VitError) as e:
+            run.tower.encode(other.plan, run.pixels, other.ws, other.out)
+        assert e.value.status == VIT_E_ARG and "different tower configuration" in str(e.value)
+        with pytest.raises(VitError):
+            other.tower.encode(run.plan, other.pixels, run.ws, run.out)
+    torch.cuda.synchronize()
+    assert np.array_equal(run.encode(), ref)

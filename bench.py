@@ -387,7 +387,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the vision tower is not sharded "
-              "across GPUs in this build", file=sys.stderr)
+              "across GPUs by this library", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -78,7 +78,7 @@ typedef int32_t vit_status;
 
 #define VIT_MAX_FULL_LAYERS 64
 
-/* Tower hyper-parameters.  Fixed by this build: patch 14, temporal_patch 2,
+/* Tower hyper-parameters.  Fixed by this library: patch 14, temporal_patch 2,
  * merge 2 (checked).  hidden % 64 == 0, head_dim = hidden / heads must be 32,
  * 64 or 80 (80 is the Qwen2-VL head size), layers >= 0. */
 typedef struct vit_config {

@@ -5,7 +5,7 @@ It shares no code with the HIP library.
 
 The pages name a vision-embedding cache shared across requests ("vLLM
 multimodal inference | ViT performance optimisation", section 2.3) but no key;
-the key is this build's reading: a 128-bit content key of an item's uint8
+the key taken here is a 128-bit content key of an item's uint8
 pixels.  With the item's L pixel bytes read as L/8 little-endian 64-bit words
 w_k (L is a multiple of 16 for every valid item), lane j is
 

@@ -6,8 +6,8 @@ It shares no code with the HIP library.
 The pages say the preprocessor resizes and pads images into pixel tensors
 ("vLLM multimodal inference | ViT performance optimisation", section 2.2) and
 that CPU preprocessing caps serving throughput (SGLang PR #35349 report) but
-fix neither the target size nor the interpolation.  The readings (also in
-the design doc): each side goes to the nearest multiple of 28 pixels, half up, at
+fix neither the target size nor the interpolation.  The readings taken
+here: each side goes to the nearest multiple of 28 pixels, half up, at
 least 28; bilinear sampling with half-pixel centres, source coordinate
 s = (d + 0.5) * S / D - 0.5 clamped to the image; weights in 11-bit fixed point
 (w = round((s - floor(s)) * 2^11)), integer arithmetic, the result rounded

@@ -27,7 +27,7 @@ in float64 by default (``dtype=np.float32`` is accepted for large cases):
 6. the patch merger: each 2x2 group of patch features -> one token through an
    MLP projector (section 2.2, encoding step 4).
 
-Readings where the pages are silent (each one is also listed in the design doc):
+Readings where the pages are silent:
 x/255 as the rescale; bfloat16 round-to-nearest-even of the exact value; row
 order (dh, dw) inside a merge unit and t-major across frames; feature order
 (c, tau, i, j); an image's single frame duplicated to the temporal patch;
